@@ -1,0 +1,201 @@
+"""CPU oracle for the FP16 x INT4 (group-128) linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may import this
+package.  The GPU library never loads it, and it loads nothing from the GPU library.
+
+Two independent implementations live here:
+
+* ``oracle.c`` (built into ``liboracle.so``): the plain C reference.  ``gemm(..., mode="f32")``
+  accumulates in fp32 with k ascending and rounds to fp16 once, the precision the pages fix
+  (Marlin deep-dive page "Marlin 完全拆解", section "让多个 warp 计算同一个输出 tile 的部分和":
+  FP32 accumulators, FP16 only at write-out).  ``mode="f64"`` is the diagnostic truth.
+* ``exact_gemm`` below: exact integer arithmetic on the dyadic values, correctly rounded to
+  fp16 by its own routine.  It is slow and only for tiny shapes; it pins the C code.
+
+The operation (MARLIN paper, arXiv 2408.11743, sec. 3.4 "Kernel Design"; deep-dive page,
+section "Marlin 要解决的精确问题"):  C = A * Bhat,  Bhat[k, n] = s[k // group, n] * (q[k, n] - 8).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c with gcc.  -ffp-contract=off keeps multiply and add separate."""
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-pthread", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_double_to_half.argtypes = [ctypes.c_double]
+    lib.oracle_double_to_half.restype = ctypes.c_uint16
+    lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_half.restype = ctypes.c_uint16
+    lib.oracle_dequant.argtypes = [ctypes.c_uint8, ctypes.c_uint16]
+    lib.oracle_dequant.restype = ctypes.c_double
+    for name in ("oracle_gemm_f32", "oracle_gemm_f64"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, p, i, i, i, i, p, i]
+        fn.restype = i
+    lib.oracle_gemv_f32.argtypes = [p, p, p, i, i, i, p]
+    lib.oracle_gemv_f32.restype = i
+    _lib = lib
+    return lib
+
+
+def lib():
+    return _load()
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a)
+
+
+def gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128, mode: str = "f32",
+         nthreads: int = 0) -> np.ndarray:
+    """C = A @ Bhat with A fp16 [M, K], q uint8 [K, N], s fp16 [K/group, N]; returns fp16 [M, N]."""
+    A = _c(np.asarray(A, dtype=np.float16))
+    q = _c(np.asarray(q, dtype=np.uint8))
+    s = _c(np.asarray(s, dtype=np.float16))
+    M, K = A.shape
+    K2, N = q.shape
+    if K2 != K or s.shape != (K // group, N):
+        raise ValueError(f"shape mismatch A{A.shape} q{q.shape} s{s.shape} group={group}")
+    C = np.empty((M, N), dtype=np.float16)
+    fn = {"f32": _load().oracle_gemm_f32, "f64": _load().oracle_gemm_f64}[mode]
+    rc = fn(A.ctypes.data, q.ctypes.data, s.ctypes.data, M, K, N, group, C.ctypes.data,
+            int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_{mode} returned {rc}")
+    return C
+
+
+def gemv(a: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128) -> np.ndarray:
+    """The M = 1 product, coded separately from gemm; returns fp16 [N]."""
+    a = _c(np.asarray(a, dtype=np.float16).reshape(-1))
+    q = _c(np.asarray(q, dtype=np.uint8))
+    s = _c(np.asarray(s, dtype=np.float16))
+    K, N = q.shape
+    if a.shape[0] != K:
+        raise ValueError("length mismatch")
+    c = np.empty((N,), dtype=np.float16)
+    rc = _load().oracle_gemv_f32(a.ctypes.data, q.ctypes.data, s.ctypes.data, K, N, group,
+                                 c.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_gemv_f32 returned {rc}")
+    return c
+
+
+def half_to_double(bits: int) -> float:
+    return _load().oracle_half_to_double(int(bits))
+
+
+def double_to_half(x: float) -> int:
+    return int(_load().oracle_double_to_half(float(x)))
+
+
+def float_to_half(x: float) -> int:
+    return int(_load().oracle_float_to_half(float(x)))
+
+
+def dequant(q: int, s_bits: int) -> float:
+    return _load().oracle_dequant(int(q), int(s_bits))
+
+
+# --------------------------------------------------------------------------------------------
+# Exact reference for tiny shapes: every finite fp16 value is an integer multiple of 2^-24, so
+# a*w is an integer multiple of 2^-48 and the whole sum is one exact Python integer.
+
+_SHIFT = 48
+
+
+def _half_bits_to_scaled(h: int) -> int:
+    """fp16 bits -> integer v with value = v * 2^-24 (finite inputs only)."""
+    e = (h >> 10) & 0x1F
+    m = h & 0x3FF
+    if e == 31:
+        raise ValueError("non-finite input")
+    v = m if e == 0 else (m + 1024) << (e - 1)
+    return -v if h & 0x8000 else v
+
+
+def round_scaled_to_half(S: int, shift: int = _SHIFT) -> int:
+    """Correctly round S * 2^-shift to fp16 bits (nearest, ties to even).  Exact zero -> +0."""
+    if S == 0:
+        return 0
+    sign = 0x8000 if S < 0 else 0
+    S = abs(S)
+    e = S.bit_length() - 1 - shift          # 2^e <= value < 2^(e+1)
+    ex = max(e, -14)
+    sh = shift + ex - 10                    # value / ulp = S / 2^sh, ulp = 2^(ex-10)
+    if sh > 0:
+        qv, rem = divmod(S, 1 << sh)
+        twice = rem << 1
+        if twice > (1 << sh) or (twice == (1 << sh) and (qv & 1)):
+            qv += 1
+    else:
+        qv = S << (-sh)
+    if qv == 2048:                          # rounding carried into the next binade
+        qv = 1024
+        ex += 1
+    if ex > 15 or (ex == 15 and qv > 2047):
+        return sign | 0x7C00
+    if qv < 1024:                           # only possible at ex == -14: subnormal
+        return sign | qv
+    return sign | ((ex + 15) << 10) | (qv - 1024)
+
+
+def exact_gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128):
+    """Exact C per output: (correctly rounded fp16, exact value as float64, sum_k |a_k w_k|).
+
+    Pure Python integer arithmetic; use only on tiny shapes.
+    """
+    A16 = np.asarray(A, dtype=np.float16).view(np.uint16)
+    s16 = np.asarray(s, dtype=np.float16).view(np.uint16)
+    q = np.asarray(q, dtype=np.uint8)
+    M, K = A16.shape
+    N = q.shape[1]
+    a_int = [[_half_bits_to_scaled(int(A16[m, k])) for k in range(K)] for m in range(M)]
+    w_int = [[_half_bits_to_scaled(int(s16[k // group, n])) * (int(q[k, n]) - 8)
+              for k in range(K)] for n in range(N)]
+    out = np.empty((M, N), dtype=np.uint16)
+    exact = np.empty((M, N), dtype=np.float64)
+    absum = np.empty((M, N), dtype=np.float64)
+    for m in range(M):
+        am = a_int[m]
+        for n in range(N):
+            wn = w_int[n]
+            tot = 0
+            tabs = 0
+            for k in range(K):
+                p = am[k] * wn[k]
+                tot += p
+                tabs += abs(p)
+            out[m, n] = round_scaled_to_half(tot)
+            exact[m, n] = tot / float(1 << _SHIFT)
+            absum[m, n] = tabs / float(1 << _SHIFT)
+    return out.view(np.float16), exact, absum

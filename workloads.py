@@ -1,0 +1,80 @@
+"""Seeded synthetic inputs and the layer shapes they are drawn for.
+
+Shared by the tests, the smoke check and the benchmark.  This module holds no part of the
+layer's arithmetic: it only draws codes, scales and activations and names shapes.
+
+Distributions (the same for every shape):
+  codes  q  ~ uniform integers 0..15 (uint8, one code per byte, [K, N] row-major)
+  scales s  ~ uniform [0.005, 0.02], rounded to fp16 ([K/group, N] row-major)
+  A         ~ N(0, sigma^2) drawn in fp32, rounded to fp16 ([M, K] row-major)
+Draw order per weight shape: q, then s, then A (largest M; smaller M use the leading rows),
+all from one ``numpy.random.default_rng(seed)`` stream.
+
+The shapes stand in for the pages' workloads: one 72k x 18k weight at group 128 (the MARLIN
+paper's Figure 1 layer, read as K = 18432 reduction rows by N = 73728 output columns) and
+Llama-2-7B / Llama-2-70B decoder-block linears (the per-layer benchmarks at batch 16).
+No model weights or datasets are used: only the shapes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+GROUP = 128
+
+
+@dataclass(frozen=True)
+class Shape:
+    name: str
+    K: int
+    N: int
+    Ms: tuple
+    sigma: float = 1.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shapes: tuple = field(default_factory=tuple)
+
+
+SMALL = Workload("single_1024x1024_m16", (Shape("1024x1024", 1024, 1024, (16,)),))
+
+LARGE = Workload("single_72kx18k_m1_128", (
+    Shape("18432x73728", 18432, 73728, (1, 2, 4, 8, 16, 32, 64, 128)),))
+
+LLAMA2_7B = Workload("llama2_7b_block_m1_16_64", (
+    Shape("7b_qkv", 4096, 12288, (1, 16, 64)),
+    Shape("7b_o", 4096, 4096, (1, 16, 64)),
+    Shape("7b_gate_up", 4096, 22016, (1, 16, 64)),
+    Shape("7b_down", 11008, 4096, (1, 16, 64)),
+))
+
+LLAMA2_70B = Workload("llama2_70b_block_m16_32_128", (
+    Shape("70b_qkv", 8192, 10240, (16, 32, 128)),
+    Shape("70b_o", 8192, 8192, (16, 32, 128)),
+    Shape("70b_gate_up", 8192, 57344, (16, 32, 128)),
+    Shape("70b_down", 28672, 8192, (16, 32, 128)),
+))
+
+COMPUTE_SWEEP = Workload("compute_8192x28672_m256_1024", (
+    Shape("8192x28672", 8192, 28672, (256, 512, 1024), sigma=0.5),))
+
+ALL = (SMALL, LARGE, LLAMA2_7B, LLAMA2_70B, COMPUTE_SWEEP)
+
+
+def draw(K: int, N: int, M: int, seed: int = 0, sigma: float = 1.0, group: int = GROUP):
+    """Return (A fp16 [M,K], q uint8 [K,N], s fp16 [K/group,N]) from one seeded stream."""
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = rng.uniform(0.005, 0.02, size=(K // group, N)).astype(np.float16)
+    A = (rng.standard_normal((M, K), dtype=np.float32) * np.float32(sigma)).astype(np.float16)
+    return A, q, s
+
+
+def draw_shape(shape: Shape, seed: int = 0, group: int = GROUP):
+    """Inputs for every M of a shape: A has max(Ms) rows; M uses A[:M]."""
+    return draw(shape.K, shape.N, max(shape.Ms), seed=seed, sigma=shape.sigma, group=group)
