@@ -1,0 +1,179 @@
+"""Benchmark: W4A16 GEMM effective GB/s on the 72k x 18k weight (K = 18432, N = 73728,
+group 128) over the batch sweep M = 1, 2, 4, ..., 128.
+
+One step = one call per M in the sweep (the whole multiply path for that batch).  `value` is
+the sweep's algorithmic bytes divided by its wall time, inputs resident in HBM.  Algorithmic
+bytes per call: D = 2MK (A) + KN/2 (codes) + KN/64 (scales) + 2MN (C); flops F = 2MKN.
+Roofline per call: T_bound = max(D / 8 TB/s, F / 2.5 PFLOP/s); fp16-weight byte bound
+D16 = 2MK + 2KN + 2MN (the MARLIN paper's uncompressed reference point).
+
+Prints one JSON line on stdout.  Single GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMM effective GB/s (% HBM peak) + TFLOP/s at M=1..128, vs 3.87x bound"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix
+GROUP = 128
+
+
+def algorithmic_bytes(M, K, N):
+    return 2 * M * K + K * N // 2 + K * N // 64 + 2 * M * N
+
+
+def fp16_weight_bytes(M, K, N):
+    return 2 * M * K + 2 * K * N + 2 * M * N
+
+
+def flops(M, K, N):
+    return 2 * M * K * N
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(A, q, s, Ms, ncols, nthreads):
+    """The oracle as it stands, on a column sample of the same workload and every M."""
+    import oracle
+    K = q.shape[0]
+    qc = np.ascontiguousarray(q[:, :ncols])
+    sc = np.ascontiguousarray(s[:, :ncols])
+    t = time.perf_counter()
+    for M in Ms:
+        oracle.gemm(A[:M], qc, sc, nthreads=nthreads)
+    dt = time.perf_counter() - t
+    byts = sum(algorithmic_bytes(M, K, ncols) for M in Ms)
+    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"all M in {list(Ms)}, K={K}, first {ncols} of the N columns "
+                      f"(the same draws as the GPU run); {dt:.1f} s of CPU time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-cols", type=int, default=16384,
+                    help="columns of the CPU-baseline sample (0 skips it)")
+    ap.add_argument("--copies", type=int, default=2,
+                    help="weight copies rotated between calls so no call hits the MALL")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixed_precision_w4a16_amd as w4
+    from workloads import LARGE, draw
+
+    shape = LARGE.shapes[0]
+    K, N, Ms = shape.K, shape.N, shape.Ms
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    t = time.perf_counter()
+    A, q, s = draw(K, N, max(Ms), seed=0, sigma=shape.sigma)
+    packed, sp = w4.pack(q, s)
+    log(f"inputs drawn and packed in {time.perf_counter() - t:.1f} s")
+    pd, sd = w4.to_device(packed, sp, dev)
+    del packed, sp
+    copies = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(args.copies - 1)]
+    Ad = torch.from_numpy(A).to(dev)
+    outs = {M: torch.empty((M, N), dtype=torch.float16, device=dev) for M in Ms}
+    ws = w4.new_workspace(max(Ms), K, N, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ncall = [0]
+
+    def call(M):
+        p_, s_ = copies[ncall[0] % len(copies)]
+        ncall[0] += 1
+        w4.gemm(Ad[:M], p_, s_, N, out=outs[M], ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        for M in Ms:
+            call(M)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, each one call per M, with a HIP event pair around every call
+    # on the stream the kernels run on.
+    ev = {M: [] for M in Ms}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for M in Ms:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(M)
+            e1.record(stream)
+            ev[M].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    sweep = []
+    tot_bytes = tot_us = 0.0
+    for M in Ms:
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev[M]])) * 1e3
+        D, D16, F = algorithmic_bytes(M, K, N), fp16_weight_bytes(M, K, N), flops(M, K, N)
+        t_bound = max(D / (HBM_PEAK_GBPS * 1e3), F / (MFMA_F16_PEAK_TFLOPS * 1e6))   # us
+        gbps = D / us / 1e3
+        sweep.append({
+            "M": M, "us": round(us, 2), "GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "TFLOPs": round(F / us / 1e6, 2),
+            "mfma_frac": round(F / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
+            "roofline_frac": round(t_bound / us, 4),
+            "bound": "hbm" if D / HBM_PEAK_GBPS >= F / (MFMA_F16_PEAK_TFLOPS * 1e3) else "mfma",
+            "speedup_vs_fp16_weight_bound": round(D16 / (HBM_PEAK_GBPS * 1e3) / us, 3),
+        })
+        tot_bytes += D
+        tot_us += us
+        log(f"M={M:4d}  {us:8.1f} us  {gbps:7.0f} GB/s ({gbps / HBM_PEAK_GBPS:5.1%} HBM)  "
+            f"{F / us / 1e6:7.1f} TFLOP/s  roofline {t_bound / us:5.1%}  "
+            f"vs fp16 bound {D16 / (HBM_PEAK_GBPS * 1e3) / us:4.2f}x")
+
+    ms_per_step = wall / args.steps * 1e3
+    value = tot_bytes * args.steps / wall / 1e9
+    achieved = tot_bytes / tot_us / 1e3          # GB/s, from the per-launch event durations
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": LARGE.name, "K": K, "N": N, "M": list(Ms), "group": GROUP,
+                   "weights": "int4 codes + fp16 scales (4.125 bits/weight)",
+                   "weight_copies_rotated": args.copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "kernel": "w4a16_gemm_kernel (all M of the sweep; mean bytes / mean time)"},
+        "sweep": sweep,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    if args.cpu_cols > 0:
+        nthreads = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(A, q, s, Ms, args.cpu_cols, nthreads)
+        log(f"cpu baseline: {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * w4a16.h -- C ABI of libw4a16: the FP16 x INT4 (group-128) linear layer on one MI355X (gfx950).
+ *
+ *   C[M x N] = A[M x K] * Bhat[K x N],   Bhat[k][n] = s[k / 128][n] * (q[k][n] - 8)
+ *
+ * A and C are fp16, q are 4-bit codes 0..15, s are fp16 scales, one per 128 consecutive rows
+ * of each column; products are accumulated in fp32 and C is rounded to fp16 once
+ * (round-to-nearest-even).
+ *   Problem statement: MARLIN paper (arXiv 2408.11743) sec. 3.4 "Kernel Design" (A fp16,
+ *   B symmetrically quantised to INT4 with one FP16 scale per G consecutive weights of a
+ *   column); Marlin deep-dive page "Marlin 完全拆解", section "Marlin 要解决的精确问题"
+ *   (dequantisation s_{g,n}(q_{k,n} - z) with the symmetric zero point folded to 8).
+ *   Interface shape: Marlin README page, usage section (an offline pack step that reorders
+ *   weights and scales, then a multiply call on pre-packed data).
+ *
+ * Conventions for every entry point:
+ *   - fp16 values travel as their IEEE binary16 bit patterns (uint16_t on the host side).
+ *   - Matrices are dense row-major with no padding: A is M x K, C is M x N, codes K x N,
+ *     scales (K/128) x N.
+ *   - Sizes are int; a negative size is W4A16_EINVAL.  All arguments are checked before
+ *     anything runs; on an error nothing is written.
+ *   - The library never takes ownership of a pointer and never allocates device memory.
+ *   - Errors are return codes; nothing is thrown or aborted across this boundary.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_GROUP 128           /* rows per scale group (the only group size supported) */
+#define W4A16_N_ALIGN 64          /* N must be a multiple of this */
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_EINVAL = -1,            /* null pointer, negative size, a code above 15 */
+    W4A16_ESHAPE = -2,            /* group != 128, K not a positive multiple of 128,
+                                     N not a multiple of 16 (pack) or 64 (gemm), or a
+                                     size limit of w4a16_gemm exceeded */
+    W4A16_EUNSUPPORTED = -3,      /* the current HIP device is not a gfx950 GPU */
+    W4A16_EHIP = -4               /* a HIP runtime call or the kernel launch failed */
+} w4a16_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *w4a16_status_string(int status);
+
+/*
+ * Offline reorder of codes and scales into the layout w4a16_gemm streams.
+ * Host memory, synchronous, no GPU needed.  Follows the pages' one-time load step that
+ * permutes weights and scales so the kernel's loads land directly in its operand registers
+ * (deep-dive page, sections "直接生成 MMA 所需的寄存器 fragment" and "全局内存布局";
+ * MARLIN paper sec. 3.4 "Maximizing Loading Bandwidth": weights are static, so tiles are
+ * reshuffled offline to be contiguous).
+ *
+ *   codes      [in]  uint8 [K*N], row-major (k, n), one code 0..15 per byte
+ *   scales     [in]  fp16 bits [(K/128)*N], row-major (g, n)
+ *   group      [in]  must be 128
+ *   packed_out [out] uint32 [K*N/8]
+ *   scales_out [out] fp16 bits [(K/128)*N]
+ *
+ * Packed layout (the part of this ABI a caller may rely on; 4.125 bits per weight):
+ *   The weight matrix is cut into blocks of 128 rows (one scale group) x 16 columns.  Block
+ *   (j, g) -- columns 16j..16j+15, rows 128g..128g+127 -- is 256 consecutive uint32 words
+ *   starting at word (j*(K/128) + g)*256, so the blocks of one 16-column slab follow each
+ *   other down K.  Word 4*l + t of a block (l = 0..63, t = 0..3) holds the 8 codes of
+ *   column 16j + (l mod 16), rows 128g + 32t + 8*(l div 16) + i for i = 0..7, code i in
+ *   nibble p(i) (bits 4p..4p+3) with p = {0, 4, 1, 5, 2, 6, 3, 7}.
+ *   scales_out[(j*(K/128) + g)*16 + c] = scales[g][16j + c], c = 0..15.
+ *
+ * Returns W4A16_OK, W4A16_EINVAL (null pointer, negative size, a code > 15) or
+ * W4A16_ESHAPE (group != 128, K not a positive multiple of 128, N not a positive multiple
+ * of 16).
+ */
+int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int group,
+               uint32_t *packed_out, uint16_t *scales_out);
+
+/*
+ * Exact inverse of w4a16_pack (host, synchronous).  For tests and tooling; not on the
+ * multiply path.  Same arguments and errors as w4a16_pack with inputs and outputs swapped.
+ */
+int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packed, int K, int N, int group,
+                 uint8_t *codes_out, uint16_t *scales_out);
+
+/*
+ * Bytes of device workspace w4a16_gemm needs for this shape on the current device (a fixed
+ * 4 KiB counter area plus room for fp32 partial output tiles), written to *bytes.
+ * A workspace sized for one shape may be reused for any shape whose requirement is not
+ * larger.  Returns W4A16_OK, W4A16_EINVAL (bytes == NULL, negative size), W4A16_ESHAPE
+ * (as w4a16_gemm), W4A16_EUNSUPPORTED (current device is not gfx950) or W4A16_EHIP.
+ */
+int w4a16_workspace_size(int M, int K, int N, size_t *bytes);
+
+/*
+ * C = A * Bhat on the current HIP device, enqueued on `stream` (a hipStream_t passed as
+ * void*; NULL means the null stream).  Asynchronous: returns once the work is enqueued.
+ *
+ *   A          [in]  device, fp16 [M*K] row-major
+ *   packed     [in]  device, uint32 [K*N/8] from w4a16_pack
+ *   scales     [in]  device, fp16 bits [(K/128)*N] from w4a16_pack (scales_out)
+ *   C          [out] device, fp16 [M*N] row-major, every element overwritten
+ *   workspace  [in/out] device, at least w4a16_workspace_size(M, K, N) bytes.  Its first
+ *                  4 KiB must be zero before the first call (zero it once after allocation);
+ *                  every call leaves them zero again.  One workspace must not be used by
+ *                  two calls that can run at the same time.
+ *
+ * The weight matrix is split into column slices and each slice's K range into 128-row
+ * tiles; workgroups take equal runs of consecutive tiles ("stripes", deep-dive page
+ * section "Split-K 与全局归约"; MARLIN README page, striped partitioning).  A slice shared
+ * by several workgroups is summed in fp32 in a fixed order, so results are identical from
+ * run to run.
+ *
+ * Alignment: A, packed and scales must be 16-byte aligned (any hipMalloc pointer is).
+ * Limits: (M + 64) * K * 2 and K * N / 2 must each be below 2^32 bytes.
+ *
+ * M == 0 is a no-op returning W4A16_OK.  Errors: W4A16_EINVAL (null pointer, negative
+ * size), W4A16_ESHAPE (K not a positive multiple of 128, N not a positive multiple of 64,
+ * a limit above exceeded), W4A16_EUNSUPPORTED (current device is not gfx950),
+ * W4A16_EHIP (launch failure).
+ */
+int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
+               int M, int K, int N, void *workspace, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,173 @@
+"""Thin Python binding of libw4a16 (the C ABI declared in include/w4a16.h).
+
+Argument marshalling only: every step of the multiply runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  Importing this package fails loudly
+when the compiled library is missing; there is no fallback path.
+
+    packed, scales_p = pack(codes, scales)          # host, offline (numpy in, numpy out)
+    packed_d, scales_d = to_device(packed, scales_p)
+    C = gemm(A, packed_d, scales_d, N)              # A: fp16 [M, K] on the GPU
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+GROUP = 128
+N_ALIGN = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(or python mixed_precision_w4a16_amd/build.py) first")
+
+# PyTorch ships its own HIP runtime (same SONAME as the system one, but its own libraries ask
+# for it under another file name).  Loading torch first makes this library bind to that one
+# runtime; loading this library first would leave two HIP runtimes in the process.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:
+    _torch = None
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i = ctypes.c_void_p, ctypes.c_int
+_lib.w4a16_status_string.argtypes = [_i]
+_lib.w4a16_status_string.restype = ctypes.c_char_p
+_lib.w4a16_pack.argtypes = [_p, _p, _i, _i, _i, _p, _p]
+_lib.w4a16_pack.restype = _i
+_lib.w4a16_unpack.argtypes = [_p, _p, _i, _i, _i, _p, _p]
+_lib.w4a16_unpack.restype = _i
+_lib.w4a16_workspace_size.argtypes = [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+_lib.w4a16_workspace_size.restype = _i
+_lib.w4a16_gemm.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _p]
+_lib.w4a16_gemm.restype = _i
+
+OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_size",
+            "w4a16_gemm")
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.w4a16_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise W4A16Error(fn, status)
+
+
+def library():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+# ------------------------------------------------------------------------------ host side
+
+def pack(codes: np.ndarray, scales: np.ndarray, group: int = GROUP):
+    """Offline reorder.  codes uint8 [K, N] (0..15), scales fp16 [K/group, N] ->
+    (packed uint32 [K*N/8], scales_packed fp16 [(K/group)*N])."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float16)
+    K, N = codes.shape
+    packed = np.empty(K * N // 8, dtype=np.uint32)
+    scales_p = np.empty(scales.size, dtype=np.float16)
+    if scales.shape != (K // group if group else 0, N):
+        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
+    _check("w4a16_pack", _lib.w4a16_pack(codes.ctypes.data, scales.ctypes.data, K, N, group,
+                                         packed.ctypes.data, scales_p.ctypes.data))
+    return packed, scales_p
+
+
+def unpack(packed: np.ndarray, scales_p: np.ndarray, K: int, N: int, group: int = GROUP):
+    """Inverse of pack: (codes uint8 [K, N], scales fp16 [K/group, N])."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    scales_p = np.ascontiguousarray(scales_p, dtype=np.float16)
+    if packed.size != K * N // 8 or scales_p.size != (K // group) * N:
+        raise ValueError("size mismatch")
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty((K // group, N), dtype=np.float16)
+    _check("w4a16_unpack", _lib.w4a16_unpack(packed.ctypes.data, scales_p.ctypes.data, K, N,
+                                             group, codes.ctypes.data, scales.ctypes.data))
+    return codes, scales
+
+
+# ------------------------------------------------------------------------------ device side
+
+def to_device(packed: np.ndarray, scales_p: np.ndarray, device="cuda"):
+    """Upload pack() output: (int32 tensor holding the uint32 words, fp16 tensor)."""
+    import torch
+    return (torch.from_numpy(np.ascontiguousarray(packed).view(np.int32)).to(device),
+            torch.from_numpy(np.ascontiguousarray(scales_p)).to(device))
+
+
+def workspace_bytes(M: int, K: int, N: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("w4a16_workspace_size", _lib.w4a16_workspace_size(M, K, N, ctypes.byref(n)))
+    return n.value
+
+
+_ws_lock = threading.Lock()
+_ws = {}
+
+
+def workspace(M: int, K: int, N: int, device=None):
+    """A zeroed workspace large enough for (M, K, N), cached per device and grown on demand.
+    Calls on different streams that may overlap need workspaces of their own (see
+    new_workspace)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    need = workspace_bytes(M, K, N)
+    with _ws_lock:
+        buf = _ws.get(dev)
+        if buf is None or buf.numel() < need:
+            buf = torch.zeros(need, dtype=torch.uint8, device=dev)
+            _ws[dev] = buf
+        return buf
+
+
+def new_workspace(M: int, K: int, N: int, device="cuda"):
+    import torch
+    return torch.zeros(workspace_bytes(M, K, N), dtype=torch.uint8, device=device)
+
+
+def gemm(A, packed, scales, N: int, out=None, ws=None, stream=None):
+    """C[M, N] = A[M, K] @ dequant(packed, scales) on A's device and the current stream.
+
+    A: fp16 [M, K] contiguous CUDA tensor.  packed: int32 [K*N/8], scales: fp16 [(K/128)*N],
+    both from to_device(pack(...)).  out: optional fp16 [M, N] contiguous tensor.
+    """
+    import torch
+    if A.dtype != torch.float16 or not A.is_cuda or A.dim() != 2 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous fp16 CUDA tensor of shape [M, K]")
+    M, K = A.shape
+    if packed.device != A.device or scales.device != A.device:
+        raise ValueError("packed and scales must be on A's device")
+    if packed.dtype != torch.int32 or packed.numel() * 8 != K * N or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous int32 tensor of K*N/8 words")
+    if scales.dtype != torch.float16 or scales.numel() * GROUP != K * N or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp16 tensor of (K/128)*N values")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    elif (out.dtype != torch.float16 or out.shape != (M, N) or not out.is_contiguous()
+          or out.device != A.device):
+        raise ValueError("out must be a contiguous fp16 tensor [M, N] on A's device")
+    if M == 0:
+        return out
+    with torch.cuda.device(A.device):
+        if ws is None:
+            ws = workspace(M, K, N, A.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        _check("w4a16_gemm", _lib.w4a16_gemm(A.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                                             out.data_ptr(), M, K, N, ws.data_ptr(),
+                                             stream.cuda_stream))
+    return out

@@ -1,0 +1,52 @@
+"""Compile libw4a16.so for gfx950 in-tree with hipcc (runs on a machine without a GPU)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "pack.cpp")]
+LIB = os.path.join(PKG, "libw4a16.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def command(out: str = LIB, extra=()) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # code object v5 loads in the HIP runtime PyTorch bundles as well as the system one
+            "-mcode-object-version=5",
+            "-Wall", "-Wno-unused-function",
+            # packed fp32 arithmetic stays off (plain fp32 only in this library)
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in ordinary VGPRs: the fp32 epilogue math reads them directly
+            # instead of copying each accumulator out of the AGPR file first
+            "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
+            "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", out, *extra]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [l for l in (res.stdout + res.stderr).splitlines()
+            if "packed-fp32-ops' is not a recognized feature" not in l]
+    if res.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,617 @@
+// FP16 x INT4 (group-128) linear layer for CDNA4 (gfx950): C = A * Bhat,
+// Bhat[k][n] = s[k/128][n] * (q[k][n] - 8), fp32 accumulation, fp16 output.
+//
+// Design (the pages' Ampere kernel is prior art; what carries over is kept, the rest is
+// rebuilt for 64-lane waves, MFMA, LDS and a 256-CU chip):
+//
+// * Weight stream.  The packed codes (layout in w4a16.h) are read with one 128-bit
+//   non-temporal load per lane per 128x16 block -- 1 KiB contiguous per wave -- straight into
+//   the registers that feed the matrix cores; no fp16 copy of the weights exists anywhere.
+//   Pages: MARLIN paper sec. 3.4 "Maximizing Loading Bandwidth" (widest loads, full lines,
+//   weights read once with an evict-first hint).
+// * Activations.  Each lane loads its own A fragments (16 bytes = 8 consecutive k of one
+//   row) straight from global memory into MFMA operand registers.  The four waves of a
+//   workgroup walk the same K tiles of adjacent column ranges in step, so they read the same
+//   A bytes and the vector L1 serves the repeats; A is re-read from L2 once per column slice
+//   (the pages' reason for wide N tiles: MARLIN paper sec. 3.4 "Bound By Weight Loading",
+//   Eq. (1)).  Loads are issued one tile ahead, in the order they are consumed, because the
+//   vector-memory counter completes in order (the pages' multi-stage prefetch, sec. 3.4
+//   "Memory Load Pipelining").  There is no LDS staging and no barrier in the main loop.
+// * Dequantisation.  One 32-bit word holds 8 codes; mask-and-OR into the fp16 exponent
+//   0x6400 gives 1024 + q (low nibbles) or 1024 + 16q (high nibbles), and one packed fp16
+//   add or FMA per pair returns q - 8 exactly.  Deep-dive page "Marlin 完全拆解", section
+//   "INT4 只是存储类型，不是这条路径的计算类型".
+// * Scales.  The MFMA sums A * (q - 8) over one 128-row group in fp32 (exact products);
+//   that partial is multiplied by the group's scale and added to the running fp32 sum.
+//   This is the grouped sum C = sum_g s_g sum_{k in g} A (q - 8) written out on the deep-dive
+//   page (section "scale 为什么有时在内环乘，有时在末尾乘"); it costs 4 FMAs per 16x16
+//   output tile per group instead of one fp16 multiply per weight.
+// * Contraction: v_mfma_f32_16x16x32_f16, tokens as the 16 rows, output columns as the 16
+//   columns; k-step loop outermost so independent accumulators separate dependent MFMAs
+//   (MARLIN paper sec. 3.2 "Tensor Core Level").
+// * Scheduling.  Tiles are 128 (K) x Nt (N) x Mt (M rows).  Tile order: column slice, then
+//   64-row M sub-problem, then K (weights of a slice are re-read from cache for the next M
+//   sub-problem: the pages' "virtual replication" of the weight grid for large M).  Each
+//   workgroup takes one contiguous run of floor/ceil(T/W) tiles (a stripe), so every CU gets
+//   the same work and only stripe ends split a slice.  Pages: deep-dive page sections
+//   "为什么规则二维网格会浪费最后一波 SM" and "大 M 时虚拟复制权重网格"; MARLIN README
+//   page, striped partitioning.  Workgroup ids are remapped so consecutive stripes sit on
+//   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs).
+// * Cross-workgroup reduction.  A slice split between stripes is summed without any
+//   waiting: each contributor writes its fp32 partial tile to its own workspace slot,
+//   fences, and bumps the slice's counter; the contributor that finds itself last adds all
+//   partials in stripe order (a fixed order, so results are bitwise repeatable), writes C,
+//   and resets the counter.  The pages sum such partials serially with locks and stage them
+//   in fp16 in the output (deep-dive page section "为什么归约串行，却不一定慢"); fp32
+//   partials and a last-arriver sum keep the same "no big temporary" property, keep full
+//   precision, and never spin, so no co-residency assumption is needed.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+
+#include "w4a16.h"
+
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;                 // 4 waves of 64
+constexpr int kWaves = 4;
+constexpr int kGroup = 128;                   // K rows per tile = one scale group
+constexpr size_t kCounterBytes = 4096;        // fixed counter area at the workspace start
+constexpr int kMaxWGs = static_cast<int>(kCounterBytes / sizeof(int));
+
+struct Params {
+    const uint16_t *A;        // fp16 [M][K]
+    const u4 *packed;         // 16-byte quads, 64 per 128x16 block
+    const uint16_t *scales;   // fp16 bits, 16 per block
+    uint16_t *C;              // fp16 [M][N]
+    int *counters;            // kMaxWGs ints, zero between calls
+    float *partials;          // 2 * W slots of Mt*Nt floats
+    int M, K, N;
+    int G;                    // K / 128: tiles per slice
+    int P;                    // M sub-problems of Mt rows
+    int W;                    // workgroups = stripes
+    long long T;              // total tiles = (N / Nt) * P * G
+};
+
+// (a & m) | o in one VALU op.  gfx9 VOP3 encodings take no literal and read at most one
+// SGPR, so left to itself the compiler splits this into v_and + v_or; the "v" constraints
+// keep both constants in (loop-invariant) VGPRs instead.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+    return r;
+}
+
+// 8 codes -> 8 fp16 values q - 8, in MFMA B-operand order (see pack.cpp for the nibbles).
+// 9 VALU ops per 8 weights: 4 mask-and-OR, 1 shift, 2 packed adds, 2 packed FMAs.
+__device__ __forceinline__ h8 dequant8(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic)
+{
+    const uint32_t w8 = w >> 8;
+    const uint32_t x0 = and_or(w, mlo, magic);     // k0, k1: fp16 1024 + q
+    const uint32_t x1 = and_or(w, mhi, magic);     // k2, k3: fp16 1024 + 16 q
+    const uint32_t x2 = and_or(w8, mlo, magic);    // k4, k5
+    const uint32_t x3 = and_or(w8, mhi, magic);    // k6, k7
+    const h2 sub = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+    const h2 add = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+    const h2 y0 = __builtin_bit_cast(h2, x0) - sub;                                // q - 8
+    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, add); // q - 8
+    const h2 y2 = __builtin_bit_cast(h2, x2) - sub;
+    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, add);
+    h8 r;
+    r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
+    r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
+    return r;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float x)
+{
+    // v_cvt_f16_f32: one rounding, nearest-even in the default mode
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// First tile of stripe r, and the stripe that owns tile t (stripes are [r*T/W, (r+1)*T/W)).
+__device__ __forceinline__ long long stripe_begin(long long r, long long T, int W)
+{
+    return r * T / W;
+}
+__device__ __forceinline__ int stripe_owner(long long t, long long T, int W)
+{
+    return static_cast<int>(((t + 1) * W - 1) / T);
+}
+
+template <int MB, int NBW>
+struct Tile {
+    static constexpr int Mt = 16 * MB;                 // rows per M sub-problem
+    static constexpr int Nt = 16 * NBW * kWaves;       // columns per slice
+    static constexpr int kSlotFloats = Mt * Nt;
+};
+
+// Raw buffer resources: base, size in bytes, gfx9 dword-access flags.  Loads past `bytes`
+// return zero, which masks the rows of A beyond M for free.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+constexpr int kNonTemporal = 2;    // buffer-load cache policy: streaming, evict first
+
+// Where the next tile's loads come from.  Tiles run in (slice, M sub-problem, K) order;
+// inside a slice only the K step changes and every offset moves by a constant.
+struct LoadCursor {
+    int g, pm, s;
+    uint32_t wblk;      // block index of this wave's first slab at K step g (uniform)
+    uint32_t a_soff;    // byte offset of K step g in an A row (uniform)
+};
+
+template <int MB, int NBW>
+__device__ __forceinline__ void load_cursor_set(const Params &p, int wave, LoadCursor &c)
+{
+    c.wblk = (static_cast<uint32_t>(c.s) * (kWaves * NBW) + wave * NBW) * p.G + c.g;
+    c.a_soff = static_cast<uint32_t>(c.g) * (kGroup * 2);
+}
+
+// This lane's byte offsets into A for each 16-row sub-tile: row arow + 16mb + lane%16,
+// column 8(lane/16) (the first k of its fragment in MFMA k-step 0).
+template <int MB>
+__device__ __forceinline__ void a_lane_offsets(const Params &p, int lane, int arow,
+                                               uint32_t (&voff)[MB])
+{
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        voff[mb] = (static_cast<uint32_t>(arow + 16 * mb + (lane & 15)) * p.K + 8 * (lane >> 4)) * 2;
+}
+
+// A fragments of one tile: 16 bytes = k 32t + 8(lane/16) .. +7 of row lane%16, per k-step
+// t and sub-tile mb.  Rows at or past M fall outside the buffer and read as zero.
+template <int MB>
+__device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t rA, const uint32_t (&voff)[MB],
+                                       uint32_t soff_in, u4 (&af)[MB][4])
+{
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(soff_in);   // uniform: keep in SGPR
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            af[mb][t] = __builtin_bit_cast(
+                u4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[mb] + 64 * t, soff, 0));
+}
+
+// This wave's packed weight quads (1 KiB contiguous per slab, non-temporal) and scales.
+template <int NBW>
+__device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
+                                       int G, int lane, uint32_t wblk, u4 (&wq)[NBW],
+                                       uint32_t (&sc)[NBW])
+{
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+        const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
+        wq[b] = __builtin_bit_cast(
+            u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, kNonTemporal));
+        // the aligned dword holding this column's scale and its neighbour's (a 16-bit load
+        // result would be re-copied across the loop back-edge)
+        sc[b] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, blk * 32u, 0);
+    }
+}
+
+template <int MB, int NBW>
+__device__ __forceinline__ void compute_tile(const u4 (&af)[MB][4], const u4 (&wq)[NBW],
+                                             const uint32_t (&sc)[NBW], f4 (&acc)[MB][NBW],
+                                             uint32_t mlo, uint32_t mhi, uint32_t magic)
+{
+    // Scales first: converting them here ends the loaded registers' live range before the
+    // next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
+    const int sshift = (threadIdx.x & 1) * 16;        // odd columns: high half of the dword
+    float sf[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+        sf[b] = half_bits_to_float(static_cast<uint16_t>(sc[b] >> sshift));
+        asm volatile("" : "+v"(sf[b]));
+    }
+    f4 part[MB][NBW];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const h8 bw = dequant8(wq[b][t], mlo, mhi, magic);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const f4 cin = (t == 0) ? f4{0.f, 0.f, 0.f, 0.f} : part[mb][b];
+                part[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(h8, af[mb][t]), bw, cin, 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[mb][b][r] = __builtin_fmaf(sf[b], part[mb][b][r], acc[mb][b][r]);
+            asm volatile("" : "+v"(acc[mb][b]));        // finish the update here
+        }
+}
+
+// acc[mb][b][r] is C[row0 + 16mb + 4(lane/16) + r][col0 + 16b + lane%16].
+template <int MB, int NBW>
+__device__ __forceinline__ void write_c(const Params &p, int wave, int lane, long long sigma,
+                                        const f4 (&acc)[MB][NBW])
+{
+    const long long s = sigma / p.P;
+    const int pm = static_cast<int>(sigma - s * p.P);
+    const int row0 = pm * 16 * MB + 4 * (lane >> 4);
+    const size_t col0 = static_cast<size_t>(s) * Tile<MB, NBW>::Nt + wave * NBW * 16 + (lane & 15);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 16 * mb + r;
+                if (row < p.M)
+                    p.C[static_cast<size_t>(row) * p.N + col0 + 16 * b] =
+                        float_to_half_bits(acc[mb][b][r]);
+            }
+}
+
+template <int MB, int NBW>
+__device__ __forceinline__ f4 *slot_ptr(const Params &p, int stripe, int slot, int wave, int mb,
+                                        int b, int lane)
+{
+    float *base = p.partials + (static_cast<size_t>(stripe) * 2 + slot) * Tile<MB, NBW>::kSlotFloats;
+    return reinterpret_cast<f4 *>(base) + ((wave * MB + mb) * NBW + b) * 64 + lane;
+}
+
+// End of this stripe's share of slice sigma (its tiles [max(t0, first of slice), last]).
+template <int MB, int NBW>
+__device__ __forceinline__ void finish_slice(const Params &p, int stripe, long long t0, long long last,
+                                             long long sigma, int tid, f4 (&acc)[MB][NBW],
+                                             int *flag)
+{
+    const int wave = tid >> 6, lane = tid & 63;
+    const long long s0 = sigma * p.G;
+    const long long first = t0 > s0 ? t0 : s0;
+    if (first == s0 && last == s0 + p.G - 1) {
+        write_c<MB, NBW>(p, wave, lane, sigma, acc);          // sole owner of the slice
+        return;
+    }
+    const int w_lo = stripe_owner(s0, p.T, p.W);
+    const int w_hi = stripe_owner(s0 + p.G - 1, p.T, p.W);
+    const int my_slot = (sigma == t0 / p.G) ? 0 : 1;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+            *slot_ptr<MB, NBW>(p, stripe, my_slot, wave, mb, b, lane) = acc[mb][b];
+    __threadfence();          // release this thread's partial at device scope
+    __syncthreads();
+    if (tid == 0)
+        *flag = atomicAdd(p.counters + w_lo, 1);
+    __syncthreads();
+    const int arrived = *flag;
+    __syncthreads();          // everyone has read the flag before it can be reused
+    if (arrived != w_hi - w_lo)
+        return;               // another contributor is still running; it will finish
+    __threadfence();          // acquire the other contributors' partials
+
+    f4 sum[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+            sum[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int w = w_lo; w <= w_hi; ++w) {                      // fixed order: along K
+        const int slot = (sigma == stripe_begin(w, p.T, p.W) / p.G) ? 0 : 1;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const f4 v = (w == stripe) ? acc[mb][b]
+                                           : *slot_ptr<MB, NBW>(p, w, slot, wave, mb, b, lane);
+                sum[mb][b] += v;
+            }
+    }
+    write_c<MB, NBW>(p, wave, lane, sigma, sum);
+    if (tid == 0)
+        atomicExch(p.counters + w_lo, 0);                     // ready for the next call
+}
+
+template <int MB, int NBW>
+__global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
+{
+    __shared__ int flag;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int lane = tid & 63;
+
+    // XCD-aware stripe id: hardware workgroup b runs on XCD b % 8; give each XCD a
+    // contiguous block of stripes.
+    int stripe = blockIdx.x;
+    if ((p.W & 7) == 0)
+        stripe = (blockIdx.x & 7) * (p.W >> 3) + (blockIdx.x >> 3);
+
+    const long long t0 = stripe_begin(stripe, p.T, p.W);
+    const long long t1 = stripe_begin(stripe + 1, p.T, p.W);
+    if (t0 >= t1)
+        return;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
+    const __amdgpu_buffer_rsrc_t rS =
+        make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
+
+    // dequant constants in VGPRs for v_and_or_b32
+    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+
+    f4 acc[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+            acc[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
+
+    // Compute position: tile t, its K step g and slice sigma.
+    long long t = t0;
+    long long sigma = t0 / p.G;
+    int g = static_cast<int>(t0 - sigma * p.G);
+
+    // Load position, kept one tile ahead of the next compute and clamped to the stripe's
+    // last tile, so every load is unconditional (a re-read of the last tile is a cache hit).
+    LoadCursor lc;
+    lc.g = g;
+    lc.s = static_cast<int>(sigma / p.P);
+    lc.pm = static_cast<int>(sigma - static_cast<long long>(lc.s) * p.P);
+    load_cursor_set<MB, NBW>(p, wave, lc);
+    uint32_t a_voff[MB];
+    a_lane_offsets<MB>(p, lane, lc.pm * 16 * MB, a_voff);
+    long long lt = t0;                 // tile lc points at
+
+    auto step_load = [&]() {
+        if (lt + 1 < t1) {
+            ++lt;
+            ++lc.g;
+            ++lc.wblk;
+            lc.a_soff += kGroup * 2;
+            if (lc.g == p.G) {         // next slice (uniform, rare)
+                lc.g = 0;
+                if (++lc.pm == p.P) {
+                    lc.pm = 0;
+                    ++lc.s;
+                }
+                load_cursor_set<MB, NBW>(p, wave, lc);
+                a_lane_offsets<MB>(p, lane, lc.pm * 16 * MB, a_voff);
+            }
+        }
+    };
+
+    // Two register buffers: tile i is computed from buffer i % 2 while tile i + 1's loads
+    // are in flight.  Every load of a tile is issued before any load of the next tile, and
+    // the vector-memory counter completes in order, so waiting for one tile never waits for
+    // a later one.
+    u4 af0[MB][4], af1[MB][4];
+    u4 wq0[NBW], wq1[NBW];
+    uint32_t sc0[NBW], sc1[NBW];
+
+    load_a<MB>(rA, a_voff, lc.a_soff, af0);
+    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);
+    step_load();
+    load_a<MB>(rA, a_voff, lc.a_soff, af1);
+    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);
+    step_load();
+
+    auto end_of_tile = [&]() {
+        if (g == p.G - 1 || t + 1 == t1) {
+            finish_slice<MB, NBW>(p, stripe, t0, t, sigma, tid, acc, &flag);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                    acc[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+        ++t;
+        if (++g == p.G) {
+            g = 0;
+            ++sigma;
+        }
+    };
+
+    // Loop over whole pairs of tiles (even tile from buffer 0, odd from buffer 1); a single
+    // trailing tile is finished after the loop.  Exiting only at the end of a pair keeps the
+    // control flow simple enough for the compiler to wait for exactly one tile's loads.
+    // The asm/scheduling barriers keep each tile's loads after the last use of the registers
+    // they overwrite; otherwise the two live ranges overlap and the register allocator adds
+    // loop-carried copies that must wait for the loads.
+    while (t + 1 < t1) {
+        compute_tile<MB, NBW>(af0, wq0, sc0, acc, mlo, mhi, magic);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_a<MB>(rA, a_voff, lc.a_soff, af0);
+        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);
+        step_load();
+        end_of_tile();
+
+        compute_tile<MB, NBW>(af1, wq1, sc1, acc, mlo, mhi, magic);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_a<MB>(rA, a_voff, lc.a_soff, af1);
+        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);
+        step_load();
+        end_of_tile();
+    }
+    if (t < t1) {
+        compute_tile<MB, NBW>(af0, wq0, sc0, acc, mlo, mhi, magic);
+        end_of_tile();
+    }
+}
+
+// ------------------------------------------------------------------------------- host side
+
+struct DeviceInfo {
+    bool queried = false;
+    bool gfx950 = false;
+    int cus = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+int current_device(DeviceInfo *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return W4A16_EHIP;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.queried) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return W4A16_EHIP;
+        const char *a = prop.gcnArchName;
+        d.gfx950 = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
+                   a[5] == '0' && (a[6] == '\0' || a[6] == ':');
+        d.cus = prop.multiProcessorCount;
+        d.queried = true;
+    }
+    *out = d;
+    return d.gfx950 ? W4A16_OK : W4A16_EUNSUPPORTED;
+}
+
+struct Config {
+    int MB, NBW;     // M sub-tiles of 16 rows; 16-column slabs per wave
+    int P, S, G, W;
+    long long T;
+};
+
+int check_gemm_shape(int M, int K, int N)
+{
+    if (M < 0 || K < 0 || N < 0)
+        return W4A16_EINVAL;
+    if (K == 0 || K % kGroup || N == 0 || N % W4A16_N_ALIGN)
+        return W4A16_ESHAPE;
+    // Buffer resources address at most 4 GiB; A offsets run up to 64 rows past M.
+    const uint64_t lim = uint64_t(1) << 32;
+    if ((static_cast<uint64_t>(M) + 64) * static_cast<uint64_t>(K) * 2 >= lim ||
+        static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= lim)
+        return W4A16_ESHAPE;
+    return W4A16_OK;
+}
+
+Config choose_config(int M, int K, int N, int cus)
+{
+    Config c{};
+    c.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int Mt = 16 * c.MB;
+    c.P = (M + Mt - 1) / Mt;
+    c.G = K / kGroup;
+    // widest slice that divides N; MB = 4 keeps 2 slabs per wave for register room
+    const int max_nbw = c.MB == 4 ? 2 : 4;
+    c.NBW = 1;
+    for (int nbw = max_nbw; nbw >= 1; nbw >>= 1)
+        if (N % (16 * kWaves * nbw) == 0) {
+            c.NBW = nbw;
+            break;
+        }
+    c.S = N / (16 * kWaves * c.NBW);
+    c.T = static_cast<long long>(c.S) * c.P * c.G;
+    long long w = static_cast<long long>(cus) * 2;
+    if (w > kMaxWGs)
+        w = kMaxWGs;
+    if (w > c.T)
+        w = c.T;
+    c.W = static_cast<int>(w);
+    return c;
+}
+
+size_t workspace_for(const Config &c)
+{
+    const size_t slot = static_cast<size_t>(16 * c.MB) * (16 * kWaves * c.NBW) * sizeof(float);
+    return kCounterBytes + 2 * static_cast<size_t>(c.W) * slot;
+}
+
+template <int MB, int NBW>
+hipError_t launch(const Params &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((w4a16_gemm_kernel<MB, NBW>), dim3(p.W), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
+{
+    if (!bytes)
+        return W4A16_EINVAL;
+    int rc = check_gemm_shape(M, K, N);
+    if (rc != W4A16_OK)
+        return rc;
+    DeviceInfo d;
+    rc = current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    *bytes = M == 0 ? kCounterBytes : workspace_for(choose_config(M, K, N, d.cus));
+    return W4A16_OK;
+}
+
+extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
+                          int M, int K, int N, void *workspace, void *stream)
+{
+    if (!A || !packed || !scales || !C || !workspace)
+        return W4A16_EINVAL;
+    int rc = check_gemm_shape(M, K, N);
+    if (rc != W4A16_OK)
+        return rc;
+    DeviceInfo d;
+    rc = current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    if (M == 0)
+        return W4A16_OK;
+
+    const Config c = choose_config(M, K, N, d.cus);
+    Params p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.packed = reinterpret_cast<const u4 *>(packed);
+    p.scales = scales;
+    p.C = static_cast<uint16_t *>(C);
+    p.counters = static_cast<int *>(workspace);
+    p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+    p.M = M;
+    p.K = K;
+    p.N = N;
+    p.G = c.G;
+    p.P = c.P;
+    p.W = c.W;
+    p.T = c.T;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (c.MB * 10 + c.NBW) {
+    case 11: e = launch<1, 1>(p, s); break;
+    case 12: e = launch<1, 2>(p, s); break;
+    case 14: e = launch<1, 4>(p, s); break;
+    case 21: e = launch<2, 1>(p, s); break;
+    case 22: e = launch<2, 2>(p, s); break;
+    case 24: e = launch<2, 4>(p, s); break;
+    case 41: e = launch<4, 1>(p, s); break;
+    case 42: e = launch<4, 2>(p, s); break;
+    default: return W4A16_EHIP;
+    }
+    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}

@@ -1,0 +1,121 @@
+// Offline weight/scale reorder for the gfx950 W4A16 kernel (host code, no GPU needed).
+//
+// The pages reorder the quantised weights once at load time so that every thread's wide
+// load delivers exactly the codes its matrix-core operand needs, with the nibbles of a word
+// in an order that a short mask-and-OR sequence turns into fp16 pairs (Marlin deep-dive page
+// "Marlin 完全拆解", sections "直接生成 MMA 所需的寄存器 fragment" and "全局内存布局";
+// MARLIN paper sec. 3.4 "Maximizing Loading Bandwidth").  The layout here is built for the
+// CDNA4 16x16x32 fp16 MFMA on 64-lane waves instead of Ampere's mma.sync fragments:
+//
+//   block (j, g) = rows 128g..128g+127 (one scale group) x columns 16j..16j+15, 1 KiB;
+//   lane l of a wave loads the block's 16-byte word quad l (one 128-bit load per lane,
+//   1 KiB contiguous per wave); word t of that quad feeds MFMA k-step t and holds column
+//   16j + l%16, rows 128g + 32t + 8(l/16) + i (i = 0..7), code i in nibble kNibble[i].
+//   Nibble pairs (0,4), (1,5), (2,6), (3,7) then become the fp16 pairs (k0,k1), (k2,k3),
+//   (k4,k5), (k6,k7) of the MFMA B operand.
+//
+// Blocks of a 16-column slab are consecutive down K, so a workgroup walking down K streams
+// contiguous memory.  Scales follow the same block order, 16 per block.
+#include "w4a16.h"
+
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+constexpr int kNibble[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+int check_shape(const void *a, const void *b, const void *c, const void *d, int K, int N,
+                int group)
+{
+    if (!a || !b || !c || !d || K < 0 || N < 0)
+        return W4A16_EINVAL;
+    if (group != W4A16_GROUP || K == 0 || N == 0 || K % W4A16_GROUP || N % 16)
+        return W4A16_ESHAPE;
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int group,
+                          uint32_t *packed_out, uint16_t *scales_out)
+{
+    int rc = check_shape(codes, scales, packed_out, scales_out, K, N, group);
+    if (rc != W4A16_OK)
+        return rc;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    for (size_t i = 0; i < nk * nn; ++i)
+        if (codes[i] > 15)
+            return W4A16_EINVAL;
+
+    const size_t G = nk / W4A16_GROUP;
+    const size_t slabs = nn / 16;
+    for (size_t j = 0; j < slabs; ++j) {
+        for (size_t g = 0; g < G; ++g) {
+            uint32_t *blk = packed_out + (j * G + g) * 256;
+            for (int l = 0; l < 64; ++l) {
+                const size_t n = j * 16 + (l & 15);
+                for (int t = 0; t < 4; ++t) {
+                    const size_t k0 = g * W4A16_GROUP + 32 * t + 8 * (l >> 4);
+                    uint32_t w = 0;
+                    for (int i = 0; i < 8; ++i)
+                        w |= static_cast<uint32_t>(codes[(k0 + i) * nn + n]) << (4 * kNibble[i]);
+                    blk[4 * l + t] = w;
+                }
+            }
+            uint16_t *sb = scales_out + (j * G + g) * 16;
+            for (int c = 0; c < 16; ++c)
+                sb[c] = scales[g * nn + j * 16 + c];
+        }
+    }
+    return W4A16_OK;
+}
+
+extern "C" int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packed, int K, int N,
+                            int group, uint8_t *codes_out, uint16_t *scales_out)
+{
+    int rc = check_shape(packed, scales_packed, codes_out, scales_out, K, N, group);
+    if (rc != W4A16_OK)
+        return rc;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    const size_t G = nk / W4A16_GROUP;
+    const size_t slabs = nn / 16;
+    for (size_t j = 0; j < slabs; ++j) {
+        for (size_t g = 0; g < G; ++g) {
+            const uint32_t *blk = packed + (j * G + g) * 256;
+            for (int l = 0; l < 64; ++l) {
+                const size_t n = j * 16 + (l & 15);
+                for (int t = 0; t < 4; ++t) {
+                    const size_t k0 = g * W4A16_GROUP + 32 * t + 8 * (l >> 4);
+                    const uint32_t w = blk[4 * l + t];
+                    for (int i = 0; i < 8; ++i)
+                        codes_out[(k0 + i) * nn + n] =
+                            static_cast<uint8_t>((w >> (4 * kNibble[i])) & 0xF);
+                }
+            }
+            const uint16_t *sb = scales_packed + (j * G + g) * 16;
+            for (int c = 0; c < 16; ++c)
+                scales_out[g * nn + j * 16 + c] = sb[c];
+        }
+    }
+    return W4A16_OK;
+}
+
+extern "C" const char *w4a16_status_string(int status)
+{
+    switch (status) {
+    case W4A16_OK:
+        return "ok";
+    case W4A16_EINVAL:
+        return "invalid argument (null pointer, negative size or code above 15)";
+    case W4A16_ESHAPE:
+        return "unsupported shape (group must be 128, K a positive multiple of 128, "
+               "N a positive multiple of 64)";
+    case W4A16_EUNSUPPORTED:
+        return "current HIP device is not a gfx950 GPU";
+    case W4A16_EHIP:
+        return "HIP runtime error";
+    default:
+        return "unknown status";
+    }
+}

@@ -1,0 +1,148 @@
+"""Host-side tests of the C ABI: exported symbols, the offline pack, argument checking.
+
+No GPU needed: w4a16_pack / w4a16_unpack are host code, and w4a16_gemm rejects bad
+arguments before touching the HIP runtime.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mixed_precision_w4a16_amd as w4
+from workloads import ALL, draw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "paper_constants.json")
+NIBBLE = [0, 4, 1, 5, 2, 6, 3, 7]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(w4.EXPORTED)
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in (w4.OK, w4.EINVAL, w4.ESHAPE, w4.EUNSUPPORTED, w4.EHIP, 12345):
+        assert w4.library().w4a16_status_string(st)
+
+
+def layout_reference(codes, scales):
+    """The packed layout exactly as include/w4a16.h states it, written with numpy indexing."""
+    K, N = codes.shape
+    G = K // 128
+    packed = np.zeros((N // 16, G, 64, 4), dtype=np.uint32)
+    l = np.arange(64)
+    for t in range(4):
+        for i in range(8):
+            k = (np.arange(G)[:, None] * 128 + 32 * t + 8 * (l[None, :] // 16) + i)   # [G, 64]
+            for j in range(N // 16):
+                n = 16 * j + (l % 16)
+                packed[j, :, :, t] |= codes[k, n[None, :]].astype(np.uint32) << np.uint32(4 * NIBBLE[i])
+    sp = scales.reshape(G, N // 16, 16).transpose(1, 0, 2).reshape(-1)
+    return packed.reshape(-1), sp
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (384, 48), (1024, 1024)])
+def test_pack_matches_documented_layout(K, N):
+    _, q, s = draw(K, N, 1, seed=K + N)
+    packed, sp = w4.pack(q, s)
+    ref_p, ref_s = layout_reference(q, s)
+    assert np.array_equal(packed, ref_p)
+    assert np.array_equal(sp.view(np.uint16), ref_s.view(np.uint16))
+
+
+def _patterns(K, N, rng):
+    yield rng.integers(0, 16, (K, N), dtype=np.uint8)
+    yield np.zeros((K, N), dtype=np.uint8)
+    yield np.full((K, N), 15, dtype=np.uint8)
+    yield ((np.arange(K)[:, None] + np.arange(N)[None, :]) % 2 * 15).astype(np.uint8)
+    yield ((np.arange(K)[:, None] * 7 + np.arange(N)[None, :] * 3) % 16).astype(np.uint8)
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (640, 208), (4096, 512)])
+def test_pack_unpack_round_trip_is_bit_exact(K, N):
+    rng = np.random.default_rng(K * N)
+    s = rng.uniform(0.005, 0.02, (K // 128, N)).astype(np.float16)
+    s[0, 0] = np.float16(-0.0)
+    s[-1, -1] = np.float16(65504.0)
+    for q in _patterns(K, N, rng):
+        packed, sp = w4.pack(q, s)
+        q2, s2 = w4.unpack(packed, sp, K, N)
+        assert np.array_equal(q2, q)
+        assert np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+
+
+def test_round_trip_at_every_workload_shape_sampled():
+    # Full-size shapes, pack/unpack on a 1024-row band (the layout is per 128-row group, so
+    # any multiple of 128 exercises the same code for every column slab of the real N).
+    for wl in ALL:
+        for sh in wl.shapes:
+            K = min(sh.K, 1024)
+            _, q, s = draw(K, sh.N, 1, seed=1)
+            packed, sp = w4.pack(q, s)
+            q2, s2 = w4.unpack(packed, sp, K, sh.N)
+            assert np.array_equal(q2, q), sh.name
+            assert np.array_equal(s2.view(np.uint16), s.view(np.uint16)), sh.name
+
+
+def test_footprint_is_4_125_bits_per_weight():
+    g = json.load(open(GOLDEN))
+    K, N = 18432, 256
+    _, q, s = draw(K, N, 1, seed=2)
+    packed, sp = w4.pack(q, s)
+    bits = (packed.nbytes + sp.nbytes) * 8 / (K * N)
+    assert bits == g["bits_per_weight_group128"]["value"]
+    # large-shape byte count at the 72k x 18k workload (codes + scales)
+    Kl, Nl = 18432, 73728
+    assert Kl * Nl // 2 + Kl // 128 * Nl * 2 == 700_710_912
+
+
+def test_pack_rejects_bad_arguments():
+    lib = w4.library()
+    q = np.zeros((256, 32), dtype=np.uint8)
+    s = np.ones((2, 32), dtype=np.float16)
+    out = np.zeros(256 * 32 // 8, dtype=np.uint32)
+    so = np.zeros(64, dtype=np.float16)
+    P = lambda a: a.ctypes.data
+    assert lib.w4a16_pack(None, P(s), 256, 32, 128, P(out), P(so)) == w4.EINVAL
+    assert lib.w4a16_pack(P(q), P(s), -1, 32, 128, P(out), P(so)) == w4.EINVAL
+    assert lib.w4a16_pack(P(q), P(s), 256, 32, 64, P(out), P(so)) == w4.ESHAPE
+    assert lib.w4a16_pack(P(q), P(s), 200, 32, 128, P(out), P(so)) == w4.ESHAPE
+    assert lib.w4a16_pack(P(q), P(s), 256, 24, 128, P(out), P(so)) == w4.ESHAPE
+    assert lib.w4a16_pack(P(q), P(s), 0, 32, 128, P(out), P(so)) == w4.ESHAPE
+    q[5, 7] = 16
+    assert lib.w4a16_pack(P(q), P(s), 256, 32, 128, P(out), P(so)) == w4.EINVAL
+    with pytest.raises(w4.W4A16Error):
+        w4.pack(q, s)
+
+
+def test_gemm_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(16)   # never dereferenced: every case fails validation first
+    assert lib.w4a16_gemm(None, d, d, d, 16, 1024, 1024, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm(d, d, d, d, 16, 1024, 1024, None, None) == w4.EINVAL
+    assert lib.w4a16_gemm(d, d, d, d, -1, 1024, 1024, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm(d, d, d, d, 16, 1000, 1024, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm(d, d, d, d, 16, 0, 1024, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm(d, d, d, d, 16, 1024, 1000, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm(d, d, d, d, 16, 1024, 32, d, None) == w4.ESHAPE
+    # size limits of the 32-bit buffer ranges
+    assert lib.w4a16_gemm(d, d, d, d, 2 ** 20, 4096, 1024, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm(d, d, d, d, 16, 2 ** 20, 2 ** 14, d, None) == w4.ESHAPE
+    n = ctypes.c_size_t(7)
+    assert lib.w4a16_workspace_size(16, 1000, 1024, ctypes.byref(n)) == w4.ESHAPE
+    assert lib.w4a16_workspace_size(16, 1024, 1024, None) == w4.EINVAL
+    assert n.value == 7

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Bar: relative Frobenius error <= 1e-3 and max |C - C_ref| <= 1e-2 * max |C_ref|, C_ref the
+fp32-accumulating oracle rounded to fp16.  Cases with an exactly representable answer
+(one-hot activations, integer sums, the zero point, power-of-two scaling) must match bit for
+bit.  Full-size workloads run in the same launch configuration the benchmark times and are
+checked on sampled columns, which the oracle computes one by one.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import mixed_precision_w4a16_amd as w4
+import oracle
+from workloads import ALL, COMPUTE_SWEEP, LARGE, LLAMA2_70B, LLAMA2_7B, SMALL, draw
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO = 1e-3
+MAX_ABS = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def bits(a):
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+def same(a, b):
+    x, y = bits(a).copy(), bits(b).copy()
+    x[x == 0x8000] = 0
+    y[y == 0x8000] = 0
+    return np.array_equal(x, y)
+
+
+class Weights:
+    """Packed weights resident on the GPU."""
+
+    def __init__(self, q, s):
+        self.K, self.N = q.shape
+        packed, sp = w4.pack(q, s)
+        self.packed, self.scales = w4.to_device(packed, sp)
+
+    def run(self, A, out=None, ws=None):
+        Ad = torch.from_numpy(np.ascontiguousarray(A)).cuda()
+        C = w4.gemm(Ad, self.packed, self.scales, self.N, out=out, ws=ws)
+        torch.cuda.synchronize()
+        return C.cpu().numpy()
+
+
+def gpu_gemm(A, q, s):
+    return Weights(q, s).run(A)
+
+
+def check(C, ref, what=""):
+    d = C.astype(np.float64) - ref.astype(np.float64)
+    nref = np.linalg.norm(ref.astype(np.float64))
+    rel = np.linalg.norm(d) / nref if nref > 0 else np.linalg.norm(d)
+    mref = np.abs(ref.astype(np.float64)).max()
+    mx = np.abs(d).max() / mref if mref > 0 else np.abs(d).max()
+    print(f"  {what} rel_fro={rel:.2e} max_abs/max|C|={mx:.2e}", flush=True)
+    assert np.isfinite(C).all(), what
+    assert rel <= REL_FRO, (what, rel)
+    assert mx <= MAX_ABS, (what, mx)
+    return rel, mx
+
+
+def test_one_hip_runtime_in_process_and_device_supported():
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(hip) == 1, hip
+    assert w4.workspace_bytes(16, 1024, 1024) >= 4096
+
+
+# ------------------------------------------------------------------ small and ragged shapes
+
+def test_small_workload_1024x1024_m16():
+    sh = SMALL.shapes[0]
+    A, q, s = draw(sh.K, sh.N, 16, seed=0)
+    check(gpu_gemm(A, q, s), oracle.gemm(A, q, s), "1024x1024 M=16")
+
+
+@pytest.mark.parametrize("M", list(range(1, 18)) + [31, 32, 33, 47, 48, 49, 63, 64, 65, 100,
+                                                     128, 129, 200])
+def test_m_sweep_ragged_rows(M):
+    A, q, s = draw(1024, 512, M, seed=M)
+    check(gpu_gemm(A, q, s), oracle.gemm(A, q, s), f"K=1024 N=512 M={M}")
+
+
+@pytest.mark.parametrize("K,N", [(128, 64), (128, 256), (256, 192), (384, 320), (1152, 64),
+                                 (18432, 64), (4096, 4096), (2048, 1344)])
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_shapes_tiles_and_reduction(K, N, M):
+    # N = 64 / 192 / 320: one 16-column slab per wave; K = 128: one tile per slice;
+    # K = 18432, N = 64: one slice split over up to 144 workgroups.
+    A, q, s = draw(K, N, M, seed=K + N + M)
+    check(gpu_gemm(A, q, s), oracle.gemm(A, q, s), f"K={K} N={N} M={M}")
+
+
+def test_m1_equals_gemv():
+    A, q, s = draw(4096, 1024, 1, seed=21)
+    check(gpu_gemm(A, q, s)[0], oracle.gemv(A[0], q, s), "M=1 vs gemv")
+
+
+# ------------------------------------------------------------------ exact cases
+
+def test_one_hot_rows_are_bit_exact():
+    # Row m of A is 1 at k_m: C[m, :] = fp16(s[k_m // 128, :] * (q[k_m, :] - 8)) exactly.
+    # Positions cover every nibble slot of a packed word, every MFMA k-step and group edges.
+    K, N = 384, 256
+    hot = [0, 1, 2, 3, 4, 5, 6, 7, 8, 15, 31, 32, 63, 64, 96, 127, 128, 129, 200, 255, 256, 383]
+    A, q, s = draw(K, N, len(hot), seed=22)
+    A[:] = 0
+    for m, k in enumerate(hot):
+        A[m, k] = -2.0 if m % 3 == 0 else 1.0
+    C = gpu_gemm(A, q, s)
+    for m, k in enumerate(hot):
+        w = s[k // 128].astype(np.float64) * (q[k].astype(np.float64) - 8.0) * float(A[m, k])
+        assert same(C[m], w.astype(np.float16)), (m, k)
+
+
+def test_integer_sums_are_bit_exact():
+    # A in {-1, 0, 1} and power-of-two scales: every partial sum is exact in fp32, so the
+    # result equals the oracle's bit for bit under any summation order or split.
+    rng = np.random.default_rng(23)
+    K, N, M = 4096, 1024, 33
+    A = rng.integers(-1, 2, (M, K)).astype(np.float16)
+    q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    s = rng.choice(np.array([0.25, 0.5, 1.0, 2.0], dtype=np.float16), (K // 128, N))
+    assert same(gpu_gemm(A, q, s), oracle.gemm(A, q, s))
+
+
+def test_zero_point_gives_zero():
+    A, q, s = draw(2048, 512, 16, seed=24)
+    q[:] = 8
+    assert (bits(gpu_gemm(A, q, s)) & 0x7FFF == 0).all()
+
+
+def test_power_of_two_scaling_is_exact():
+    A, q, s = draw(4096, 1024, 16, seed=25)
+    W = Weights(q, s)
+    C = W.run(A).astype(np.float32)
+    C2 = W.run((A.astype(np.float32) * 2).astype(np.float16)).astype(np.float32)
+    big = np.abs(C) >= 2.0 ** -13
+    assert np.array_equal(C2[big], 2 * C[big])
+
+
+def test_repeated_runs_are_bitwise_identical():
+    # many slices split between workgroups: the cross-workgroup sum order is fixed
+    A, q, s = draw(18432, 512, 16, seed=26)
+    W = Weights(q, s)
+    first = W.run(A)
+    for _ in range(3):
+        assert np.array_equal(bits(W.run(A)), bits(first))
+    check(first, oracle.gemm(A, q, s), "K=18432 N=512 M=16")
+
+
+def test_nested_m_agrees():
+    A, q, s = draw(2048, 1024, 128, seed=27)
+    W = Weights(q, s)
+    c128 = W.run(A)
+    c16 = W.run(A[:16])
+    check(c16, c128[:16].astype(np.float16), "M=16 vs M=128 rows")
+
+
+# ------------------------------------------------------------------ boundary behaviour
+
+def test_m_zero_is_a_no_op():
+    _, q, s = draw(256, 64, 1, seed=28)
+    W = Weights(q, s)
+    out = torch.full((0, 64), 7.0, dtype=torch.float16, device="cuda")
+    Ad = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    r = w4.gemm(Ad, W.packed, W.scales, 64, out=out)
+    assert r.shape == (0, 64)
+    lib = w4.library()
+    ws = w4.new_workspace(1, 256, 64)
+    st = lib.w4a16_gemm(Ad.data_ptr() or 16, W.packed.data_ptr(), W.scales.data_ptr(),
+                        out.data_ptr() or 16, 0, 256, 64, ws.data_ptr(), None)
+    assert st == w4.OK
+
+
+def test_bad_shapes_rejected_on_device():
+    _, q, s = draw(256, 64, 1, seed=29)
+    W = Weights(q, s)
+    A = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
+    lib = w4.library()
+    ws = w4.new_workspace(4, 256, 64)
+    out = torch.empty((4, 64), dtype=torch.float16, device="cuda")
+    args = (A.data_ptr(), W.packed.data_ptr(), W.scales.data_ptr(), out.data_ptr())
+    assert lib.w4a16_gemm(*args, 4, 200, 64, ws.data_ptr(), None) == w4.ESHAPE
+    assert lib.w4a16_gemm(*args, 4, 256, 100, ws.data_ptr(), None) == w4.ESHAPE
+    assert lib.w4a16_gemm(*args, 4, 256, 64, None, None) == w4.EINVAL
+
+
+def test_workspace_shared_across_shapes_stays_clean():
+    shapes = [(18432, 256, 16), (1024, 512, 3), (4096, 1024, 64), (18432, 64, 1), (1024, 512, 3)]
+    need = max(w4.workspace_bytes(M, K, N) for K, N, M in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (K, N, M) in enumerate(shapes):
+        A, q, s = draw(K, N, M, seed=30 + i)
+        check(Weights(q, s).run(A, ws=ws), oracle.gemm(A, q, s), f"shared ws K={K} N={N} M={M}")
+        assert int(ws[:4096].count_nonzero()) == 0      # counters back to zero
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sampled_check(shape, seed=0, ncols=48):
+    A, q, s = draw(shape.K, shape.N, max(shape.Ms), seed=seed, sigma=shape.sigma)
+    W = Weights(q, s)
+    rng = np.random.default_rng(1000 + shape.K)
+    cols = np.unique(np.concatenate([[0, 1, 15, 16, shape.N - 1],
+                                     rng.choice(shape.N, ncols, replace=False)]))
+    qc, sc = np.ascontiguousarray(q[:, cols]), np.ascontiguousarray(s[:, cols])
+    del q, s
+    gc.collect()
+    ref_all = oracle.gemm(A, qc, sc)              # oracle on the sampled columns only
+    for M in shape.Ms:
+        C = W.run(A[:M])
+        assert np.isfinite(C).all()
+        check(C[:, cols], ref_all[:M], f"{shape.name} M={M} ({len(cols)} sampled columns)")
+    del W
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("shape", [sh for wl in (SMALL, LARGE, LLAMA2_7B, LLAMA2_70B,
+                                                 COMPUTE_SWEEP) for sh in wl.shapes],
+                         ids=lambda sh: sh.name)
+def test_full_size_workloads_sampled(shape):
+    _sampled_check(shape)
