@@ -9,14 +9,12 @@
 //   the registers that feed the matrix cores; no fp16 copy of the weights exists anywhere.
 //   Pages: MARLIN paper sec. 3.4 "Maximizing Loading Bandwidth" (widest loads, full lines,
 //   weights read once with an evict-first hint).
-// * Activations.  Each lane loads its own A fragments (16 bytes = 8 consecutive k of one
-//   row) straight from global memory into MFMA operand registers.  The four waves of a
-//   workgroup walk the same K tiles of adjacent column ranges in step, so they read the same
-//   A bytes and the vector L1 serves the repeats; A is re-read from L2 once per column slice
-//   (the pages' reason for wide N tiles: MARLIN paper sec. 3.4 "Bound By Weight Loading",
-//   Eq. (1)).  Loads are issued one tile ahead, in the order they are consumed, because the
-//   vector-memory counter completes in order (the pages' multi-stage prefetch, sec. 3.4
-//   "Memory Load Pipelining").  There is no LDS staging and no barrier in the main loop.
+// * Activations.  The A tile of each 128-row K step is loaded once per workgroup (one
+//   16-byte chunk per thread per 16 rows) and staged in a two-stage LDS ring, XOR-swizzled
+//   so stores and the 16-lane fragment reads are bank-conflict-free; all four waves read
+//   their MFMA fragments from it.  A is re-read from L2 once per column slice, so wide
+//   slices keep its traffic below the weight stream's (MARLIN paper sec. 3.4 "Bound By
+//   Weight Loading", Eq. (1); "Shared Memory Layouts"; "Memory Load Pipelining").
 // * Dequantisation.  One 32-bit word holds 8 codes; mask-and-OR into the fp16 exponent
 //   0x6400 gives 1024 + q (low nibbles) or 1024 + 16q (high nibbles), and one packed fp16
 //   add or FMA per pair returns q - 8 exactly.  Deep-dive page "Marlin 完全拆解", section
@@ -38,10 +36,11 @@
 //   page, striped partitioning.  Workgroup ids are remapped so consecutive stripes sit on
 //   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs).
 // * Cross-workgroup reduction.  A slice split between stripes is summed without any
-//   waiting: each contributor writes its fp32 partial tile to its own workspace slot,
-//   fences, and bumps the slice's counter; the contributor that finds itself last adds all
-//   partials in stripe order (a fixed order, so results are bitwise repeatable), writes C,
-//   and resets the counter.  The pages sum such partials serially with locks and stage them
+//   waiting: each contributor writes its fp32 partial tile to its own workspace slot with
+//   device-scope (write-through) stores, waits for them, and bumps the slice's counter; the
+//   contributor that finds itself last reads the partials back past the L2 and adds them in
+//   stripe order (a fixed order, so results are bitwise repeatable), writes C, and resets the
+//   counter.  No cache-wide writeback or invalidate is issued.  The pages sum such partials serially with locks and stage them
 //   in fp16 in the output (deep-dive page section "为什么归约串行，却不一定慢"); fp32
 //   partials and a last-arriver sum keep the same "no big temporary" property, keep full
 //   precision, and never spin, so no co-residency assumption is needed.
@@ -137,6 +136,7 @@ template <int MB, int NBW>
 struct Tile {
     static constexpr int Mt = 16 * MB;                 // rows per M sub-problem
     static constexpr int Nt = 16 * NBW * kWaves;       // columns per slice
+    static constexpr int kStageQuads = MB * 256;       // 16-byte LDS chunks per A stage
     static constexpr int kSlotFloats = Mt * Nt;
 };
 
@@ -147,7 +147,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-constexpr int kNonTemporal = 2;    // buffer-load cache policy: streaming, evict first
+constexpr int kNonTemporal = 2;    // cache policy: streaming, evict first (weights, read once)
+constexpr int kDeviceScope = 16;   // cache policy sc1: write through / read past the XCD's L2
 
 // Where the next tile's loads come from.  Tiles run in (slice, M sub-problem, K) order;
 // inside a slice only the K step changes and every offset moves by a constant.
@@ -164,30 +165,40 @@ __device__ __forceinline__ void load_cursor_set(const Params &p, int wave, LoadC
     c.a_soff = static_cast<uint32_t>(c.g) * (kGroup * 2);
 }
 
-// This lane's byte offsets into A for each 16-row sub-tile: row arow + 16mb + lane%16,
-// column 8(lane/16) (the first k of its fragment in MFMA k-step 0).
+// The A tile of one K step (Mt rows x 128 k) is loaded by the whole workgroup, one 16-byte
+// chunk per thread per 16-row sub-tile: thread `tid` takes row tid/16 and chunk tid%16
+// (k = 8 * chunk .. +7).  Its byte offset in A for sub-problem row `arow`:
 template <int MB>
-__device__ __forceinline__ void a_lane_offsets(const Params &p, int lane, int arow,
-                                               uint32_t (&voff)[MB])
+__device__ __forceinline__ void a_thread_offsets(const Params &p, int tid, int arow,
+                                                 uint32_t (&voff)[MB])
 {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        voff[mb] = (static_cast<uint32_t>(arow + 16 * mb + (lane & 15)) * p.K + 8 * (lane >> 4)) * 2;
+        voff[mb] = (static_cast<uint32_t>(arow + 16 * mb + (tid >> 4)) * p.K + 8 * (tid & 15)) * 2;
 }
 
-// A fragments of one tile: 16 bytes = k 32t + 8(lane/16) .. +7 of row lane%16, per k-step
-// t and sub-tile mb.  Rows at or past M fall outside the buffer and read as zero.
+// Global -> registers.  Rows at or past M fall outside the buffer and read as zero.
 template <int MB>
 __device__ __forceinline__ void load_a(__amdgpu_buffer_rsrc_t rA, const uint32_t (&voff)[MB],
-                                       uint32_t soff_in, u4 (&af)[MB][4])
+                                       uint32_t soff_in, u4 (&ar)[MB])
 {
     const uint32_t soff = __builtin_amdgcn_readfirstlane(soff_in);   // uniform: keep in SGPR
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
+        ar[mb] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[mb], soff, 0));
+}
+
+// Registers -> LDS stage, XOR-swizzled: chunk c of row i goes to position c ^ (i mod 16), so
+// the 16 lanes that read one k-chunk of 16 different rows hit 16 different bank groups
+// (MARLIN paper sec. 3.4 "Shared Memory Layouts": (i, j) -> (i, i XOR j)).  The stores are
+// conflict-free too: the 16 threads of a row write a permutation of its 16 chunks.
+template <int MB>
+__device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
+{
+    const int r = tid >> 4, c = tid & 15;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            af[mb][t] = __builtin_bit_cast(
-                u4, __builtin_amdgcn_raw_buffer_load_b128(rA, voff[mb] + 64 * t, soff, 0));
+    for (int mb = 0; mb < MB; ++mb)
+        stage[(16 * mb + r) * 16 + (c ^ r)] = ar[mb];
 }
 
 // This wave's packed weight quads (1 KiB contiguous per slab, non-temporal) and scales.
@@ -208,19 +219,28 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
 }
 
 template <int MB, int NBW>
-__device__ __forceinline__ void compute_tile(const u4 (&af)[MB][4], const u4 (&wq)[NBW],
+__device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4 (&wq)[NBW],
                                              const uint32_t (&sc)[NBW], f4 (&acc)[MB][NBW],
                                              uint32_t mlo, uint32_t mhi, uint32_t magic)
 {
     // Scales first: converting them here ends the loaded registers' live range before the
     // next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
-    const int sshift = (threadIdx.x & 1) * 16;        // odd columns: high half of the dword
+    const int sshift = (lane & 1) * 16;               // odd columns: high half of the dword
     float sf[NBW];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         sf[b] = half_bits_to_float(static_cast<uint16_t>(sc[b] >> sshift));
         asm volatile("" : "+v"(sf[b]));
     }
+    // A fragments from LDS: row lane%16 of each sub-tile, k = 32t + 8(lane/16) .. +7.
+    const int row = lane & 15, quad = lane >> 4;
+    h8 a[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
+
     f4 part[MB][NBW];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -230,8 +250,7 @@ __device__ __forceinline__ void compute_tile(const u4 (&af)[MB][4], const u4 (&w
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const f4 cin = (t == 0) ? f4{0.f, 0.f, 0.f, 0.f} : part[mb][b];
-                part[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    __builtin_bit_cast(h8, af[mb][t]), bw, cin, 0, 0, 0);
+                part[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bw, cin, 0, 0, 0);
             }
         }
     }
@@ -268,17 +287,27 @@ __device__ __forceinline__ void write_c(const Params &p, int wave, int lane, lon
             }
 }
 
+// Byte offset of this lane's 16-byte piece of sub-tile (mb, b) in partial slot `slot` of
+// stripe `stripe`.
 template <int MB, int NBW>
-__device__ __forceinline__ f4 *slot_ptr(const Params &p, int stripe, int slot, int wave, int mb,
-                                        int b, int lane)
+__device__ __forceinline__ uint32_t slot_offset(int stripe, int slot, int wave, int mb, int b,
+                                                int lane)
 {
-    float *base = p.partials + (static_cast<size_t>(stripe) * 2 + slot) * Tile<MB, NBW>::kSlotFloats;
-    return reinterpret_cast<f4 *>(base) + ((wave * MB + mb) * NBW + b) * 64 + lane;
+    return ((static_cast<uint32_t>(stripe) * 2 + slot) * Tile<MB, NBW>::kSlotFloats +
+            ((wave * MB + mb) * NBW + b) * 256 + lane * 4) * 4;
 }
 
 // End of this stripe's share of slice sigma (its tiles [max(t0, first of slice), last]).
+//
+// A split slice is summed without waiting on anyone.  Partials travel through the
+// workspace with device-scope cache policy: stores write through to memory and loads read
+// past the (per-XCD, not mutually coherent) L2s, so no cache-wide writeback or invalidate is
+// needed.  Each wave waits for its own partial stores to complete before the workgroup
+// barrier; only then does thread 0 bump the slice counter (a device-scope atomic).  The
+// contributor that draws the last count has, by then, every other partial in memory.
 template <int MB, int NBW>
-__device__ __forceinline__ void finish_slice(const Params &p, int stripe, long long t0, long long last,
+__device__ __forceinline__ void finish_slice(const Params &p, __amdgpu_buffer_rsrc_t rP,
+                                             int stripe, long long t0, long long last,
                                              long long sigma, int tid, f4 (&acc)[MB][NBW],
                                              int *flag)
 {
@@ -296,17 +325,19 @@ __device__ __forceinline__ void finish_slice(const Params &p, int stripe, long l
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
-            *slot_ptr<MB, NBW>(p, stripe, my_slot, wave, mb, b, lane) = acc[mb][b];
-    __threadfence();          // release this thread's partial at device scope
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u4, acc[mb][b]), rP,
+                slot_offset<MB, NBW>(stripe, my_slot, wave, mb, b, lane), 0, kDeviceScope);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's partial is in memory
     __syncthreads();
     if (tid == 0)
-        *flag = atomicAdd(p.counters + w_lo, 1);
+        *flag = __hip_atomic_fetch_add(p.counters + w_lo, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int arrived = *flag;
     __syncthreads();          // everyone has read the flag before it can be reused
     if (arrived != w_hi - w_lo)
         return;               // another contributor is still running; it will finish
-    __threadfence();          // acquire the other contributors' partials
 
     f4 sum[MB][NBW];
 #pragma unroll
@@ -320,19 +351,23 @@ __device__ __forceinline__ void finish_slice(const Params &p, int stripe, long l
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
-                const f4 v = (w == stripe) ? acc[mb][b]
-                                           : *slot_ptr<MB, NBW>(p, w, slot, wave, mb, b, lane);
+                const f4 v = (w == stripe)
+                    ? acc[mb][b]
+                    : __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                          rP, slot_offset<MB, NBW>(w, slot, wave, mb, b, lane), 0, kDeviceScope));
                 sum[mb][b] += v;
             }
     }
     write_c<MB, NBW>(p, wave, lane, sigma, sum);
     if (tid == 0)
-        atomicExch(p.counters + w_lo, 0);                     // ready for the next call
+        __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int MB, int NBW>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
 {
+    using TL = Tile<MB, NBW>;
+    __shared__ u4 lds[2 * TL::kStageQuads];
     __shared__ int flag;
 
     const int tid = threadIdx.x;
@@ -356,6 +391,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
     const __amdgpu_buffer_rsrc_t rS =
         make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(p.partials, static_cast<uint32_t>(2u * p.W * TL::kSlotFloats * 4u));
 
     // dequant constants in VGPRs for v_and_or_b32
     const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
@@ -372,15 +409,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     long long sigma = t0 / p.G;
     int g = static_cast<int>(t0 - sigma * p.G);
 
-    // Load position, kept one tile ahead of the next compute and clamped to the stripe's
-    // last tile, so every load is unconditional (a re-read of the last tile is a cache hit).
+    // Load position, clamped to the stripe's last tile so every load is unconditional (a
+    // re-read of the last tile is a cache hit).  A loads run two tiles ahead of the compute;
+    // each A load is issued before the weight load of the same tile (see the schedule below).
     LoadCursor lc;
     lc.g = g;
     lc.s = static_cast<int>(sigma / p.P);
     lc.pm = static_cast<int>(sigma - static_cast<long long>(lc.s) * p.P);
     load_cursor_set<MB, NBW>(p, wave, lc);
     uint32_t a_voff[MB];
-    a_lane_offsets<MB>(p, lane, lc.pm * 16 * MB, a_voff);
+    a_thread_offsets<MB>(p, tid, lc.pm * 16 * MB, a_voff);
     long long lt = t0;                 // tile lc points at
 
     auto step_load = [&]() {
@@ -396,29 +434,34 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
                     ++lc.s;
                 }
                 load_cursor_set<MB, NBW>(p, wave, lc);
-                a_lane_offsets<MB>(p, lane, lc.pm * 16 * MB, a_voff);
+                a_thread_offsets<MB>(p, tid, lc.pm * 16 * MB, a_voff);
             }
         }
     };
 
-    // Two register buffers: tile i is computed from buffer i % 2 while tile i + 1's loads
-    // are in flight.  Every load of a tile is issued before any load of the next tile, and
-    // the vector-memory counter completes in order, so waiting for one tile never waits for
-    // a later one.
-    u4 af0[MB][4], af1[MB][4];
+    // Registers: weights double-buffered (tile i in buffer i % 2); A staged through `ar`
+    // into a two-stage LDS ring (tile i in stage i % 2).  Per tile i the order is
+    //   store A(i+1) -> LDS, load A(i+2) -> ar, barrier, compute(i), load W(i+2).
+    // The vector-memory counter completes in order, and every A load is issued before the
+    // weight load of the same tile, so waiting for A(i+1) never waits for a weight tile that
+    // is not needed yet: each weight tile has one whole tile of compute to arrive in.
+    u4 ar[MB];
     u4 wq0[NBW], wq1[NBW];
     uint32_t sc0[NBW], sc1[NBW];
+    u4 *const st0 = lds;
+    u4 *const st1 = lds + TL::kStageQuads;
 
-    load_a<MB>(rA, a_voff, lc.a_soff, af0);
-    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);
+    load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0)
+    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);        // W(t0)
+    store_a<MB>(st0, tid, ar);
     step_load();
-    load_a<MB>(rA, a_voff, lc.a_soff, af1);
-    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);
-    step_load();
+    load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0+1)
+    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
+    step_load();                                              // lc -> t0+2
 
     auto end_of_tile = [&]() {
         if (g == p.G - 1 || t + 1 == t1) {
-            finish_slice<MB, NBW>(p, stripe, t0, t, sigma, tid, acc, &flag);
+            finish_slice<MB, NBW>(p, rP, stripe, t0, t, sigma, tid, acc, &flag);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -432,31 +475,34 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         }
     };
 
-    // Loop over whole pairs of tiles (even tile from buffer 0, odd from buffer 1); a single
-    // trailing tile is finished after the loop.  Exiting only at the end of a pair keeps the
-    // control flow simple enough for the compiler to wait for exactly one tile's loads.
-    // The asm/scheduling barriers keep each tile's loads after the last use of the registers
-    // they overwrite; otherwise the two live ranges overlap and the register allocator adds
-    // loop-carried copies that must wait for the loads.
+    // Whole pairs of tiles per iteration; a single trailing tile is finished after the
+    // loop.  Exiting only at the end of a pair keeps the control flow simple enough for the
+    // compiler to wait for exactly one tile's loads.  The asm/scheduling barriers keep each
+    // tile's loads after the last use of the registers they overwrite.
     while (t + 1 < t1) {
-        compute_tile<MB, NBW>(af0, wq0, sc0, acc, mlo, mhi, magic);
+        store_a<MB>(st1, tid, ar);                            // A(t+1)
+        load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
+        __syncthreads();
+        compute_tile<MB, NBW>(st0, lane, wq0, sc0, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_a<MB>(rA, a_voff, lc.a_soff, af0);
-        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);
+        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);    // W(t+2)
         step_load();
         end_of_tile();
 
-        compute_tile<MB, NBW>(af1, wq1, sc1, acc, mlo, mhi, magic);
+        store_a<MB>(st0, tid, ar);                            // A(t+1)
+        load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
+        __syncthreads();
+        compute_tile<MB, NBW>(st1, lane, wq1, sc1, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_a<MB>(rA, a_voff, lc.a_soff, af1);
-        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);
+        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);    // W(t+2)
         step_load();
         end_of_tile();
     }
     if (t < t1) {
-        compute_tile<MB, NBW>(af0, wq0, sc0, acc, mlo, mhi, magic);
+        __syncthreads();
+        compute_tile<MB, NBW>(st0, lane, wq0, sc0, acc, mlo, mhi, magic);
         end_of_tile();
     }
 }
