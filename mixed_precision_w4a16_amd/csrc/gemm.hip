@@ -35,12 +35,14 @@
 //   "为什么规则二维网格会浪费最后一波 SM" and "大 M 时虚拟复制权重网格"; MARLIN README
 //   page, striped partitioning.  Workgroup ids are remapped so consecutive stripes sit on
 //   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs).
-// * Cross-workgroup reduction.  A slice split between stripes is summed without any
-//   waiting: each contributor writes its fp32 partial tile to its own workspace slot with
-//   device-scope (write-through) stores, waits for them, and bumps the slice's counter; the
-//   contributor that finds itself last reads the partials back past the L2 and adds them in
-//   stripe order (a fixed order, so results are bitwise repeatable), writes C, and resets the
-//   counter.  No cache-wide writeback or invalidate is issued.  The pages sum such partials serially with locks and stage them
+// * Cross-workgroup reduction.  Only the first and last slice of a stripe can be shared
+//   with a neighbouring stripe.  At such a slice's end the workgroup writes its fp32 partial
+//   tile to its own workspace slot with device-scope (write-through) stores and streams on
+//   without waiting.  After its last tile it waits once for its stores, bumps each shared
+//   slice's counter, and the contributor that draws the last count reads the partials back
+//   past the L2, adds them in stripe order (a fixed order, so results are bitwise
+//   repeatable), writes C and resets the counter.  No cache-wide writeback or invalidate is
+//   issued and no workgroup ever waits for another.  The pages sum such partials serially with locks and stage them
 //   in fp16 in the output (deep-dive page section "为什么归约串行，却不一定慢"); fp32
 //   partials and a last-arriver sum keep the same "no big temporary" property, keep full
 //   precision, and never spin, so no co-residency assumption is needed.
@@ -48,6 +50,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <algorithm>
 #include <mutex>
 
 #include "w4a16.h"
@@ -297,70 +300,86 @@ __device__ __forceinline__ uint32_t slot_offset(int stripe, int slot, int wave, 
             ((wave * MB + mb) * NBW + b) * 256 + lane * 4) * 4;
 }
 
-// End of this stripe's share of slice sigma (its tiles [max(t0, first of slice), last]).
-//
-// A split slice is summed without waiting on anyone.  Partials travel through the
-// workspace with device-scope cache policy: stores write through to memory and loads read
-// past the (per-XCD, not mutually coherent) L2s, so no cache-wide writeback or invalidate is
-// needed.  Each wave waits for its own partial stores to complete before the workgroup
-// barrier; only then does thread 0 bump the slice counter (a device-scope atomic).  The
-// contributor that draws the last count has, by then, every other partial in memory.
+// Partial tile of a split slice -> this stripe's workspace slot, with device-scope
+// (write-through) stores.  Nothing waits here: the stores complete while streaming goes on.
 template <int MB, int NBW>
-__device__ __forceinline__ void finish_slice(const Params &p, __amdgpu_buffer_rsrc_t rP,
-                                             int stripe, long long t0, long long last,
-                                             long long sigma, int tid, f4 (&acc)[MB][NBW],
-                                             int *flag)
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t rP, int stripe, int slot,
+                                              int wave, int lane, const f4 (&acc)[MB][NBW])
 {
-    const int wave = tid >> 6, lane = tid & 63;
-    const long long s0 = sigma * p.G;
-    const long long first = t0 > s0 ? t0 : s0;
-    if (first == s0 && last == s0 + p.G - 1) {
-        write_c<MB, NBW>(p, wave, lane, sigma, acc);          // sole owner of the slice
-        return;
-    }
-    const int w_lo = stripe_owner(s0, p.T, p.W);
-    const int w_hi = stripe_owner(s0 + p.G - 1, p.T, p.W);
-    const int my_slot = (sigma == t0 / p.G) ? 0 : 1;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
             __builtin_amdgcn_raw_buffer_store_b128(
                 __builtin_bit_cast(u4, acc[mb][b]), rP,
-                slot_offset<MB, NBW>(stripe, my_slot, wave, mb, b, lane), 0, kDeviceScope);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's partial is in memory
-    __syncthreads();
-    if (tid == 0)
-        *flag = __hip_atomic_fetch_add(p.counters + w_lo, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int arrived = *flag;
-    __syncthreads();          // everyone has read the flag before it can be reused
-    if (arrived != w_hi - w_lo)
-        return;               // another contributor is still running; it will finish
+                slot_offset<MB, NBW>(stripe, slot, wave, mb, b, lane), 0, kDeviceScope);
+}
 
+// Sum the partials of split slice sigma in stripe order (a fixed order: results repeat bit
+// for bit) and write C.  Partials are read past the L2 with device-scope loads.
+template <int MB, int NBW>
+__device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rsrc_t rP,
+                                             long long sigma, int w_lo, int w_hi, int wave,
+                                             int lane)
+{
     f4 sum[MB][NBW];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
             sum[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int w = w_lo; w <= w_hi; ++w) {                      // fixed order: along K
+    for (int w = w_lo; w <= w_hi; ++w) {
         const int slot = (sigma == stripe_begin(w, p.T, p.W) / p.G) ? 0 : 1;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int b = 0; b < NBW; ++b) {
-                const f4 v = (w == stripe)
-                    ? acc[mb][b]
-                    : __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
-                          rP, slot_offset<MB, NBW>(w, slot, wave, mb, b, lane), 0, kDeviceScope));
-                sum[mb][b] += v;
-            }
+            for (int b = 0; b < NBW; ++b)
+                sum[mb][b] += __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rP, slot_offset<MB, NBW>(w, slot, wave, mb, b, lane), 0, kDeviceScope));
     }
     write_c<MB, NBW>(p, wave, lane, sigma, sum);
-    if (tid == 0)
-        __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After the stripe's last tile: settle the (at most two) split slices it touched -- the
+// first, which it may have entered part-way (slot 0), and the last, which it may have left
+// part-way (slot 1).  part0 / part1 are those slices as recorded when their partials were
+// stored, or -1.  Every wave first waits for all its stores (the partials are then in
+// memory), the workgroup synchronises, and thread 0 counts this stripe in for each split
+// slice with a device-scope atomic.  The stripe that draws the last count of a slice sums
+// all its partials and writes C.  Nobody ever waits for another workgroup, so no
+// co-residency is assumed.
+template <int MB, int NBW>
+__device__ __forceinline__ void settle_split_slices(const Params &p, __amdgpu_buffer_rsrc_t rP,
+                                                    long long part0, long long part1, int tid,
+                                                    int *flag)
+{
+    if (part0 < 0 && part1 < 0)
+        return;
+    const int wave = tid >> 6, lane = tid & 63;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's partials are in memory
+    __syncthreads();
+    if (tid == 0) {
+        if (part0 >= 0)
+            flag[0] = __hip_atomic_fetch_add(p.counters + stripe_owner(part0 * p.G, p.T, p.W), 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (part1 >= 0)
+            flag[1] = __hip_atomic_fetch_add(p.counters + stripe_owner(part1 * p.G, p.T, p.W), 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const long long sigma = i == 0 ? part0 : part1;
+        if (sigma < 0)
+            continue;
+        const int w_lo = stripe_owner(sigma * p.G, p.T, p.W);
+        const int w_hi = stripe_owner(sigma * p.G + p.G - 1, p.T, p.W);
+        if (flag[i] != w_hi - w_lo)
+            continue;               // another contributor is still running; it will finish
+        reduce_slice<MB, NBW>(p, rP, sigma, w_lo, w_hi, wave, lane);
+        if (tid == 0)
+            __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int MB, int NBW>
@@ -368,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
 {
     using TL = Tile<MB, NBW>;
     __shared__ u4 lds[2 * TL::kStageQuads];
-    __shared__ int flag;
+    __shared__ int flag[2];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -406,8 +425,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
 
     // Compute position: tile t, its K step g and slice sigma.
     long long t = t0;
-    long long sigma = t0 / p.G;
+    const long long sigma0 = t0 / p.G;           // the stripe's first slice
+    long long sigma = sigma0;
     int g = static_cast<int>(t0 - sigma * p.G);
+    long long part0 = -1, part1 = -1;            // split slices whose partials were stored
 
     // Load position, clamped to the stripe's last tile so every load is unconditional (a
     // re-read of the last tile is a cache hit).  A loads run two tiles ahead of the compute;
@@ -459,9 +480,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
     step_load();                                              // lc -> t0+2
 
+    // End of a tile: at a slice's end, write C if this stripe owns the whole slice, else
+    // leave its partial in the workspace for settle_split_slices.
     auto end_of_tile = [&]() {
         if (g == p.G - 1 || t + 1 == t1) {
-            finish_slice<MB, NBW>(p, rP, stripe, t0, t, sigma, tid, acc, &flag);
+            const long long s0 = sigma * p.G;
+            if (t0 <= s0 && t == s0 + p.G - 1) {
+                write_c<MB, NBW>(p, wave, lane, sigma, acc);
+            } else if (sigma == sigma0) {
+                store_partial<MB, NBW>(rP, stripe, 0, wave, lane, acc);
+                part0 = sigma;
+            } else {
+                store_partial<MB, NBW>(rP, stripe, 1, wave, lane, acc);
+                part1 = sigma;
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -476,7 +508,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     };
 
     // Whole pairs of tiles per iteration; a single trailing tile is finished after the
-    // loop.  Exiting only at the end of a pair keeps the control flow simple enough for the
+    // loop.  A slice's end is handled before the next weight tile is requested, so the
+    // epilogue's wait for its own stores only waits for loads the next tile needs anyway.  Exiting only at the end of a pair keeps the control flow simple enough for the
     // compiler to wait for exactly one tile's loads.  The asm/scheduling barriers keep each
     // tile's loads after the last use of the registers they overwrite.
     while (t + 1 < t1) {
@@ -486,9 +519,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         compute_tile<MB, NBW>(st0, lane, wq0, sc0, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
+        end_of_tile();
         load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);    // W(t+2)
         step_load();
-        end_of_tile();
 
         store_a<MB>(st0, tid, ar);                            // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
@@ -496,15 +529,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         compute_tile<MB, NBW>(st1, lane, wq1, sc1, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
+        end_of_tile();
         load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);    // W(t+2)
         step_load();
-        end_of_tile();
     }
     if (t < t1) {
         __syncthreads();
         compute_tile<MB, NBW>(st0, lane, wq0, sc0, acc, mlo, mhi, magic);
         end_of_tile();
     }
+    settle_split_slices<MB, NBW>(p, rP, part0, part1, tid, flag);
 }
 
 // ------------------------------------------------------------------------------- host side
@@ -559,6 +593,51 @@ int check_gemm_shape(int M, int K, int N)
     return W4A16_OK;
 }
 
+template <int MB, int NBW>
+int resident_per_cu()
+{
+    // workgroups of this variant one CU can hold at once (registers and LDS permitting)
+    static const int n = [] {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, w4a16_gemm_kernel<MB, NBW>, kThreads,
+                                                         0) != hipSuccess || b < 1)
+            b = 1;
+        return b;
+    }();
+    return n;
+}
+
+int resident_per_cu(int MB, int NBW)
+{
+    switch (MB * 10 + NBW) {
+    case 11: return resident_per_cu<1, 1>();
+    case 12: return resident_per_cu<1, 2>();
+    case 14: return resident_per_cu<1, 4>();
+    case 21: return resident_per_cu<2, 1>();
+    case 22: return resident_per_cu<2, 2>();
+    case 24: return resident_per_cu<2, 4>();
+    case 41: return resident_per_cu<4, 1>();
+    case 42: return resident_per_cu<4, 2>();
+    default: return 1;
+    }
+}
+
+// Number of stripes: a whole number of workgroups per CU, so every CU streams the same
+// amount (a fractional count leaves some CUs with one workgroup more than others).  Two per
+// CU keep the weight stream busy up to M = 32; at 64-row tiles each byte carries more work
+// and three per CU measure faster.
+int choose_stripes(long long T, int MB, int NBW, int cus)
+{
+    (void)NBW;
+    const int per_cu = MB <= 2 ? 2 : 3;
+    long long w = static_cast<long long>(cus) * per_cu;
+    if (w > kMaxWGs)
+        w = kMaxWGs;
+    if (w > T)
+        w = T;
+    return static_cast<int>(w);
+}
+
 Config choose_config(int M, int K, int N, int cus)
 {
     Config c{};
@@ -576,12 +655,7 @@ Config choose_config(int M, int K, int N, int cus)
         }
     c.S = N / (16 * kWaves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
-    long long w = static_cast<long long>(cus) * 2;
-    if (w > kMaxWGs)
-        w = kMaxWGs;
-    if (w > c.T)
-        w = c.T;
-    c.W = static_cast<int>(w);
+    c.W = choose_stripes(c.T, c.MB, c.NBW, cus);
     return c;
 }
 
