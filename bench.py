@@ -26,6 +26,23 @@ METRIC = "W4A16 GEMM effective GB/s (% HBM peak) + TFLOP/s at M=1..128, vs 3.87x
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix
 GROUP = 128
+CALIB_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
+KERNEL_SOURCE = os.path.join(ROOT, "mixed_precision_w4a16_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter runs, if they were taken on the
+    kernel source as it is now (else None)."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec
 
 
 def algorithmic_bytes(M, K, N):
@@ -69,6 +86,8 @@ def main():
                     help="columns of the CPU-baseline sample (0 skips it)")
     ap.add_argument("--copies", type=int, default=2,
                     help="weight copies rotated between calls so no call hits the MALL")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -126,6 +145,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    if args.calib_copy:
+        # a plain elementwise kernel that reads CALIB_BYTES and writes CALIB_BYTES
+        x = torch.ones(CALIB_BYTES // 2, dtype=torch.float16, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(2):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+
     sweep = []
     tot_bytes = tot_us = 0.0
     for M in Ms:
@@ -151,6 +178,13 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = tot_bytes * args.steps / wall / 1e9
     achieved = tot_bytes / tot_us / 1e3          # GB/s, from the per-launch event durations
+    traffic = measured_traffic()
+    traffic_bytes = None
+    if traffic is not None:
+        per_m = traffic["per_M"]
+        traffic_bytes = float(np.mean([per_m[str(M)]["hbm_bytes"] for M in Ms]))
+        for row in sweep:
+            row["hbm_bytes_measured"] = per_m[str(row["M"])]["hbm_bytes"]
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -162,7 +196,7 @@ def main():
                    "weight_copies_rotated": args.copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
+                     "traffic": traffic_bytes,
                      "kernel": "w4a16_gemm_kernel (all M of the sweep; mean bytes / mean time)"},
         "sweep": sweep,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

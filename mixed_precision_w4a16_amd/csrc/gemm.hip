@@ -10,7 +10,7 @@
 //   Pages: MARLIN paper sec. 3.4 "Maximizing Loading Bandwidth" (widest loads, full lines,
 //   weights read once with an evict-first hint).
 // * Activations.  The A tile of each 128-row K step is loaded once per workgroup (one
-//   16-byte chunk per thread per 16 rows) and staged in a two-stage LDS ring, XOR-swizzled
+//   16-byte chunk per thread per 16 rows) and staged in a three-stage LDS ring, XOR-swizzled
 //   so stores and the 16-lane fragment reads are bank-conflict-free; all four waves read
 //   their MFMA fragments from it.  A is re-read from L2 once per column slice, so wide
 //   slices keep its traffic below the weight stream's (MARLIN paper sec. 3.4 "Bound By
@@ -37,12 +37,12 @@
 //   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs).
 // * Cross-workgroup reduction.  Only the first and last slice of a stripe can be shared
 //   with a neighbouring stripe.  At such a slice's end the workgroup writes its fp32 partial
-//   tile to its own workspace slot with device-scope (write-through) stores and streams on
-//   without waiting.  After its last tile it waits once for its stores, bumps each shared
-//   slice's counter, and the contributor that draws the last count reads the partials back
-//   past the L2, adds them in stripe order (a fixed order, so results are bitwise
-//   repeatable), writes C and resets the counter.  No cache-wide writeback or invalidate is
-//   issued and no workgroup ever waits for another.  The pages sum such partials serially with locks and stage them
+//   tile to its own workspace slot with device-scope stores and streams on without
+//   waiting.  After its last tile it waits once for its stores, releases them at device
+//   scope and bumps each shared slice's counter; the contributor that draws the last count
+//   acquires at device scope, adds the partials in stripe order (a fixed order, so results
+//   are bitwise repeatable), writes C and resets the counter.  The cache-wide fences run
+//   once per workgroup after its stream has ended, and no workgroup ever waits for another.  The pages sum such partials serially with locks and stage them
 //   in fp16 in the output (deep-dive page section "为什么归约串行，却不一定慢"); fp32
 //   partials and a last-arriver sum keep the same "no big temporary" property, keep full
 //   precision, and never spin, so no co-residency assumption is needed.
@@ -140,6 +140,7 @@ struct Tile {
     static constexpr int Mt = 16 * MB;                 // rows per M sub-problem
     static constexpr int Nt = 16 * NBW * kWaves;       // columns per slice
     static constexpr int kStageQuads = MB * 256;       // 16-byte LDS chunks per A stage
+    static constexpr int kStages = 3;                  // A ring depth (see the kernel loop)
     static constexpr int kSlotFloats = Mt * Nt;
 };
 
@@ -343,11 +344,13 @@ __device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rs
 // After the stripe's last tile: settle the (at most two) split slices it touched -- the
 // first, which it may have entered part-way (slot 0), and the last, which it may have left
 // part-way (slot 1).  part0 / part1 are those slices as recorded when their partials were
-// stored, or -1.  Every wave first waits for all its stores (the partials are then in
-// memory), the workgroup synchronises, and thread 0 counts this stripe in for each split
-// slice with a device-scope atomic.  The stripe that draws the last count of a slice sums
-// all its partials and writes C.  Nobody ever waits for another workgroup, so no
-// co-residency is assumed.
+// stored, or -1.  Every wave first waits for its stores, the workgroup synchronises, and
+// thread 0 releases the partials at device scope and counts this stripe in for each split
+// slice with a device-scope atomic.  The stripe that draws the last count of a slice
+// acquires at device scope, sums all its partials and writes C.  The L2s of the XCDs are not
+// coherent with each other, and a workgroup's XCD is not known in advance, so both fences
+// are needed; they run once per workgroup, after its stream has ended.  Nobody ever waits
+// for another workgroup, so no co-residency is assumed.
 template <int MB, int NBW>
 __device__ __forceinline__ void settle_split_slices(const Params &p, __amdgpu_buffer_rsrc_t rP,
                                                     long long part0, long long part1, int tid,
@@ -356,9 +359,12 @@ __device__ __forceinline__ void settle_split_slices(const Params &p, __amdgpu_bu
     if (part0 < 0 && part1 < 0)
         return;
     const int wave = tid >> 6, lane = tid & 63;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's partials are in memory
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's partial stores are done
     __syncthreads();
     if (tid == 0) {
+        // Release at device scope: the workgroup's partials (ordered before this point by
+        // the barrier) become visible to every XCD before the counters move.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         if (part0 >= 0)
             flag[0] = __hip_atomic_fetch_add(p.counters + stripe_owner(part0 * p.G, p.T, p.W), 1,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -376,6 +382,9 @@ __device__ __forceinline__ void settle_split_slices(const Params &p, __amdgpu_bu
         const int w_hi = stripe_owner(sigma * p.G + p.G - 1, p.T, p.W);
         if (flag[i] != w_hi - w_lo)
             continue;               // another contributor is still running; it will finish
+        // Acquire at device scope: drop any stale copy of the other contributors' partials
+        // this XCD's caches may hold before reading them.
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         reduce_slice<MB, NBW>(p, rP, sigma, w_lo, w_hi, wave, lane);
         if (tid == 0)
             __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -386,7 +395,7 @@ template <int MB, int NBW>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
 {
     using TL = Tile<MB, NBW>;
-    __shared__ u4 lds[2 * TL::kStageQuads];
+    __shared__ u4 lds[TL::kStages * TL::kStageQuads];
     __shared__ int flag[2];
 
     const int tid = threadIdx.x;
@@ -461,20 +470,24 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     };
 
     // Registers: weights double-buffered (tile i in buffer i % 2); A staged through `ar`
-    // into a two-stage LDS ring (tile i in stage i % 2).  Per tile i the order is
-    //   store A(i+1) -> LDS, load A(i+2) -> ar, barrier, compute(i), load W(i+2).
+    // into a three-stage LDS ring (tile i in stage i % 3).  Per tile i the order is
+    //   store A(i+1) -> stage (i+1) % 3, load A(i+2) -> ar, barrier, compute(i), load W(i+2).
+    // Ring safety: the stage written at tile i was last read by compute(i-2), and no wave
+    // passes barrier(i-1) before every wave has finished compute(i-2); the data stored at
+    // tile i is visible to compute(i+1) through barrier(i).  (With two stages a fast wave
+    // could overwrite the stage a slow wave is still reading.)
     // The vector-memory counter completes in order, and every A load is issued before the
     // weight load of the same tile, so waiting for A(i+1) never waits for a weight tile that
     // is not needed yet: each weight tile has one whole tile of compute to arrive in.
     u4 ar[MB];
     u4 wq0[NBW], wq1[NBW];
     uint32_t sc0[NBW], sc1[NBW];
-    u4 *const st0 = lds;
-    u4 *const st1 = lds + TL::kStageQuads;
+    int st_cp = 0, st_st = 1;             // ring stages being computed from / stored to
+    auto next_stage = [](int x) { return x == TL::kStages - 1 ? 0 : x + 1; };
 
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0)
     load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);        // W(t0)
-    store_a<MB>(st0, tid, ar);
+    store_a<MB>(lds, tid, ar);                                // stage 0
     step_load();
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0+1)
     load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
@@ -508,34 +521,38 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     };
 
     // Whole pairs of tiles per iteration; a single trailing tile is finished after the
-    // loop.  A slice's end is handled before the next weight tile is requested, so the
-    // epilogue's wait for its own stores only waits for loads the next tile needs anyway.  Exiting only at the end of a pair keeps the control flow simple enough for the
-    // compiler to wait for exactly one tile's loads.  The asm/scheduling barriers keep each
-    // tile's loads after the last use of the registers they overwrite.
+    // loop.  Exiting only at the end of a pair keeps the control flow simple enough for the
+    // compiler to wait for exactly one tile's loads.  A slice's end is handled before the
+    // next weight tile is requested.  The asm/scheduling barriers keep each tile's loads
+    // after the last use of the registers they overwrite.
     while (t + 1 < t1) {
-        store_a<MB>(st1, tid, ar);                            // A(t+1)
+        store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
-        compute_tile<MB, NBW>(st0, lane, wq0, sc0, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
         load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);    // W(t+2)
         step_load();
+        st_cp = st_st;
+        st_st = next_stage(st_st);
 
-        store_a<MB>(st0, tid, ar);                            // A(t+1)
+        store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
-        compute_tile<MB, NBW>(st1, lane, wq1, sc1, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq1, sc1, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
         load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);    // W(t+2)
         step_load();
+        st_cp = st_st;
+        st_st = next_stage(st_st);
     }
     if (t < t1) {
         __syncthreads();
-        compute_tile<MB, NBW>(st0, lane, wq0, sc0, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
         end_of_tile();
     }
     settle_split_slices<MB, NBW>(p, rP, part0, part1, tid, flag);
@@ -593,42 +610,12 @@ int check_gemm_shape(int M, int K, int N)
     return W4A16_OK;
 }
 
-template <int MB, int NBW>
-int resident_per_cu()
-{
-    // workgroups of this variant one CU can hold at once (registers and LDS permitting)
-    static const int n = [] {
-        int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, w4a16_gemm_kernel<MB, NBW>, kThreads,
-                                                         0) != hipSuccess || b < 1)
-            b = 1;
-        return b;
-    }();
-    return n;
-}
-
-int resident_per_cu(int MB, int NBW)
-{
-    switch (MB * 10 + NBW) {
-    case 11: return resident_per_cu<1, 1>();
-    case 12: return resident_per_cu<1, 2>();
-    case 14: return resident_per_cu<1, 4>();
-    case 21: return resident_per_cu<2, 1>();
-    case 22: return resident_per_cu<2, 2>();
-    case 24: return resident_per_cu<2, 4>();
-    case 41: return resident_per_cu<4, 1>();
-    case 42: return resident_per_cu<4, 2>();
-    default: return 1;
-    }
-}
-
 // Number of stripes: a whole number of workgroups per CU, so every CU streams the same
 // amount (a fractional count leaves some CUs with one workgroup more than others).  Two per
 // CU keep the weight stream busy up to M = 32; at 64-row tiles each byte carries more work
 // and three per CU measure faster.
-int choose_stripes(long long T, int MB, int NBW, int cus)
+int choose_stripes(long long T, int MB, int cus)
 {
-    (void)NBW;
     const int per_cu = MB <= 2 ? 2 : 3;
     long long w = static_cast<long long>(cus) * per_cu;
     if (w > kMaxWGs)
@@ -655,7 +642,7 @@ Config choose_config(int M, int K, int N, int cus)
         }
     c.S = N / (16 * kWaves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
-    c.W = choose_stripes(c.T, c.MB, c.NBW, cus);
+    c.W = choose_stripes(c.T, c.MB, cus);
     return c;
 }
 

@@ -107,6 +107,22 @@ def test_shapes_tiles_and_reduction(K, N, M):
     check(gpu_gemm(A, q, s), oracle.gemm(A, q, s), f"K={K} N={N} M={M}")
 
 
+@pytest.mark.parametrize("M,K,N", [(64, 18432, 4096), (128, 4096, 8192), (64, 18432, 1024),
+                                   (100, 8192, 4096), (16, 18432, 2048), (32, 18432, 4096)])
+def test_long_stripes_many_contributors_fresh_workspaces(M, K, N):
+    # Slices shared by many stripes, more workgroups than fit on the chip at once (so some
+    # start late, on whichever XCD has room), and a freshly zero-filled workspace whose lines
+    # other caches may still hold: the device-scope release/acquire must make every
+    # partial visible to the stripe that sums it.
+    A, q, s = draw(K, N, M, seed=M + K + N)
+    W = Weights(q, s)
+    ref = oracle.gemm(A, q, s)
+    for rep in range(2):
+        ws = w4.new_workspace(M, K, N)
+        check(W.run(A, ws=ws), ref, f"M={M} K={K} N={N} rep={rep}")
+        assert int(ws[:4096].count_nonzero()) == 0
+
+
 def test_m1_equals_gemv():
     A, q, s = draw(4096, 1024, 1, seed=21)
     check(gpu_gemm(A, q, s)[0], oracle.gemv(A[0], q, s), "M=1 vs gemv")
