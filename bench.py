@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-cols", type=int, default=16384,
+    ap.add_argument("--cpu-cols", type=int, default=65536,
                     help="columns of the CPU-baseline sample (0 skips it)")
     ap.add_argument("--copies", type=int, default=2,
                     help="weight copies rotated between calls so no call hits the MALL")

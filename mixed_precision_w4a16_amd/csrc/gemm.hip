@@ -205,17 +205,21 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
         stage[(16 * mb + r) * 16 + (c ^ r)] = ar[mb];
 }
 
-// This wave's packed weight quads (1 KiB contiguous per slab, non-temporal) and scales.
-template <int NBW>
+// This wave's packed weight quads (1 KiB contiguous per slab) and scales.  With 16-row
+// tiles every weight byte is used once, so it is streamed non-temporally (evict first, the
+// pages' evict_first hint).  Larger tiles re-read a slice's weights for the next 64-row
+// sub-problem right away, and measure faster with the weights left in the cache.
+template <int MB, int NBW>
 __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
                                        int G, int lane, uint32_t wblk, u4 (&wq)[NBW],
                                        uint32_t (&sc)[NBW])
 {
+    constexpr int policy = MB == 1 ? kNonTemporal : 0;
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
         wq[b] = __builtin_bit_cast(
-            u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, kNonTemporal));
+            u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, policy));
         // the aligned dword holding this column's scale and its neighbour's (a 16-bit load
         // result would be re-copied across the loop back-edge)
         sc[b] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, blk * 32u, 0);
@@ -489,11 +493,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     auto next_stage = [](int x) { return x == TL::kStages - 1 ? 0 : x + 1; };
 
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0)
-    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);        // W(t0)
+    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);        // W(t0)
     store_a<MB>(lds, tid, ar);                                // stage 0
     step_load();
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0+1)
-    load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
+    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
     step_load();                                              // lc -> t0+2
 
     // End of a tile: at a slice's end, write C if this stripe owns the whole slice, else
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
-        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);    // W(t+2)
+        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);    // W(t+2)
         step_load();
         st_cp = st_st;
         st_st = next_stage(st_st);
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
-        load_w<NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);    // W(t+2)
+        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);    // W(t+2)
         step_load();
         st_cp = st_st;
         st_st = next_stage(st_st);
