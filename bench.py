@@ -80,8 +80,8 @@ def cpu_baseline(A, q, s, Ms, ncols, nthreads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-cols", type=int, default=65536,
                     help="columns of the CPU-baseline sample (0 skips it)")
     ap.add_argument("--copies", type=int, default=2,
