@@ -226,6 +226,18 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
     }
 }
 
+// Where the group scale is applied.  Small tiles (MB <= 2) keep (q - 8) exact: the MFMA
+// sums A * (q - 8) over the group in fp32 and the fp32 partial is scaled once per output
+// (4 FMAs per 16x16 tile per group).  With 64 or more rows the per-tile FMAs and the partial
+// registers cost more than scaling the weights: each dequantised pair is multiplied by the
+// column's scale in fp16 (one packed multiply per two weights, the pages' own order:
+// dequantise, scale, then MMA) and the MFMA accumulates straight into the output sum.  The
+// rounding of s * (q - 8) to fp16 is below 2^-11 relative per weight.
+template <int MB>
+struct ScaleMode {
+    static constexpr bool kWeights = MB >= 4;
+};
+
 template <int MB, int NBW>
 __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4 (&wq)[NBW],
                                              const uint32_t (&sc)[NBW], f4 (&acc)[MB][NBW],
@@ -235,10 +247,17 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
     // next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
     const int sshift = (lane & 1) * 16;               // odd columns: high half of the dword
     float sf[NBW];
+    h8 s8[NBW];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
-        sf[b] = half_bits_to_float(static_cast<uint16_t>(sc[b] >> sshift));
-        asm volatile("" : "+v"(sf[b]));
+        if constexpr (ScaleMode<MB>::kWeights) {
+            const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sc[b] >> sshift));
+            s8[b] = h8{sh, sh, sh, sh, sh, sh, sh, sh};
+            asm volatile("" : "+v"(s8[b]));
+        } else {
+            sf[b] = half_bits_to_float(static_cast<uint16_t>(sc[b] >> sshift));
+            asm volatile("" : "+v"(sf[b]));
+        }
     }
     // A fragments from LDS: row lane%16 of each sub-tile, k = 32t + 8(lane/16) .. +7.
     const int row = lane & 15, quad = lane >> 4;
@@ -248,6 +267,26 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
+
+    if constexpr (ScaleMode<MB>::kWeights) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const h8 bw = dequant8(wq[b][t], mlo, mhi, magic) * s8[b];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bw, acc[mb][b],
+                                                                        0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                asm volatile("" : "+v"(acc[mb][b]));    // finish the update here
+        return;
+    }
 
     f4 part[MB][NBW];
 #pragma unroll
@@ -619,12 +658,10 @@ int check_gemm_shape(int M, int K, int N)
 
 // Number of stripes: a whole number of workgroups per CU, so every CU streams the same
 // amount (a fractional count leaves some CUs with one workgroup more than others).  Two per
-// CU keep the weight stream busy up to M = 32; at 64-row tiles each byte carries more work
-// and three per CU measure faster.
-int choose_stripes(long long T, int MB, int cus)
+// CU measured best for every tile size.
+int choose_stripes(long long T, int cus)
 {
-    const int per_cu = MB <= 2 ? 2 : 3;
-    long long w = static_cast<long long>(cus) * per_cu;
+    long long w = static_cast<long long>(cus) * 2;
     if (w > kMaxWGs)
         w = kMaxWGs;
     if (w > T)
@@ -639,17 +676,16 @@ Config choose_config(int M, int K, int N, int cus)
     const int Mt = 16 * c.MB;
     c.P = (M + Mt - 1) / Mt;
     c.G = K / kGroup;
-    // widest slice that divides N; MB = 4 keeps 2 slabs per wave for register room
-    const int max_nbw = c.MB == 4 ? 2 : 4;
+    // widest slice (4 slabs per wave) that divides N
     c.NBW = 1;
-    for (int nbw = max_nbw; nbw >= 1; nbw >>= 1)
+    for (int nbw = 4; nbw >= 1; nbw >>= 1)
         if (N % (16 * kWaves * nbw) == 0) {
             c.NBW = nbw;
             break;
         }
     c.S = N / (16 * kWaves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
-    c.W = choose_stripes(c.T, c.MB, cus);
+    c.W = choose_stripes(c.T, cus);
     return c;
 }
 
@@ -725,6 +761,7 @@ extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t 
     case 24: e = launch<2, 4>(p, s); break;
     case 41: e = launch<4, 1>(p, s); break;
     case 42: e = launch<4, 2>(p, s); break;
+    case 44: e = launch<4, 4>(p, s); break;
     default: return W4A16_EHIP;
     }
     return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
