@@ -52,6 +52,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "w4a16.h"
 
@@ -135,10 +136,10 @@ __device__ __forceinline__ int stripe_owner(long long t, long long T, int W)
     return static_cast<int>(((t + 1) * W - 1) / T);
 }
 
-template <int MB, int NBW>
+template <int MB, int NBW, int WAVES = kWaves>
 struct Tile {
     static constexpr int Mt = 16 * MB;                 // rows per M sub-problem
-    static constexpr int Nt = 16 * NBW * kWaves;       // columns per slice
+    static constexpr int Nt = 16 * NBW * WAVES;        // columns per slice
     static constexpr int kStageQuads = MB * 256;       // 16-byte LDS chunks per A stage
     static constexpr int kStages = 3;                  // A ring depth (see the kernel loop)
     static constexpr int kSlotFloats = Mt * Nt;
@@ -162,10 +163,10 @@ struct LoadCursor {
     uint32_t a_soff;    // byte offset of K step g in an A row (uniform)
 };
 
-template <int MB, int NBW>
+template <int MB, int NBW, int WAVES = kWaves>
 __device__ __forceinline__ void load_cursor_set(const Params &p, int wave, LoadCursor &c)
 {
-    c.wblk = (static_cast<uint32_t>(c.s) * (kWaves * NBW) + wave * NBW) * p.G + c.g;
+    c.wblk = (static_cast<uint32_t>(c.s) * (WAVES * NBW) + wave * NBW) * p.G + c.g;
     c.a_soff = static_cast<uint32_t>(c.g) * (kGroup * 2);
 }
 
@@ -224,6 +225,16 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
         // result would be re-copied across the loop back-edge)
         sc[b] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, blk * 32u, 0);
     }
+}
+
+// One slab of load_w (used by the wide kernel, which spreads its loads over the tile).
+__device__ __forceinline__ void load_w_slab(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
+                                            int G, int lane, uint32_t wblk, int b, u4 &wq,
+                                            uint32_t &sc)
+{
+    const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
+    wq = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, 0));
+    sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, blk * 32u, 0);
 }
 
 // Where the group scale is applied.  Small tiles (MB <= 2) keep (q - 8) exact: the MFMA
@@ -312,128 +323,261 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
         }
 }
 
-// acc[mb][b][r] is C[row0 + 16mb + 4(lane/16) + r][col0 + 16b + lane%16].
-template <int MB, int NBW>
-__device__ __forceinline__ void write_c(const Params &p, int wave, int lane, long long sigma,
-                                        const f4 (&acc)[MB][NBW])
+// Opaque copy of a uniform value: offsets derived from it are computed where they are used.
+// Without it the compiler hoists every loop-invariant store offset of the epilogue out of the
+// main loop and keeps them all live there.
+__device__ __forceinline__ uint32_t opaque(uint32_t x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// acc[mb][b][r] is C[row0 + 16mb + 4(lane/16) + r][col0 + 16b + lane%16].  C is written
+// through a buffer resource of exactly M * N * 2 bytes: stores to rows at or past M fall
+// outside it and are dropped by the hardware, so no per-row test is needed.  The lane's own
+// offset is one VGPR; the tile's position and the (mb, r) row are a running scalar offset and
+// 16b columns an immediate.
+template <int MB, int NBW, int WAVES = kWaves>
+__device__ __forceinline__ void write_c(const Params &p, __amdgpu_buffer_rsrc_t rC, int wave,
+                                        int lane, long long sigma, const f4 (&acc)[MB][NBW])
 {
     const long long s = sigma / p.P;
     const int pm = static_cast<int>(sigma - s * p.P);
-    const int row0 = pm * 16 * MB + 4 * (lane >> 4);
-    const size_t col0 = static_cast<size_t>(s) * Tile<MB, NBW>::Nt + wave * NBW * 16 + (lane & 15);
+    const uint32_t rowN = opaque(static_cast<uint32_t>(p.N) * 2);
+    const uint32_t voff = ((4 * (lane >> 4)) * static_cast<uint32_t>(p.N) + wave * NBW * 16 +
+                           (lane & 15)) * 2;
+    uint32_t srow = __builtin_amdgcn_readfirstlane(
+        (static_cast<uint32_t>(pm * 16 * MB) * static_cast<uint32_t>(p.N) +
+         static_cast<uint32_t>(s) * Tile<MB, NBW, WAVES>::Nt) * 2);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-        for (int b = 0; b < NBW; ++b)
+        for (int r = 0; r < 4; ++r) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 16 * mb + r;
-                if (row < p.M)
-                    p.C[static_cast<size_t>(row) * p.N + col0 + 16 * b] =
-                        float_to_half_bits(acc[mb][b][r]);
-            }
+            for (int b = 0; b < NBW; ++b)
+                __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(acc[mb][b][r]), rC,
+                                                      voff + 32 * b, srow, 0);
+            srow += rowN;
+        }
+        srow += 12 * rowN;             // the other three lane groups' rows of this 16-row block
+    }
 }
 
-// Byte offset of this lane's 16-byte piece of sub-tile (mb, b) in partial slot `slot` of
-// stripe `stripe`.
-template <int MB, int NBW>
-__device__ __forceinline__ uint32_t slot_offset(int stripe, int slot, int wave, int mb, int b,
-                                                int lane)
+// Partial slot layout: slot `slot` of stripe `stripe` holds the workgroup's Mt x Nt fp32 tile
+// as 16-byte pieces, piece (wave, mb, b, lane) at 16 * (((wave * MB + mb) * NBW + b) * 64 + lane).
+// The 128-row tiles keep only the lane part in a vector register and compute the rest as a
+// scalar offset where it is used (their vector registers are all taken by the accumulators);
+// the smaller tiles keep whole offsets in vector registers, which measures faster there.
+template <int MB, int NBW, int WAVES>
+__device__ __forceinline__ uint32_t slot_base(int stripe, int slot, int wave, int mb, int b)
 {
-    return ((static_cast<uint32_t>(stripe) * 2 + slot) * Tile<MB, NBW>::kSlotFloats +
-            ((wave * MB + mb) * NBW + b) * 256 + lane * 4) * 4;
+    return ((static_cast<uint32_t>(stripe) * 2 + slot) * Tile<MB, NBW, WAVES>::kSlotFloats +
+            ((wave * MB + mb) * NBW + b) * 256) * 4;
+}
+
+template <int MB, int NBW, int WAVES>
+__device__ __forceinline__ void slot_store(__amdgpu_buffer_rsrc_t rP, uint32_t sbase, int stripe,
+                                           int slot, int wave, int mb, int b, int lane, f4 v)
+{
+    if constexpr (MB >= 8)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), rP, lane * 16,
+                                               sbase + (mb * NBW + b) * 1024, kDeviceScope);
+    else
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u4, v), rP,
+            slot_base<MB, NBW, WAVES>(stripe, slot, wave, mb, b) + lane * 16, 0, kDeviceScope);
+}
+
+template <int MB, int NBW, int WAVES>
+__device__ __forceinline__ f4 slot_load(__amdgpu_buffer_rsrc_t rP, uint32_t sbase, int stripe,
+                                        int slot, int wave, int mb, int b, int lane)
+{
+    if constexpr (MB >= 8)
+        return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rP, lane * 16, sbase + (mb * NBW + b) * 1024,
+                                          kDeviceScope));
+    else
+        return __builtin_bit_cast(
+            f4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rP, slot_base<MB, NBW, WAVES>(stripe, slot, wave, mb, b) + lane * 16, 0,
+                    kDeviceScope));
+}
+
+// Scalar base of a wave's pieces in a slot (used by the 128-row tiles).
+template <int MB, int NBW, int WAVES>
+__device__ __forceinline__ uint32_t slot_sbase(int stripe, int slot, int wave)
+{
+    return opaque(__builtin_amdgcn_readfirstlane(slot_base<MB, NBW, WAVES>(stripe, slot, wave, 0, 0)));
 }
 
 // Partial tile of a split slice -> this stripe's workspace slot, with device-scope
 // (write-through) stores.  Nothing waits here: the stores complete while streaming goes on.
-template <int MB, int NBW>
+template <int MB, int NBW, int WAVES = kWaves>
 __device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t rP, int stripe, int slot,
                                               int wave, int lane, const f4 (&acc)[MB][NBW])
 {
+    const uint32_t sbase = MB >= 8 ? slot_sbase<MB, NBW, WAVES>(stripe, slot, wave) : 0;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u4, acc[mb][b]), rP,
-                slot_offset<MB, NBW>(stripe, slot, wave, mb, b, lane), 0, kDeviceScope);
+            slot_store<MB, NBW, WAVES>(rP, sbase, stripe, slot, wave, mb, b, lane, acc[mb][b]);
 }
 
-// Sum the partials of split slice sigma in stripe order (a fixed order: results repeat bit
-// for bit) and write C.  Partials are read past the L2 with device-scope loads.
-template <int MB, int NBW>
-__device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rsrc_t rP,
-                                             long long sigma, int w_lo, int w_hi, int wave,
-                                             int lane)
+// The partial slot stripe w used for split slice sigma: 0 if sigma is the slice the stripe
+// starts in, else 1 (the slice it ends in).
+__device__ __forceinline__ int slot_of(const Params &p, long long sigma, int w)
 {
-    f4 sum[MB][NBW];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int b = 0; b < NBW; ++b)
-            sum[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int w = w_lo; w <= w_hi; ++w) {
-        const int slot = (sigma == stripe_begin(w, p.T, p.W) / p.G) ? 0 : 1;
+    return sigma == stripe_begin(w, p.T, p.W) / p.G ? 0 : 1;
+}
+
+// Sum the pieces of split slice sigma in stripe order w_lo .. w_hi (a fixed order: results
+// repeat bit for bit) and write C.  The sum is formed in `acc`, which on entry either holds the
+// first piece (the owner's own, kept in registers) or is free, and then gets the first piece
+// from its slot like the others: either way the additions are the same.  Partials are read
+// past the L2 with device-scope loads, half a tile at a time so that the loads in flight fit
+// in the registers next to the sum (spilling would serialise them).
+template <int MB, int NBW, int WAVES = kWaves>
+__device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rsrc_t rP,
+                                             __amdgpu_buffer_rsrc_t rC, long long sigma,
+                                             int w_lo, int w_hi, int wave, int lane,
+                                             bool first_in_regs, f4 (&acc)[MB][NBW])
+{
+    constexpr int H = MB >= 8 ? MB / 4 : (MB >= 2 ? MB / 2 : 1);   // row blocks per load round
+    if (!first_in_regs) {
+        const int slot = slot_of(p, sigma, w_lo);
+        const uint32_t sbase = MB >= 8 ? slot_sbase<MB, NBW, WAVES>(w_lo, slot, wave) : 0;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int b = 0; b < NBW; ++b)
-                sum[mb][b] += __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rP, slot_offset<MB, NBW>(w, slot, wave, mb, b, lane), 0, kDeviceScope));
+                acc[mb][b] = slot_load<MB, NBW, WAVES>(rP, sbase, w_lo, slot, wave, mb, b, lane);
     }
-    write_c<MB, NBW>(p, wave, lane, sigma, sum);
+    for (int w = w_lo + 1; w <= w_hi; ++w) {
+        const int slot = slot_of(p, sigma, w);
+        const uint32_t sbase = MB >= 8 ? slot_sbase<MB, NBW, WAVES>(w, slot, wave) : 0;
+#pragma unroll
+        for (int h = 0; h < MB; h += H) {
+            f4 x[H][NBW];
+#pragma unroll
+            for (int mb = 0; mb < H; ++mb)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                    x[mb][b] = slot_load<MB, NBW, WAVES>(rP, sbase, w, slot, wave, h + mb, b, lane);
+#pragma unroll
+            for (int mb = 0; mb < H; ++mb)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                    acc[h + mb][b] += x[mb][b];
+        }
+    }
+    write_c<MB, NBW, WAVES>(p, rC, wave, lane, sigma, acc);
 }
 
-// After the stripe's last tile: settle the (at most two) split slices it touched -- the
-// first, which it may have entered part-way (slot 0), and the last, which it may have left
-// part-way (slot 1).  part0 / part1 are those slices as recorded when their partials were
-// stored, or -1.  Every wave waits for its own stores, the workgroup synchronises, and
-// thread 0 counts this stripe in for each split slice with a device-scope atomic.  The
-// stripe that draws the last count of a slice sums all its partials and writes C.  Nobody
-// ever waits for another workgroup, so no co-residency is assumed.
+// End of a slice (or of the stripe) for the running accumulators.  Three cases:
+//  * the stripe computed the whole slice: write C;
+//  * the stripe entered the slice part-way (so it is the slice it started in): store the
+//    piece to slot 0 and record it in `nonown`;
+//  * the stripe holds the slice's first tile but not its last (so this is its last tile):
+//    it is the slice's owner and keeps its piece in the accumulators for settle().
+template <int MB, int NBW, int WAVES = kWaves>
+__device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_t rP,
+                                          __amdgpu_buffer_rsrc_t rC, int stripe, long long t0,
+                                          long long t, long long sigma, int wave, int lane,
+                                          const f4 (&acc)[MB][NBW], long long &nonown,
+                                          long long &own)
+{
+    const long long s0 = sigma * p.G;
+    if (t0 <= s0 && t == s0 + p.G - 1) {
+        write_c<MB, NBW, WAVES>(p, rC, wave, lane, sigma, acc);
+    } else if (t0 <= s0) {
+        own = sigma;
+    } else {
+        store_partial<MB, NBW, WAVES>(rP, stripe, 0, wave, lane, acc);
+        nonown = sigma;
+    }
+}
+
+// After the stripe's last tile: settle the (at most two) split slices it touched.  A split
+// slice is shared by stripes w_lo .. w_hi; its owner w_lo holds the slice's first tiles, which
+// come at the very end of w_lo's stripe, while the others entered the slice part-way and (all
+// but the middle ones) finished their pieces early.  The owner is therefore usually the last
+// to arrive, and it then sums the others' stored pieces with its own, which it never stores.
+//
+// Each slice has a counter (at counters[w_lo]): every other contributor adds 1 once its piece
+// is stored; the owner adds kArrived when it arrives.  The owner sums at once if the other
+// c - 1 pieces are all in; otherwise it stores its piece too and adds 1, and whoever brings
+// the low count to c (owner or not) sums everything from the slots.  Exactly one contributor
+// sums, it resets the counter, and nobody waits for another workgroup, so no co-residency is
+// assumed.  Thread 0 does the counting; the result is broadcast through LDS.
 //
 // Visibility without cache-wide fences.  The XCDs' L2s are not coherent with each other,
 // and a workgroup's XCD is not known in advance.  Partial slots are therefore only ever
 // written with device-scope stores and read with device-scope loads -- the cache-policy
 // encodings the compiler itself uses for device-scope atomic stores and loads, which must be
 // coherent across XCDs.  A writer's stores have completed (s_waitcnt vmcnt(0)) before its
-// counter increment is issued, and a reader issues its loads only after its own increment
-// has returned the final count.  Each slot is written once per call and read once, after its
-// write, and a slot owns whole cache lines, so no XCD can hold a stale copy made during the
-// call; copies from earlier work do not survive the cache invalidation at kernel start.
-// A release/acquire fence pair would add an L2 writeback and invalidate per workgroup;
-// measured, that costs about a sixth of the runtime at M <= 16.
-template <int MB, int NBW>
-__device__ __forceinline__ void settle_split_slices(const Params &p, __amdgpu_buffer_rsrc_t rP,
-                                                    long long part0, long long part1, int tid,
-                                                    int *flag)
+// counter increment is issued, and a reader issues its loads only after its own counter
+// access has returned a value that includes every writer's increment.  Each slot is written
+// at most once per call and read once, after its write, and a slot owns whole cache lines, so
+// no XCD can hold a stale copy made during the call; copies from earlier work do not survive
+// the cache invalidation at kernel start.  A release/acquire fence pair would add an L2
+// writeback and invalidate per workgroup; measured, that costs about a sixth of the runtime
+// at M <= 16.
+constexpr int kArrived = 1 << 16;
+constexpr int kCountMask = kArrived - 1;
+
+template <int MB, int NBW, int WAVES = kWaves>
+__device__ __forceinline__ void settle(const Params &p, __amdgpu_buffer_rsrc_t rP,
+                                       __amdgpu_buffer_rsrc_t rC, int stripe, long long nonown,
+                                       long long own, int tid, f4 (&acc)[MB][NBW], int *flag)
 {
-    if (part0 < 0 && part1 < 0)
+    if (nonown < 0 && own < 0)
         return;
     const int wave = tid >> 6, lane = tid & 63;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's partial stores are done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's stores are done
     __syncthreads();
     if (tid == 0) {
-        if (part0 >= 0)
-            flag[0] = __hip_atomic_fetch_add(p.counters + stripe_owner(part0 * p.G, p.T, p.W), 1,
+        if (nonown >= 0)
+            flag[0] = __hip_atomic_fetch_add(p.counters + stripe_owner(nonown * p.G, p.T, p.W), 1,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (part1 >= 0)
-            flag[1] = __hip_atomic_fetch_add(p.counters + stripe_owner(part1 * p.G, p.T, p.W), 1,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (own >= 0)
+            flag[1] = __hip_atomic_fetch_add(p.counters + stripe, kArrived, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const long long sigma = i == 0 ? part0 : part1;
-        if (sigma < 0)
-            continue;
-        const int w_lo = stripe_owner(sigma * p.G, p.T, p.W);
-        const int w_hi = stripe_owner(sigma * p.G + p.G - 1, p.T, p.W);
-        if (flag[i] != w_hi - w_lo)
-            continue;               // another contributor is still running; it will finish
-        reduce_slice<MB, NBW>(p, rP, sigma, w_lo, w_hi, wave, lane);
-        if (tid == 0)
-            __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The owned slice first: its piece is still in the accumulators, which are dead after.
+    if (own >= 0) {
+        const int w_hi = stripe_owner(own * p.G + p.G - 1, p.T, p.W);
+        const int c = w_hi - stripe + 1;
+        if ((flag[1] & kCountMask) == c - 1) {
+            reduce_slice<MB, NBW, WAVES>(p, rP, rC, own, stripe, w_hi, wave, lane, true, acc);
+            if (tid == 0)
+                __hip_atomic_store(p.counters + stripe, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            store_partial<MB, NBW, WAVES>(rP, stripe, slot_of(p, own, stripe), wave, lane, acc);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0)
+                flag[1] = __hip_atomic_fetch_add(p.counters + stripe, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (((flag[1] + 1) & kCountMask) == c) {
+                reduce_slice<MB, NBW, WAVES>(p, rP, rC, own, stripe, w_hi, wave, lane, false, acc);
+                if (tid == 0)
+                    __hip_atomic_store(p.counters + stripe, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (nonown >= 0) {
+        const int w_lo = stripe_owner(nonown * p.G, p.T, p.W);
+        const int w_hi = stripe_owner(nonown * p.G + p.G - 1, p.T, p.W);
+        const int v = flag[0] + 1;
+        if ((v & kArrived) && (v & kCountMask) == w_hi - w_lo + 1) {
+            reduce_slice<MB, NBW, WAVES>(p, rP, rC, nonown, w_lo, w_hi, wave, lane, false, acc);
+            if (tid == 0)
+                __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -467,6 +611,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
     const __amdgpu_buffer_rsrc_t rP =
         make_rsrc(p.partials, static_cast<uint32_t>(2u * p.W * TL::kSlotFloats * 4u));
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
 
     // dequant constants in VGPRs for v_and_or_b32
     const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
@@ -483,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     const long long sigma0 = t0 / p.G;           // the stripe's first slice
     long long sigma = sigma0;
     int g = static_cast<int>(t0 - sigma * p.G);
-    long long part0 = -1, part1 = -1;            // split slices whose partials were stored
+    long long nonown = -1, own = -1;             // split slices (see slice_end / settle)
 
     // Load position, clamped to the stripe's last tile so every load is unconditional (a
     // re-read of the last tile is a cache hit).  A loads run two tiles ahead of the compute;
@@ -539,20 +685,15 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
     step_load();                                              // lc -> t0+2
 
-    // End of a tile: at a slice's end, write C if this stripe owns the whole slice, else
-    // leave its partial in the workspace for settle_split_slices.
+    // End of a tile: at a slice's end, hand the accumulators to slice_end.  The stripe's last
+    // piece is finished after the loop (it may be kept in the accumulators for settle).
     auto end_of_tile = [&]() {
-        if (g == p.G - 1 || t + 1 == t1) {
-            const long long s0 = sigma * p.G;
-            if (t0 <= s0 && t == s0 + p.G - 1) {
-                write_c<MB, NBW>(p, wave, lane, sigma, acc);
-            } else if (sigma == sigma0) {
-                store_partial<MB, NBW>(rP, stripe, 0, wave, lane, acc);
-                part0 = sigma;
-            } else {
-                store_partial<MB, NBW>(rP, stripe, 1, wave, lane, acc);
-                part1 = sigma;
-            }
+        if (t + 1 == t1) {
+            ++t;
+            return;
+        }
+        if (g == p.G - 1) {
+            slice_end<MB, NBW>(p, rP, rC, stripe, t0, t, sigma, wave, lane, acc, nonown, own);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -601,7 +742,300 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
         end_of_tile();
     }
-    settle_split_slices<MB, NBW>(p, rP, part0, part1, tid, flag);
+    slice_end<MB, NBW>(p, rP, rC, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
+    settle<MB, NBW>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
+}
+
+// ------------------------------------------------------------------- wide tile, M >= 128
+//
+// Once every 128-row block of A meets a weight tile, the product is bound by the matrix
+// cores, not by the weight stream (MARLIN paper sec. 3.2 and its Eq. (1): arithmetic
+// intensity grows with the batch).  The cost to keep under the MFMA time is the dequantisation:
+// 13 VALU ops (9 to decode, 4 to scale) per 8 weights of one B fragment.  That fragment feeds
+// one 16x16x32 MFMA per 16 rows the wave covers, so each wave takes all 128 rows of the tile
+// and 64 columns (8 x 4 accumulator tiles, 128 VGPRs): decode work is about 40% of the MFMA
+// time and overlaps it.  The weights of a 128-row K step are still one 1 KiB load per slab per
+// wave, straight into registers.
+//
+// A arrives by DMA: buffer loads that write LDS directly (no staging registers, no LDS store
+// instructions), into a ring of 32 KiB stages (128 rows x 128 k).  A DMA writes 64 consecutive
+// 16-byte LDS chunks, so the XOR swizzle of the ring is applied on the global side: the lane
+// that fills LDS position p of row r fetches chunk p ^ (r mod 16) of that row.
+//
+// Four waves side by side in N make a 128 x 256 workgroup tile; two workgroups share a CU
+// (2 x 64 KiB of LDS for a two-stage ring, at most 256 VGPRs per lane), so one workgroup's
+// barrier and load waits are covered by the other's MFMAs.  A and the weights are fetched one
+// tile ahead.  The kernel is written for any wave count and ring depth: an eight-wave,
+// 128 x 512, three-stage variant (loads two tiles ahead, half the A traffic per FLOP) measured
+// no faster, its extra weight buffers pushing the register allocator into spills.
+//
+// Measured (hardware counters, ablations): with the loads and the barrier removed the loop
+// keeps the matrix cores about 80% busy; the loads cost the rest.  Neither the LDS reads, the
+// dequantisation nor spreading the loads over the tile changes that.
+
+constexpr int kWideMB = 8;
+constexpr int kWideNBW = 4;
+
+// A stage is filled by 32 DMAs of 4 rows each; wave w issues DMAs ND * w .. ND * w + ND - 1
+// (ND = 32 / WAVES), DMA j filling stage rows 4j .. 4j + 3.  Lane l of DMA j fetches row
+// r = 4j + l / 16 of the tile, chunk c = (l mod 16) ^ (r mod 16).  Since ND is a multiple of 4,
+// r mod 16 = 4 (d mod 4) + l / 16 for the wave's d-th DMA: the lane-dependent part of the
+// offset, l / 16 rows plus 16 c bytes, takes four values (d mod 4); the rest, the tile's first
+// row, 4 (ND w + d) rows and the K step, is uniform.
+// This wave's DMAs for one A stage: `rowoff` is the byte offset of the wave's first row (tile
+// row + 4 ND w) plus the K step.  The four lane offsets are recomputed here from an opaque copy of the lane
+// index (a few VALU ops): kept live across the main loop instead, they are the first values
+// the register allocator spills, and every reload then waits for all outstanding loads.
+template <int WAVES>
+__device__ __forceinline__ void wide_dma_a(const Params &p, __amdgpu_buffer_rsrc_t rA, u4 *stage,
+                                           int wave, int lane_in, uint32_t rowoff)
+{
+    constexpr int ND = 32 / WAVES;
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    uint32_t lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = (lane & 15) ^ ((4 * j + (lane >> 4)) & 15);
+        lo[j] = (static_cast<uint32_t>(lane >> 4) * p.K + 8 * c) * 2;
+    }
+    const uint32_t row4 = static_cast<uint32_t>(p.K) * 8;         // 4 rows, in bytes
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void *)(stage + (ND * wave + d) * 64), 16,
+            lo[d & 3], __builtin_amdgcn_readfirstlane(rowoff + d * row4), 0, 0);
+}
+
+// 8 weights, decoded and scaled: fp16(s * (q - 8)), one rounding.
+__device__ __forceinline__ h8 dequant8_scaled(uint32_t w, h2 s, uint32_t mlo, uint32_t mhi,
+                                              uint32_t magic)
+{
+    const uint32_t w8 = w >> 8;
+    const uint32_t x0 = and_or(w, mlo, magic);
+    const uint32_t x1 = and_or(w, mhi, magic);
+    const uint32_t x2 = and_or(w8, mlo, magic);
+    const uint32_t x3 = and_or(w8, mhi, magic);
+    const h2 sub = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+    const h2 add = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+    const h2 y0 = (__builtin_bit_cast(h2, x0) - sub) * s;
+    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, add) * s;
+    const h2 y2 = (__builtin_bit_cast(h2, x2) - sub) * s;
+    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, add) * s;
+    h8 r;
+    r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
+    r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
+    return r;
+}
+
+// One 128-row K step of the wave's 128 x 64 output block.  Per 32-k MFMA step the four B
+// fragments are decoded first; then each A fragment (row block mb) is read from LDS once and
+// used by four MFMAs.
+__device__ __forceinline__ void wide_compute(const u4 *stage, int lane,
+                                             const u4 (&wq)[kWideNBW],
+                                             const uint32_t (&sc)[kWideNBW],
+                                             f4 (&acc)[kWideMB][kWideNBW], uint32_t mlo,
+                                             uint32_t mhi, uint32_t magic)
+{
+    const int sshift = (lane & 1) * 16;
+    h2 s2[kWideNBW];
+#pragma unroll
+    for (int b = 0; b < kWideNBW; ++b) {
+        const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sc[b] >> sshift));
+        s2[b] = h2{sh, sh};
+        asm volatile("" : "+v"(s2[b]));
+    }
+    const int row = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        h8 bw[kWideNBW];
+#pragma unroll
+        for (int b = 0; b < kWideNBW; ++b)
+            bw[b] = dequant8_scaled(wq[b][t], s2[b], mlo, mhi, magic);
+#pragma unroll
+        for (int mb = 0; mb < kWideMB; ++mb) {
+            const h8 a = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
+#pragma unroll
+            for (int b = 0; b < kWideNBW; ++b)
+                acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[b], acc[mb][b], 0, 0, 0);
+        }
+    }
+}
+
+// s_waitcnt immediate for "vmcnt(n)" alone (lgkmcnt and expcnt left at their maxima).
+constexpr int vmcnt_imm(int n)
+{
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+template <int WAVES, int STAGES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(Params p)
+{
+    using TL = Tile<kWideMB, kWideNBW, WAVES>;
+    constexpr int MB = kWideMB, NBW = kWideNBW;
+    constexpr int ND = 32 / WAVES;             // A DMAs per wave per tile
+    constexpr int NW = 2 * NBW;                // weight + scale loads per wave per tile
+    // The stages are separate arrays: with distinct objects the compiler can tell that the
+    // reads of one stage do not depend on a DMA into another (it waits for pending LDS DMA
+    // before any LDS read that may alias it).
+    __shared__ u4 st0[TL::kStageQuads];
+    __shared__ u4 st1[TL::kStageQuads];
+    __shared__ u4 st2[STAGES > 2 ? TL::kStageQuads : 1];
+    __shared__ int flag[2];
+    auto stage = [&](auto k) __attribute__((always_inline)) -> u4 * {
+        if constexpr (decltype(k)::value == 0) return st0;
+        else if constexpr (decltype(k)::value == 1) return st1;
+        else return st2;
+    };
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+
+    int stripe = blockIdx.x;
+    if ((p.W & 7) == 0)
+        stripe = (blockIdx.x & 7) * (p.W >> 3) + (blockIdx.x >> 3);
+    const long long t0 = stripe_begin(stripe, p.T, p.W);
+    const long long t1 = stripe_begin(stripe + 1, p.T, p.W);
+    if (t0 >= t1)
+        return;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
+    const __amdgpu_buffer_rsrc_t rS =
+        make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(p.partials, static_cast<uint32_t>(2u * p.W * TL::kSlotFloats * 4u));
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
+    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+
+    f4 acc[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+            acc[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
+
+    long long t = t0;
+    long long sigma = t0 / p.G;
+    int g = static_cast<int>(t0 - sigma * p.G);
+    long long nonown = -1, own = -1;
+
+    // Load position, clamped to the stripe's last tile so that every tile issues the same
+    // loads (the last tiles re-read their own data into idle buffers).  A branch around the
+    // loads would leave the compiler's waits at the join assuming no loads were issued,
+    // i.e. waiting for everything.
+    LoadCursor lc;
+    lc.g = g;
+    lc.s = static_cast<int>(sigma / p.P);
+    lc.pm = static_cast<int>(sigma - static_cast<long long>(lc.s) * p.P);
+    load_cursor_set<MB, NBW, WAVES>(p, wave, lc);
+    // byte offset of the wave's first A row at the load position's K step (uniform)
+    auto a_rowoff = [&]() __attribute__((always_inline)) {
+        return (static_cast<uint32_t>(lc.pm * TL::Mt + 4 * ND * wave) * p.K) * 2 + lc.a_soff;
+    };
+    long long lt = t0;
+
+    auto advance = [&]() __attribute__((always_inline)) {
+        if (lt + 1 < t1) {
+            ++lt;
+            ++lc.g;
+            ++lc.wblk;
+            lc.a_soff += kGroup * 2;
+            if (lc.g == p.G) {
+                lc.g = 0;
+                if (++lc.pm == p.P) {
+                    lc.pm = 0;
+                    ++lc.s;
+                }
+                load_cursor_set<MB, NBW, WAVES>(p, wave, lc);
+            }
+        }
+    };
+
+    // Weight buffers, one per stage: tile i uses stage and buffer i % STAGES.
+    u4 wq[STAGES][NBW];
+    uint32_t sc[STAGES][NBW];
+
+    // Issue the loads of the tile at the load position into stage / buffer k, the DMAs first
+    // (the asm and scheduling barriers keep that order), and move the cursor on.
+    auto issue = [&](auto k) __attribute__((always_inline)) {
+        constexpr int K = decltype(k)::value;
+        wide_dma_a<WAVES>(p, rA, stage(k), wave, lane, a_rowoff());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+            load_w_slab(rW, rS, p.G, lane, lc.wblk, b, wq[K][b], sc[K][b]);
+        advance();
+    };
+
+    auto end_of_tile = [&]() __attribute__((always_inline)) {
+        if (t + 1 == t1) {
+            ++t;
+            return;
+        }
+        if (g == p.G - 1) {
+            slice_end<MB, NBW, WAVES>(p, rP, rC, stripe, t0, t, sigma, wave, lane, acc, nonown,
+                                      own);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                    acc[mb][b] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+        ++t;
+        if (++g == p.G) {
+            g = 0;
+            ++sigma;
+        }
+    };
+
+    // Tile i (phase k = i % STAGES): wait until A(i) has landed, barrier, issue the loads of
+    // tile i + STAGES - 1 into the stage / buffer that tile i - 1 used, compute tile i.
+    // A(i) was issued STAGES - 1 tiles ago; every tile issues ND DMAs then NW weight loads,
+    // and the vector-memory counter completes in order, so A(i) has landed once at most
+    // NW + (STAGES - 2) * (ND + NW) operations are outstanding (stores issued since only make
+    // the wait stricter).  The barrier then makes A(i) visible to every wave, and the stage
+    // about to be refilled was last read by compute(i - 1), which every wave has finished
+    // before it reaches the barrier.
+    constexpr int kWaitA = NW + (STAGES - 2) * (ND + NW);
+    auto tile = [&](auto k) __attribute__((always_inline)) {
+        constexpr int K = decltype(k)::value;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitA));
+        __syncthreads();
+        issue(std::integral_constant<int, (K + STAGES - 1) % STAGES>{});
+        wide_compute(stage(k), lane, wq[K], sc[K], acc, mlo, mhi, magic);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        end_of_tile();
+    };
+
+    issue(std::integral_constant<int, 0>{});
+    if constexpr (STAGES > 2)
+        issue(std::integral_constant<int, 1>{});
+
+    // Whole rounds of STAGES tiles (phases 0 .. STAGES-1), then up to STAGES - 1 more.
+    while (t + STAGES - 1 < t1) {
+        tile(std::integral_constant<int, 0>{});
+        tile(std::integral_constant<int, 1>{});
+        if constexpr (STAGES > 2)
+            tile(std::integral_constant<int, 2>{});
+    }
+    if (t < t1)
+        tile(std::integral_constant<int, 0>{});
+    if constexpr (STAGES > 2)
+        if (t < t1)
+            tile(std::integral_constant<int, 1>{});
+    // The last tiles' re-read DMAs may still be writing LDS: let them land before the
+    // workgroup's LDS can be handed to another workgroup.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    slice_end<MB, NBW, WAVES>(p, rP, rC, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
+    settle<MB, NBW, WAVES>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
 }
 
 // ------------------------------------------------------------------------------- host side
@@ -638,6 +1072,7 @@ int current_device(DeviceInfo *out)
 
 struct Config {
     int MB, NBW;     // M sub-tiles of 16 rows; 16-column slabs per wave
+    int waves;       // waves per workgroup
     int P, S, G, W;
     long long T;
 };
@@ -648,20 +1083,20 @@ int check_gemm_shape(int M, int K, int N)
         return W4A16_EINVAL;
     if (K == 0 || K % kGroup || N == 0 || N % W4A16_N_ALIGN)
         return W4A16_ESHAPE;
-    // Buffer resources address at most 4 GiB; A offsets run up to 64 rows past M.
+    // Buffer resources address at most 4 GiB; A and C offsets run up to 128 rows past M.
     const uint64_t lim = uint64_t(1) << 32;
-    if ((static_cast<uint64_t>(M) + 64) * static_cast<uint64_t>(K) * 2 >= lim ||
+    if ((static_cast<uint64_t>(M) + 128) * static_cast<uint64_t>(K) * 2 >= lim ||
+        (static_cast<uint64_t>(M) + 128) * static_cast<uint64_t>(N) * 2 >= lim ||
         static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= lim)
         return W4A16_ESHAPE;
     return W4A16_OK;
 }
 
 // Number of stripes: a whole number of workgroups per CU, so every CU streams the same
-// amount (a fractional count leaves some CUs with one workgroup more than others).  Two per
-// CU measured best for every tile size.
-int choose_stripes(long long T, int cus)
+// amount (a fractional count leaves some CUs with one workgroup more than others).
+int choose_stripes(long long T, int cus, int per_cu)
 {
-    long long w = static_cast<long long>(cus) * 2;
+    long long w = static_cast<long long>(cus) * per_cu;
     if (w > kMaxWGs)
         w = kMaxWGs;
     if (w > T)
@@ -673,25 +1108,39 @@ Config choose_config(int M, int K, int N, int cus)
 {
     Config c{};
     c.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    c.waves = kWaves;
+    c.G = K / kGroup;
+    const int per_cu = 2;                        // two workgroups per CU measured best
+    if (M > 64 && N % (16 * kWideNBW * kWaves) == 0) {
+        // Wide tiles (all rows of a 128-row block per wave) unless the output has so few of
+        // them that each would be split between more than four stripes: the split pieces are
+        // then summed serially by one workgroup, and 64-row tiles (twice as many, half the
+        // partial size) measure faster.
+        const long long tiles = static_cast<long long>(N / (16 * kWideNBW * kWaves)) *
+                                ((M + 16 * kWideMB - 1) / (16 * kWideMB));
+        const long long stripes = std::min<long long>(static_cast<long long>(cus) * per_cu,
+                                                      tiles * c.G);
+        if (4 * tiles >= stripes)
+            c.MB = kWideMB;
+    }
     const int Mt = 16 * c.MB;
     c.P = (M + Mt - 1) / Mt;
-    c.G = K / kGroup;
     // widest slice (4 slabs per wave) that divides N
     c.NBW = 1;
     for (int nbw = 4; nbw >= 1; nbw >>= 1)
-        if (N % (16 * kWaves * nbw) == 0) {
+        if (N % (16 * c.waves * nbw) == 0) {
             c.NBW = nbw;
             break;
         }
-    c.S = N / (16 * kWaves * c.NBW);
+    c.S = N / (16 * c.waves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
-    c.W = choose_stripes(c.T, cus);
+    c.W = choose_stripes(c.T, cus, per_cu);
     return c;
 }
 
 size_t workspace_for(const Config &c)
 {
-    const size_t slot = static_cast<size_t>(16 * c.MB) * (16 * kWaves * c.NBW) * sizeof(float);
+    const size_t slot = static_cast<size_t>(16 * c.MB) * (16 * c.waves * c.NBW) * sizeof(float);
     return kCounterBytes + 2 * static_cast<size_t>(c.W) * slot;
 }
 
@@ -699,6 +1148,14 @@ template <int MB, int NBW>
 hipError_t launch(const Params &p, hipStream_t stream)
 {
     hipLaunchKernelGGL((w4a16_gemm_kernel<MB, NBW>), dim3(p.W), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int WAVES, int STAGES>
+hipError_t launch_wide(const Params &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((w4a16_gemm_wide_kernel<WAVES, STAGES>), dim3(p.W), dim3(64 * WAVES), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -762,6 +1219,7 @@ extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t 
     case 41: e = launch<4, 1>(p, s); break;
     case 42: e = launch<4, 2>(p, s); break;
     case 44: e = launch<4, 4>(p, s); break;
+    case kWideMB * 10 + kWideNBW: e = launch_wide<kWaves, 2>(p, s); break;
     default: return W4A16_EHIP;
     }
     return e == hipSuccess ? W4A16_OK : W4A16_EHIP;

@@ -123,6 +123,32 @@ def test_long_stripes_many_contributors_fresh_workspaces(M, K, N):
         assert int(ws[:4096].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("M,K,N", [(128, 4096, 768), (300, 2048, 1280), (129, 1024, 256),
+                                   (256, 4096, 1536), (513, 1024, 2048)])
+def test_wide_tiles_both_shapes_ragged_rows(M, K, N):
+    # M > 64 takes the 128-row tiles: 512-column slices where N allows (N = 1536, 2048),
+    # else 256-column slices (N = 768, 1280, 256); M = 129, 300, 513 leave ragged row blocks.
+    A, q, s = draw(K, N, M, seed=M * 7 + N)
+    check(gpu_gemm(A, q, s), oracle.gemm(A, q, s), f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 18432, 512), (200, 18432, 768), (96, 9216, 256)])
+def test_one_slice_split_over_many_stripes(M, K, N):
+    # Very few output tiles over a long K: slices are shared by dozens of one- or two-tile
+    # stripes that all finish together, so the slice's owner is sometimes the last to arrive
+    # (and sums from its registers) and sometimes not (and stores its piece like the others).
+    # Whoever sums, the order is fixed: repeated runs must agree bit for bit.
+    A, q, s = draw(K, N, M, seed=M + N)
+    W = Weights(q, s)
+    ref = oracle.gemm(A, q, s)
+    first = W.run(A)
+    check(first, ref, f"M={M} K={K} N={N}")
+    for rep in range(4):
+        ws = w4.new_workspace(M, K, N)
+        assert np.array_equal(bits(W.run(A, ws=ws)), bits(first)), rep
+        assert int(ws[:4096].count_nonzero()) == 0
+
+
 def test_m1_equals_gemv():
     A, q, s = draw(4096, 1024, 1, seed=21)
     check(gpu_gemm(A, q, s)[0], oracle.gemv(A[0], q, s), "M=1 vs gemv")
