@@ -7,6 +7,11 @@ bytes per call: D = 2MK (A) + KN/2 (codes) + KN/64 (scales) + 2MN (C); flops F =
 Roofline per call: T_bound = max(D / 8 TB/s, F / 2.5 PFLOP/s); fp16-weight byte bound
 D16 = 2MK + 2KN + 2MN (the MARLIN paper's uncompressed reference point).
 
+`roofline` covers the dominant kernel: the 16-row tile kernel that serves M = 1..16, five of
+the eight calls and about half the sweep's time; HBM-bound, so achieved = its algorithmic
+bytes per launch / its mean launch time.  `roofline_by_kernel` gives the same for every kernel
+of the sweep, the 128-row (M = 128) kernel against the fp16 MFMA peak.
+
 Prints one JSON line on stdout.  Single GPU only.
 """
 from __future__ import annotations
@@ -28,6 +33,16 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix
 GROUP = 128
 CALIB_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
+
+# The kernel each M of the sweep runs (the library picks it from M: 16-row tiles up to
+# M = 16, 32-row up to 32, 64-row up to 64, then 128-row tiles on this shape), and the roof
+# that bounds it.
+KERNELS = [
+    ("w4a16_gemm_kernel<1,4> (16-row tiles)", (1, 2, 4, 8, 16), "hbm"),
+    ("w4a16_gemm_kernel<2,4> (32-row tiles)", (32,), "hbm"),
+    ("w4a16_gemm_kernel<4,4> (64-row tiles)", (64,), "hbm"),
+    ("w4a16_gemm_wide_kernel<4,2> (128-row tiles)", (128,), "mfma"),
+]
 KERNEL_SOURCE = os.path.join(ROOT, "mixed_precision_w4a16_amd", "csrc", "gemm.hip")
 
 
@@ -154,7 +169,7 @@ def main():
         torch.cuda.synchronize()
 
     sweep = []
-    tot_bytes = tot_us = 0.0
+    tot_bytes = 0.0
     for M in Ms:
         us = float(np.mean([a.elapsed_time(b) for a, b in ev[M]])) * 1e3
         D, D16, F = algorithmic_bytes(M, K, N), fp16_weight_bytes(M, K, N), flops(M, K, N)
@@ -170,22 +185,35 @@ def main():
             "speedup_vs_fp16_weight_bound": round(D16 / (HBM_PEAK_GBPS * 1e3) / us, 3),
         })
         tot_bytes += D
-        tot_us += us
         log(f"M={M:4d}  {us:8.1f} us  {gbps:7.0f} GB/s ({gbps / HBM_PEAK_GBPS:5.1%} HBM)  "
             f"{F / us / 1e6:7.1f} TFLOP/s  roofline {t_bound / us:5.1%}  "
             f"vs fp16 bound {D16 / (HBM_PEAK_GBPS * 1e3) / us:4.2f}x")
 
     ms_per_step = wall / args.steps * 1e3
     value = tot_bytes * args.steps / wall / 1e9
-    achieved = tot_bytes / tot_us / 1e3          # GB/s, from the per-launch event durations
     traffic = measured_traffic()
-    traffic_bytes = None
     if traffic is not None:
-        per_m = traffic["per_M"]
-        traffic_bytes = float(np.mean([per_m[str(M)]["hbm_bytes"] for M in Ms]))
         for row in sweep:
-            row["hbm_bytes_measured"] = per_m[str(row["M"])]["hbm_bytes"]
+            row["hbm_bytes_measured"] = traffic["per_M"][str(row["M"])]["hbm_bytes"]
+    by_M = {row["M"]: row for row in sweep}
 
+    def roof(name, ms, bound):
+        ms = [m for m in ms if m in by_M]
+        us = float(np.mean([by_M[m]["us"] for m in ms]))
+        if bound == "hbm":
+            a = float(np.mean([algorithmic_bytes(m, K, N) for m in ms])) / us / 1e3
+            peak, unit = HBM_PEAK_GBPS, "GB/s"
+        else:
+            a = float(np.mean([flops(m, K, N) for m in ms])) / us / 1e6
+            peak, unit = MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
+        tb = None
+        if traffic is not None:
+            tb = float(np.mean([traffic["per_M"][str(m)]["hbm_bytes"] for m in ms]))
+        return {"bound": bound, "achieved": round(a, 1), "peak": peak, "unit": unit,
+                "frac": round(a / peak, 4), "traffic": tb, "kernel": name, "M": ms,
+                "mean_launch_us": round(us, 2)}
+
+    kernels = [roof(*k) for k in KERNELS]
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -194,10 +222,8 @@ def main():
         "config": {"workload": LARGE.name, "K": K, "N": N, "M": list(Ms), "group": GROUP,
                    "weights": "int4 codes + fp16 scales (4.125 bits/weight)",
                    "weight_copies_rotated": args.copies},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_bytes,
-                     "kernel": "w4a16_gemm_kernel (all M of the sweep; mean bytes / mean time)"},
+        "roofline": kernels[0],
+        "roofline_by_kernel": kernels,
         "sweep": sweep,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},

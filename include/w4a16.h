@@ -114,7 +114,8 @@ int w4a16_workspace_size(int M, int K, int N, size_t *bytes);
  * run to run.
  *
  * Alignment: A, packed and scales must be 16-byte aligned (any hipMalloc pointer is).
- * Limits: (M + 128) * K * 2 and K * N / 2 must each be below 2^32 bytes.
+ * Limits: (M + 128) * K * 2, (M + 128) * N * 2 and K * N / 2 must each be below 2^32 bytes
+ * (the kernels address A, C and the packed weights through 32-bit buffer offsets).
  *
  * M == 0 is a no-op returning W4A16_OK.  Errors: W4A16_EINVAL (null pointer, negative
  * size), W4A16_ESHAPE (K not a positive multiple of 128, N not a positive multiple of 64,

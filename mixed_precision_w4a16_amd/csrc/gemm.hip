@@ -19,11 +19,12 @@
 //   0x6400 gives 1024 + q (low nibbles) or 1024 + 16q (high nibbles), and one packed fp16
 //   add or FMA per pair returns q - 8 exactly.  Deep-dive page "Marlin 完全拆解", section
 //   "INT4 只是存储类型，不是这条路径的计算类型".
-// * Scales.  The MFMA sums A * (q - 8) over one 128-row group in fp32 (exact products);
-//   that partial is multiplied by the group's scale and added to the running fp32 sum.
-//   This is the grouped sum C = sum_g s_g sum_{k in g} A (q - 8) written out on the deep-dive
-//   page (section "scale 为什么有时在内环乘，有时在末尾乘"); it costs 4 FMAs per 16x16
-//   output tile per group instead of one fp16 multiply per weight.
+// * Scales.  With 16- and 32-row tiles the MFMA sums A * (q - 8) over one 128-row group in
+//   fp32 (exact products) and that partial is multiplied by the group's scale and added to
+//   the running fp32 sum: the grouped sum C = sum_g s_g sum_{k in g} A (q - 8) written out on
+//   the deep-dive page (section "scale 为什么有时在内环乘，有时在末尾乘"), 4 FMAs per 16x16 output
+//   tile per group.  With 64 or more rows a decoded fragment feeds enough MFMAs that scaling
+//   the weights in fp16 (the pages' own order) is cheaper.
 // * Contraction: v_mfma_f32_16x16x32_f16, tokens as the 16 rows, output columns as the 16
 //   columns; k-step loop outermost so independent accumulators separate dependent MFMAs
 //   (MARLIN paper sec. 3.2 "Tensor Core Level").
@@ -36,16 +37,19 @@
 //   page, striped partitioning.  Workgroup ids are remapped so consecutive stripes sit on
 //   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs).
 // * Cross-workgroup reduction.  Only the first and last slice of a stripe can be shared
-//   with a neighbouring stripe.  At such a slice's end the workgroup writes its fp32 partial
-//   tile to its own workspace slot with device-scope stores and streams on without
-//   waiting.  After its last tile it waits once for its stores and bumps each shared
-//   slice's counter; the contributor that draws the last count reads the partials back
-//   with device-scope loads, adds them in stripe order (a fixed order, so results are
-//   bitwise repeatable), writes C and resets the counter.  No cache-wide writeback or
-//   invalidate is issued, and no workgroup ever waits for another.  The pages sum such partials serially with locks and stage them
-//   in fp16 in the output (deep-dive page section "为什么归约串行，却不一定慢"); fp32
-//   partials and a last-arriver sum keep the same "no big temporary" property, keep full
-//   precision, and never spin, so no co-residency assumption is needed.
+//   with a neighbouring stripe.  A stripe that entered a slice part-way writes its fp32 piece
+//   to its own workspace slot with device-scope stores and streams on without waiting; the
+//   stripe holding the slice's first tiles (its owner, usually the last to finish it) keeps
+//   its piece in registers.  After its last tile each stripe counts in once per shared slice;
+//   exactly one contributor -- the owner if it arrives last -- sums the pieces in stripe order
+//   (a fixed order, so results are bitwise repeatable), writes C and resets the counter.  No
+//   cache-wide writeback or invalidate is issued, and no workgroup ever waits for another.
+//   The pages sum such partials serially with locks and stage them in fp16 in the output
+//   (deep-dive page section "为什么归约串行，却不一定慢"); fp32 partials and a last-arriver sum
+//   keep the same "no big temporary" property, keep full precision, and never spin, so no
+//   co-residency assumption is needed.
+// * M > 64 runs a second kernel with 128-row tiles (w4a16_gemm_wide_kernel, further down):
+//   every weight tile meets a whole 128-row block of A, A is brought into LDS by DMA.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>

@@ -142,6 +142,7 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
     # size limits of the 32-bit buffer ranges
     assert lib.w4a16_gemm(d, d, d, d, 2 ** 20, 4096, 1024, d, None) == w4.ESHAPE
     assert lib.w4a16_gemm(d, d, d, d, 16, 2 ** 20, 2 ** 14, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm(d, d, d, d, 2 ** 15, 128, 2 ** 16, d, None) == w4.ESHAPE   # C >= 4 GiB
     n = ctypes.c_size_t(7)
     assert lib.w4a16_workspace_size(16, 1000, 1024, ctypes.byref(n)) == w4.ESHAPE
     assert lib.w4a16_workspace_size(16, 1024, 1024, None) == w4.EINVAL
