@@ -210,16 +210,17 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
         stage[(16 * mb + r) * 16 + (c ^ r)] = ar[mb];
 }
 
-// This wave's packed weight quads (1 KiB contiguous per slab) and scales.  With 16-row
-// tiles every weight byte is used once, so it is streamed non-temporally (evict first, the
-// pages' evict_first hint).  Larger tiles re-read a slice's weights for the next 64-row
-// sub-problem right away, and measure faster with the weights left in the cache.
+// This wave's packed weight quads (1 KiB contiguous per slab) and scales.  With 16- and
+// 32-row tiles every weight byte is used once (M <= 32 is one row sub-problem), so it is
+// streamed non-temporally (evict first, the pages' evict_first hint) and A stays in the L2.
+// 64-row tiles can run several row sub-problems that re-read a slice's weights right away,
+// and measure faster with the weights left in the cache.
 template <int MB, int NBW>
 __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
                                        int G, int lane, uint32_t wblk, u4 (&wq)[NBW],
                                        uint32_t (&sc)[NBW])
 {
-    constexpr int policy = MB == 1 ? kNonTemporal : 0;
+    constexpr int policy = MB <= 2 ? kNonTemporal : 0;
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
