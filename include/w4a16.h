@@ -69,7 +69,10 @@ const char *w4a16_status_string(int status);
  *   other down K.  Word 4*l + t of a block (l = 0..63, t = 0..3) holds the 8 codes of
  *   column 16j + (l mod 16), rows 128g + 32t + 8*(l div 16) + i for i = 0..7, code i in
  *   nibble p(i) (bits 4p..4p+3) with p = {0, 4, 1, 5, 2, 6, 3, 7}.
- *   scales_out[(j*(K/128) + g)*16 + c] = scales[g][16j + c], c = 0..15.
+ *   Scales are grouped by Q consecutive slabs, Q = 4 if N is a multiple of 256, else 2 if N
+ *   is a multiple of 128, else 1 (the slabs one wave of w4a16_gemm works on):
+ *   scales_out[(((j div Q)*(K/128) + g)*16 + c)*Q + (j mod Q)] = scales[g][16j + c],
+ *   c = 0..15, so the Q scales of one column at one group are adjacent.
  *
  * Returns W4A16_OK, W4A16_EINVAL (null pointer, negative size, a code > 15) or
  * W4A16_ESHAPE (group != 128, K not a positive multiple of 128, N not a positive multiple

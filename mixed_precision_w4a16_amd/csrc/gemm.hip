@@ -119,6 +119,28 @@ __device__ __forceinline__ h8 dequant8(uint32_t w, uint32_t mlo, uint32_t mhi, u
     return r;
 }
 
+// 8 weights, decoded and scaled: fp16(s * (q - 8)), one rounding.
+__device__ __forceinline__ h8 dequant8_scaled(uint32_t w, h2 s, uint32_t mlo, uint32_t mhi,
+                                              uint32_t magic)
+{
+    const uint32_t w8 = w >> 8;
+    const uint32_t x0 = and_or(w, mlo, magic);
+    const uint32_t x1 = and_or(w, mhi, magic);
+    const uint32_t x2 = and_or(w8, mlo, magic);
+    const uint32_t x3 = and_or(w8, mhi, magic);
+    const h2 sub = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+    const h2 add = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+    const h2 y0 = (__builtin_bit_cast(h2, x0) - sub) * s;
+    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, add) * s;
+    const h2 y2 = (__builtin_bit_cast(h2, x2) - sub) * s;
+    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, add) * s;
+    h8 r;
+    r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
+    r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
+    return r;
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t b)
 {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
@@ -164,6 +186,7 @@ constexpr int kDeviceScope = 16;   // cache policy sc1: write through / read pas
 struct LoadCursor {
     int g, pm, s;
     uint32_t wblk;      // block index of this wave's first slab at K step g (uniform)
+    uint32_t sblk;      // index of this wave's scale group at K step g (uniform)
     uint32_t a_soff;    // byte offset of K step g in an A row (uniform)
 };
 
@@ -171,6 +194,7 @@ template <int MB, int NBW, int WAVES = kWaves>
 __device__ __forceinline__ void load_cursor_set(const Params &p, int wave, LoadCursor &c)
 {
     c.wblk = (static_cast<uint32_t>(c.s) * (WAVES * NBW) + wave * NBW) * p.G + c.g;
+    c.sblk = (static_cast<uint32_t>(c.s) * WAVES + wave) * p.G + c.g;
     c.a_soff = static_cast<uint32_t>(c.g) * (kGroup * 2);
 }
 
@@ -210,6 +234,42 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
         stage[(16 * mb + r) * 16 + (c ^ r)] = ar[mb];
 }
 
+// Scales of a wave's NBW slabs at one K step: w4a16_pack stores the NBW scales of a column
+// side by side (NBW = 4 / 2: 8 / 4 bytes per column), so one load per lane brings all of them;
+// with NBW = 1 a lane loads the aligned dword holding its column's scale and its neighbour's.
+// (A 16-bit load result would be re-copied across the loop back-edge.)
+template <int NBW>
+struct ScaleRegs {
+    static constexpr int n = NBW >= 2 ? NBW / 2 : 1;
+};
+
+template <int NBW>
+__device__ __forceinline__ void load_scales(__amdgpu_buffer_rsrc_t rS, int lane, uint32_t sblk,
+                                            uint32_t (&sc)[ScaleRegs<NBW>::n])
+{
+    const uint32_t so = __builtin_amdgcn_readfirstlane(sblk * (32u * (NBW >= 2 ? NBW : 1)));
+    if constexpr (NBW == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, (lane & 15) * 8, so, 0);
+        sc[0] = v[0];
+        sc[1] = v[1];
+    } else if constexpr (NBW == 2) {
+        sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 15) * 4, so, 0);
+    } else {
+        sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, so, 0);
+    }
+}
+
+// fp16 bits of slab b's scale for this lane's column.
+template <int NBW>
+__device__ __forceinline__ uint16_t scale_bits(const uint32_t (&sc)[ScaleRegs<NBW>::n], int b,
+                                               int lane)
+{
+    if constexpr (NBW >= 2)
+        return static_cast<uint16_t>(sc[b >> 1] >> ((b & 1) * 16));
+    else
+        return static_cast<uint16_t>(sc[0] >> ((lane & 1) * 16));
+}
+
 // This wave's packed weight quads (1 KiB contiguous per slab) and scales.  With 16- and
 // 32-row tiles every weight byte is used once (M <= 32 is one row sub-problem), so it is
 // streamed non-temporally (evict first, the pages' evict_first hint) and A stays in the L2.
@@ -217,8 +277,8 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
 // and measure faster with the weights left in the cache.
 template <int MB, int NBW>
 __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
-                                       int G, int lane, uint32_t wblk, u4 (&wq)[NBW],
-                                       uint32_t (&sc)[NBW])
+                                       int G, int lane, uint32_t wblk, uint32_t sblk,
+                                       u4 (&wq)[NBW], uint32_t (&sc)[ScaleRegs<NBW>::n])
 {
     constexpr int policy = MB <= 2 ? kNonTemporal : 0;
 #pragma unroll
@@ -226,20 +286,8 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
         const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
         wq[b] = __builtin_bit_cast(
             u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, policy));
-        // the aligned dword holding this column's scale and its neighbour's (a 16-bit load
-        // result would be re-copied across the loop back-edge)
-        sc[b] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, blk * 32u, 0);
     }
-}
-
-// One slab of load_w (used by the wide kernel, which spreads its loads over the tile).
-__device__ __forceinline__ void load_w_slab(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
-                                            int G, int lane, uint32_t wblk, int b, u4 &wq,
-                                            uint32_t &sc)
-{
-    const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
-    wq = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, 0));
-    sc = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, blk * 32u, 0);
+    load_scales<NBW>(rS, lane, sblk, sc);
 }
 
 // Where the group scale is applied.  Small tiles (MB <= 2) keep (q - 8) exact: the MFMA
@@ -256,22 +304,22 @@ struct ScaleMode {
 
 template <int MB, int NBW>
 __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4 (&wq)[NBW],
-                                             const uint32_t (&sc)[NBW], f4 (&acc)[MB][NBW],
-                                             uint32_t mlo, uint32_t mhi, uint32_t magic)
+                                             const uint32_t (&sc)[ScaleRegs<NBW>::n],
+                                             f4 (&acc)[MB][NBW], uint32_t mlo, uint32_t mhi,
+                                             uint32_t magic)
 {
     // Scales first: converting them here ends the loaded registers' live range before the
     // next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
-    const int sshift = (lane & 1) * 16;               // odd columns: high half of the dword
     float sf[NBW];
-    h8 s8[NBW];
+    h2 s2[NBW];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         if constexpr (ScaleMode<MB>::kWeights) {
-            const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sc[b] >> sshift));
-            s8[b] = h8{sh, sh, sh, sh, sh, sh, sh, sh};
-            asm volatile("" : "+v"(s8[b]));
+            const _Float16 sh = __builtin_bit_cast(_Float16, scale_bits<NBW>(sc, b, lane));
+            s2[b] = h2{sh, sh};
+            asm volatile("" : "+v"(s2[b]));
         } else {
-            sf[b] = half_bits_to_float(static_cast<uint16_t>(sc[b] >> sshift));
+            sf[b] = half_bits_to_float(scale_bits<NBW>(sc, b, lane));
             asm volatile("" : "+v"(sf[b]));
         }
     }
@@ -289,7 +337,7 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
-                const h8 bw = dequant8(wq[b][t], mlo, mhi, magic) * s8[b];
+                const h8 bw = dequant8_scaled(wq[b][t], s2[b], mlo, mhi, magic);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bw, acc[mb][b],
@@ -653,6 +701,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
             ++lt;
             ++lc.g;
             ++lc.wblk;
+            ++lc.sblk;
             lc.a_soff += kGroup * 2;
             if (lc.g == p.G) {         // next slice (uniform, rare)
                 lc.g = 0;
@@ -678,16 +727,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     // is not needed yet: each weight tile has one whole tile of compute to arrive in.
     u4 ar[MB];
     u4 wq0[NBW], wq1[NBW];
-    uint32_t sc0[NBW], sc1[NBW];
+    uint32_t sc0[ScaleRegs<NBW>::n], sc1[ScaleRegs<NBW>::n];
     int st_cp = 0, st_st = 1;             // ring stages being computed from / stored to
     auto next_stage = [](int x) { return x == TL::kStages - 1 ? 0 : x + 1; };
 
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0)
-    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);        // W(t0)
+    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq0, sc0);        // W(t0)
     store_a<MB>(lds, tid, ar);                                // stage 0
     step_load();
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0+1)
-    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);        // W(t0+1)
+    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq1, sc1);        // W(t0+1)
     step_load();                                              // lc -> t0+2
 
     // End of a tile: at a slice's end, hand the accumulators to slice_end.  The stripe's last
@@ -725,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
-        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq0, sc0);    // W(t+2)
+        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq0, sc0);    // W(t+2)
         step_load();
         st_cp = st_st;
         st_st = next_stage(st_st);
@@ -737,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
-        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, wq1, sc1);    // W(t+2)
+        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq1, sc1);    // W(t+2)
         step_load();
         st_cp = st_st;
         st_st = next_stage(st_st);
@@ -812,42 +861,19 @@ __device__ __forceinline__ void wide_dma_a(const Params &p, __amdgpu_buffer_rsrc
             lo[d & 3], __builtin_amdgcn_readfirstlane(rowoff + d * row4), 0, 0);
 }
 
-// 8 weights, decoded and scaled: fp16(s * (q - 8)), one rounding.
-__device__ __forceinline__ h8 dequant8_scaled(uint32_t w, h2 s, uint32_t mlo, uint32_t mhi,
-                                              uint32_t magic)
-{
-    const uint32_t w8 = w >> 8;
-    const uint32_t x0 = and_or(w, mlo, magic);
-    const uint32_t x1 = and_or(w, mhi, magic);
-    const uint32_t x2 = and_or(w8, mlo, magic);
-    const uint32_t x3 = and_or(w8, mhi, magic);
-    const h2 sub = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-    const h2 add = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
-    const h2 y0 = (__builtin_bit_cast(h2, x0) - sub) * s;
-    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, add) * s;
-    const h2 y2 = (__builtin_bit_cast(h2, x2) - sub) * s;
-    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, add) * s;
-    h8 r;
-    r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
-    r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
-    return r;
-}
-
 // One 128-row K step of the wave's 128 x 64 output block.  Per 32-k MFMA step the four B
 // fragments are decoded first; then each A fragment (row block mb) is read from LDS once and
 // used by four MFMAs.
 __device__ __forceinline__ void wide_compute(const u4 *stage, int lane,
                                              const u4 (&wq)[kWideNBW],
-                                             const uint32_t (&sc)[kWideNBW],
+                                             const uint32_t (&sc)[ScaleRegs<kWideNBW>::n],
                                              f4 (&acc)[kWideMB][kWideNBW], uint32_t mlo,
                                              uint32_t mhi, uint32_t magic)
 {
-    const int sshift = (lane & 1) * 16;
     h2 s2[kWideNBW];
 #pragma unroll
     for (int b = 0; b < kWideNBW; ++b) {
-        const _Float16 sh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sc[b] >> sshift));
+        const _Float16 sh = __builtin_bit_cast(_Float16, scale_bits<kWideNBW>(sc, b, lane));
         s2[b] = h2{sh, sh};
         asm volatile("" : "+v"(s2[b]));
     }
@@ -880,7 +906,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
     using TL = Tile<kWideMB, kWideNBW, WAVES>;
     constexpr int MB = kWideMB, NBW = kWideNBW;
     constexpr int ND = 32 / WAVES;             // A DMAs per wave per tile
-    constexpr int NW = 2 * NBW;                // weight + scale loads per wave per tile
+    constexpr int NW = NBW + 1;                // weight + scale loads per wave per tile
     // The stages are separate arrays: with distinct objects the compiler can tell that the
     // reads of one stage do not depend on a DMA into another (it waits for pending LDS DMA
     // before any LDS read that may alias it).
@@ -950,6 +976,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
             ++lt;
             ++lc.g;
             ++lc.wblk;
+            ++lc.sblk;
             lc.a_soff += kGroup * 2;
             if (lc.g == p.G) {
                 lc.g = 0;
@@ -964,7 +991,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
     // Weight buffers, one per stage: tile i uses stage and buffer i % STAGES.
     u4 wq[STAGES][NBW];
-    uint32_t sc[STAGES][NBW];
+    uint32_t sc[STAGES][ScaleRegs<NBW>::n];
 
     // Issue the loads of the tile at the load position into stage / buffer k, the DMAs first
     // (the asm and scheduling barriers keep that order), and move the cursor on.
@@ -973,9 +1000,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
         wide_dma_a<WAVES>(p, rA, stage(k), wave, lane, a_rowoff());
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < NBW; ++b)
-            load_w_slab(rW, rS, p.G, lane, lc.wblk, b, wq[K][b], sc[K][b]);
+        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq[K], sc[K]);
         advance();
     };
 

@@ -15,7 +15,10 @@
 //   (k4,k5), (k6,k7) of the MFMA B operand.
 //
 // Blocks of a 16-column slab are consecutive down K, so a workgroup walking down K streams
-// contiguous memory.  Scales follow the same block order, 16 per block.
+// contiguous memory.  Scales are grouped for the same walk: a wave works on Q consecutive
+// slabs (Q = 4, 2 or 1: the widest that divides N / 64, as the kernel chooses), and the Q
+// scales of one column of those slabs at one group are adjacent, so one 2Q-byte load per
+// lane brings all the scales a wave needs for a K step.
 #include "w4a16.h"
 
 #include <cstddef>
@@ -24,6 +27,19 @@
 namespace {
 
 constexpr int kNibble[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+// Slabs per scale group: the widest of 4, 2, 1 such that N is a multiple of 64 * Q (N a
+// multiple of 16 only: 1).
+size_t slabs_per_scale_group(size_t N)
+{
+    return N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1);
+}
+
+// Position in scales_out of scale (g, column 16j + c).
+size_t scale_index(size_t j, size_t g, size_t c, size_t G, size_t Q)
+{
+    return (((j / Q) * G + g) * 16 + c) * Q + j % Q;
+}
 
 int check_shape(const void *a, const void *b, const void *c, const void *d, int K, int N,
                 int group)
@@ -50,6 +66,7 @@ extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, i
 
     const size_t G = nk / W4A16_GROUP;
     const size_t slabs = nn / 16;
+    const size_t Q = slabs_per_scale_group(nn);
     for (size_t j = 0; j < slabs; ++j) {
         for (size_t g = 0; g < G; ++g) {
             uint32_t *blk = packed_out + (j * G + g) * 256;
@@ -63,9 +80,8 @@ extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, i
                     blk[4 * l + t] = w;
                 }
             }
-            uint16_t *sb = scales_out + (j * G + g) * 16;
-            for (int c = 0; c < 16; ++c)
-                sb[c] = scales[g * nn + j * 16 + c];
+            for (size_t c = 0; c < 16; ++c)
+                scales_out[scale_index(j, g, c, G, Q)] = scales[g * nn + j * 16 + c];
         }
     }
     return W4A16_OK;
@@ -80,6 +96,7 @@ extern "C" int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packe
     const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
     const size_t G = nk / W4A16_GROUP;
     const size_t slabs = nn / 16;
+    const size_t Q = slabs_per_scale_group(nn);
     for (size_t j = 0; j < slabs; ++j) {
         for (size_t g = 0; g < G; ++g) {
             const uint32_t *blk = packed + (j * G + g) * 256;
@@ -93,9 +110,8 @@ extern "C" int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packe
                             static_cast<uint8_t>((w >> (4 * kNibble[i])) & 0xF);
                 }
             }
-            const uint16_t *sb = scales_packed + (j * G + g) * 16;
-            for (int c = 0; c < 16; ++c)
-                scales_out[g * nn + j * 16 + c] = sb[c];
+            for (size_t c = 0; c < 16; ++c)
+                scales_out[g * nn + j * 16 + c] = scales_packed[scale_index(j, g, c, G, Q)];
         }
     }
     return W4A16_OK;

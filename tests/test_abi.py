@@ -51,11 +51,14 @@ def layout_reference(codes, scales):
             for j in range(N // 16):
                 n = 16 * j + (l % 16)
                 packed[j, :, :, t] |= codes[k, n[None, :]].astype(np.uint32) << np.uint32(4 * NIBBLE[i])
-    sp = scales.reshape(G, N // 16, 16).transpose(1, 0, 2).reshape(-1)
+    Q = 4 if N % 256 == 0 else (2 if N % 128 == 0 else 1)
+    # [g][slab group u][slab b in group][c] -> [u][g][c][b]
+    sp = scales.reshape(G, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2).reshape(-1)
     return packed.reshape(-1), sp
 
 
-@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (384, 48), (1024, 1024)])
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (384, 48), (1024, 1024), (256, 384),
+                                 (128, 128), (256, 320)])
 def test_pack_matches_documented_layout(K, N):
     _, q, s = draw(K, N, 1, seed=K + N)
     packed, sp = w4.pack(q, s)
