@@ -13,7 +13,9 @@ Two independent implementations live here:
   fp16 by its own routine.  It is slow and only for tiny shapes; it pins the C code.
 
 The operation (MARLIN paper, arXiv 2408.11743, sec. 3.4 "Kernel Design"; deep-dive page,
-section "Marlin 要解决的精确问题"):  C = A * Bhat,  Bhat[k, n] = s[k // group, n] * (q[k, n] - 8).
+section "Marlin 要解决的精确问题"):  C = A * Bhat,  Bhat[k, n] = s[k // group, n] * (q[k, n] - z),
+z = 8 (symmetric) or a zero-point code z[k // group, n] in 0..15 (the page's general affine
+form s_{g,n}(q_{k,n} - z_{g,n})).  group = 128, or group = K for one scale per column.
 """
 from __future__ import annotations
 
@@ -57,6 +59,12 @@ def _load():
     lib.oracle_float_to_half.restype = ctypes.c_uint16
     lib.oracle_dequant.argtypes = [ctypes.c_uint8, ctypes.c_uint16]
     lib.oracle_dequant.restype = ctypes.c_double
+    lib.oracle_dequant_zp.argtypes = [ctypes.c_uint8, ctypes.c_uint16, ctypes.c_uint8]
+    lib.oracle_dequant_zp.restype = ctypes.c_double
+    for name in ("oracle_gemm_zp_f32", "oracle_gemm_zp_f64"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, p, p, i, i, i, i, p, i]
+        fn.restype = i
     for name in ("oracle_gemm_f32", "oracle_gemm_f64"):
         fn = getattr(lib, name)
         fn.argtypes = [p, p, p, i, i, i, i, p, i]
@@ -76,8 +84,9 @@ def _c(a: np.ndarray) -> np.ndarray:
 
 
 def gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128, mode: str = "f32",
-         nthreads: int = 0) -> np.ndarray:
-    """C = A @ Bhat with A fp16 [M, K], q uint8 [K, N], s fp16 [K/group, N]; returns fp16 [M, N]."""
+         nthreads: int = 0, zeros: np.ndarray | None = None) -> np.ndarray:
+    """C = A @ Bhat with A fp16 [M, K], q uint8 [K, N], s fp16 [K/group, N] and optional zero
+    points uint8 [K/group, N] (default 8); returns fp16 [M, N]."""
     A = _c(np.asarray(A, dtype=np.float16))
     q = _c(np.asarray(q, dtype=np.uint8))
     s = _c(np.asarray(s, dtype=np.float16))
@@ -86,9 +95,17 @@ def gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128, mode: st
     if K2 != K or s.shape != (K // group, N):
         raise ValueError(f"shape mismatch A{A.shape} q{q.shape} s{s.shape} group={group}")
     C = np.empty((M, N), dtype=np.float16)
-    fn = {"f32": _load().oracle_gemm_f32, "f64": _load().oracle_gemm_f64}[mode]
-    rc = fn(A.ctypes.data, q.ctypes.data, s.ctypes.data, M, K, N, group, C.ctypes.data,
-            int(nthreads))
+    if zeros is None:
+        fn = {"f32": _load().oracle_gemm_f32, "f64": _load().oracle_gemm_f64}[mode]
+        rc = fn(A.ctypes.data, q.ctypes.data, s.ctypes.data, M, K, N, group, C.ctypes.data,
+                int(nthreads))
+    else:
+        z = _c(np.asarray(zeros, dtype=np.uint8))
+        if z.shape != s.shape:
+            raise ValueError(f"zeros shape {z.shape} != scales shape {s.shape}")
+        fn = {"f32": _load().oracle_gemm_zp_f32, "f64": _load().oracle_gemm_zp_f64}[mode]
+        rc = fn(A.ctypes.data, q.ctypes.data, s.ctypes.data, z.ctypes.data, M, K, N, group,
+                C.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemm_{mode} returned {rc}")
     return C
@@ -122,8 +139,10 @@ def float_to_half(x: float) -> int:
     return int(_load().oracle_float_to_half(float(x)))
 
 
-def dequant(q: int, s_bits: int) -> float:
-    return _load().oracle_dequant(int(q), int(s_bits))
+def dequant(q: int, s_bits: int, z: int | None = None) -> float:
+    if z is None:
+        return _load().oracle_dequant(int(q), int(s_bits))
+    return _load().oracle_dequant_zp(int(q), int(s_bits), int(z))
 
 
 # --------------------------------------------------------------------------------------------
@@ -169,18 +188,25 @@ def round_scaled_to_half(S: int, shift: int = _SHIFT) -> int:
     return sign | ((ex + 15) << 10) | (qv - 1024)
 
 
-def exact_gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128):
+def exact_gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128,
+               zeros: np.ndarray | None = None):
     """Exact C per output: (correctly rounded fp16, exact value as float64, sum_k |a_k w_k|).
 
-    Pure Python integer arithmetic; use only on tiny shapes.
+    Pure Python integer arithmetic; use only on tiny shapes.  zeros: uint8 [K/group, N] zero
+    points (default 8).
     """
     A16 = np.asarray(A, dtype=np.float16).view(np.uint16)
     s16 = np.asarray(s, dtype=np.float16).view(np.uint16)
     q = np.asarray(q, dtype=np.uint8)
     M, K = A16.shape
     N = q.shape[1]
+    z = None if zeros is None else np.asarray(zeros, dtype=np.uint8)
+
+    def zp(k, n):
+        return 8 if z is None else int(z[k // group, n])
+
     a_int = [[_half_bits_to_scaled(int(A16[m, k])) for k in range(K)] for m in range(M)]
-    w_int = [[_half_bits_to_scaled(int(s16[k // group, n])) * (int(q[k, n]) - 8)
+    w_int = [[_half_bits_to_scaled(int(s16[k // group, n])) * (int(q[k, n]) - zp(k, n))
               for k in range(K)] for n in range(N)]
     out = np.empty((M, N), dtype=np.uint16)
     exact = np.empty((M, N), dtype=np.float64)

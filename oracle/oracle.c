@@ -12,12 +12,15 @@
  *        M x K matrix A with a K x N matrix B"; Marlin deep-dive page ("Marlin 完全拆解"),
  *        section "Marlin 要解决的精确问题", formula C = A B.
  *
- *   Bhat[k][n] = s[g][n] * (q[k][n] - 8),   g = floor(k / group),  q in {0..15}
- *     -- deep-dive page, same section, the dequantisation formula s_{g,n}(q_{k,n} - z_{g,n})
- *        with the symmetric zero point z = 8 (section "INT4 只是存储类型", where the
- *        zero point 8 is folded into the subtraction constant, giving q - 8);
- *        MARLIN paper sec. 3.4 "Kernel Design": symmetric INT4, one FP16 scale per G
- *        consecutive weights in each column; sec. 2.2: groups of 128 contiguous values.
+ *   Bhat[k][n] = s[g][n] * (q[k][n] - z[g][n]),   g = floor(k / group),  q, z in {0..15}
+ *     -- deep-dive page, same section, the dequantisation formula s_{g,n}(q_{k,n} - z_{g,n});
+ *        the main path is symmetric with z = 8 (section "INT4 只是存储类型", where the zero
+ *        point 8 is folded into the subtraction constant, giving q - 8), and the general
+ *        affine form takes a zero point per group and column (an integer code 0..15 here,
+ *        like q: the page leaves its type open).  MARLIN paper sec. 3.4 "Kernel Design":
+ *        symmetric INT4, one FP16 scale per G consecutive weights in each column; sec. 2.2:
+ *        groups of 128 contiguous values.  group = K is one scale per column (deep-dive
+ *        page, section "scale 为什么有时在内环乘，有时在末尾乘": AB = (AQ) diag(s)).
  *
  *   Accumulation in FP32, FP16 only when C is written
  *     -- deep-dive page, section "让多个 warp 计算同一个输出 tile 的部分和": the FP32
@@ -25,7 +28,7 @@
  *
  * The fp32 oracle takes k in ascending order, multiplies then adds (the file must be
  * compiled with -ffp-contract=off so no FMA is formed), and rounds the fp32 sum to fp16
- * with round-to-nearest-even.  s*(q-8) is exact in fp32 (11-bit by 4-bit significands), so
+ * with round-to-nearest-even.  s*(q-z) is exact in fp32 (11-bit by 5-bit significands), so
  * the only roundings are the product a*w, each addition, and the final fp16 rounding.
  *
  * The fp64 variant is a diagnostic "truth": a*w is exact in fp64 (26 significant bits) and
@@ -103,6 +106,12 @@ double oracle_dequant(uint8_t q, uint16_t s_bits)
     return oracle_half_to_double(s_bits) * (double)((int)q - 8);
 }
 
+/* The same with a zero point z: s * (q - z). */
+double oracle_dequant_zp(uint8_t q, uint16_t s_bits, uint8_t z)
+{
+    return oracle_half_to_double(s_bits) * (double)((int)q - (int)z);
+}
+
 /* ---------------------------------------------------------------- GEMM */
 
 typedef struct {
@@ -110,6 +119,7 @@ typedef struct {
     const double *a64;       /* A converted to fp64 (exact), M x K */
     const uint8_t *q;        /* codes, K x N row-major */
     const uint16_t *s;       /* scales (fp16 bits), (K/group) x N row-major */
+    const uint8_t *z;        /* zero points, (K/group) x N row-major, or NULL for 8 */
     uint16_t *C;             /* output fp16 bits, M x N row-major */
     int M, K, N, group;
     int n0, n1;              /* this worker's column range */
@@ -130,15 +140,16 @@ static void *oracle_worker(void *arg)
         return (void *)1;
 
     for (int n = j->n0; n < j->n1; ++n) {
-        /* Column n of Bhat: s[floor(k/group)][n] * (q[k][n] - 8). */
+        /* Column n of Bhat: s[floor(k/group)][n] * (q[k][n] - z[floor(k/group)][n]). */
         for (int k = 0; k < K; ++k) {
             int g = k / j->group;
             uint16_t sb = j->s[(size_t)g * N + n];
-            int qm8 = (int)j->q[(size_t)k * N + n] - 8;
+            int zp = j->z ? (int)j->z[(size_t)g * N + n] : 8;
+            int qmz = (int)j->q[(size_t)k * N + n] - zp;
             if (j->wide)
-                w64[k] = oracle_half_to_double(sb) * (double)qm8;
+                w64[k] = oracle_half_to_double(sb) * (double)qmz;
             else
-                w32[k] = (float)oracle_half_to_double(sb) * (float)qm8;
+                w32[k] = (float)oracle_half_to_double(sb) * (float)qmz;
         }
         /* C[m][n] = sum_k A[m][k] * Bhat[k][n], k ascending. */
         for (int m = 0; m < M; ++m) {
@@ -165,7 +176,7 @@ static void *oracle_worker(void *arg)
 }
 
 static int oracle_gemm_impl(const uint16_t *A, const uint8_t *q, const uint16_t *s,
-                            int M, int K, int N, int group, uint16_t *C,
+                            const uint8_t *z, int M, int K, int N, int group, uint16_t *C,
                             int nthreads, int wide)
 {
     if (!A || !q || !s || !C || M <= 0 || K <= 0 || N <= 0 || group <= 0 || K % group)
@@ -173,6 +184,10 @@ static int oracle_gemm_impl(const uint16_t *A, const uint8_t *q, const uint16_t 
     for (size_t i = 0; i < (size_t)K * N; ++i)
         if (q[i] > 15)
             return -1;
+    if (z)
+        for (size_t i = 0; i < (size_t)(K / group) * N; ++i)
+            if (z[i] > 15)
+                return -1;
 
     size_t na = (size_t)M * K;
     float *a32 = NULL;
@@ -213,6 +228,7 @@ static int oracle_gemm_impl(const uint16_t *A, const uint8_t *q, const uint16_t 
         j->a64 = a64;
         j->q = q;
         j->s = s;
+        j->z = z;
         j->C = C;
         j->M = M;
         j->K = K;
@@ -252,14 +268,27 @@ done:
 int oracle_gemm_f32(const uint16_t *A, const uint8_t *q, const uint16_t *s,
                     int M, int K, int N, int group, uint16_t *C, int nthreads)
 {
-    return oracle_gemm_impl(A, q, s, M, K, N, group, C, nthreads, 0);
+    return oracle_gemm_impl(A, q, s, NULL, M, K, N, group, C, nthreads, 0);
 }
 
 /* fp64 accumulation (diagnostic truth), fp16 RNE output from fp64. */
 int oracle_gemm_f64(const uint16_t *A, const uint8_t *q, const uint16_t *s,
                     int M, int K, int N, int group, uint16_t *C, int nthreads)
 {
-    return oracle_gemm_impl(A, q, s, M, K, N, group, C, nthreads, 1);
+    return oracle_gemm_impl(A, q, s, NULL, M, K, N, group, C, nthreads, 1);
+}
+
+/* The same two with a zero point per group and column (z codes 0..15; NULL means 8). */
+int oracle_gemm_zp_f32(const uint16_t *A, const uint8_t *q, const uint16_t *s, const uint8_t *z,
+                       int M, int K, int N, int group, uint16_t *C, int nthreads)
+{
+    return oracle_gemm_impl(A, q, s, z, M, K, N, group, C, nthreads, 0);
+}
+
+int oracle_gemm_zp_f64(const uint16_t *A, const uint8_t *q, const uint16_t *s, const uint8_t *z,
+                       int M, int K, int N, int group, uint16_t *C, int nthreads)
+{
+    return oracle_gemm_impl(A, q, s, z, M, K, N, group, C, nthreads, 1);
 }
 
 /* The M = 1 case written out on its own: one activation row against every column.

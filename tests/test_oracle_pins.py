@@ -271,3 +271,130 @@ def test_printed_dequant_constants_reproduce_code_minus_8():
             y = np.array([(word & hi) | magic], dtype=np.uint32).view(np.float16).astype(np.float64)
             assert list(x - (1024 + z)) == [qa - z, qb - z]
             assert list(y / 16 - (64 + z)) == [qb - z, qa - z]
+
+
+# ------------------------------------------------------------------ zero points, one scale per column
+# The general affine dequantisation s_{g,n} (q_{k,n} - z_{g,n}) of the deep-dive page (section
+# "Marlin 要解决的精确问题") and one scale per column (group = K; section "scale 为什么有时在内环乘，
+# 有时在末尾乘": AB = (AQ) diag(s)).
+
+from workloads import draw_zeros  # noqa: E402
+
+
+def test_dequant_with_zero_point_is_affine_and_vanishes_at_z():
+    for z in range(16):
+        for sb in (0x2000, 0x1E1F, 0x3C00):
+            s = float(np.uint16(sb).view(np.float16))
+            w = [oracle.dequant(q, sb, z) for q in range(16)]
+            assert w[z] == 0.0
+            assert all(w[q] == s * (q - z) for q in range(16))
+    assert all(oracle.dequant(q, 0x2000, 8) == oracle.dequant(q, 0x2000) for q in range(16))
+
+
+@pytest.mark.parametrize("group_is_k", [False, True])
+def test_zero_point_8_equals_the_symmetric_path(group_is_k):
+    K, N, M = 384, 24, 5
+    g = K if group_is_k else 128
+    A, q, s = draw(K, N, M, seed=41, group=g)
+    z = np.full((K // g, N), 8, dtype=np.uint8)
+    for mode in ("f32", "f64"):
+        assert np.array_equal(bits(oracle.gemm(A, q, s, group=g, mode=mode, zeros=z)),
+                              bits(oracle.gemm(A, q, s, group=g, mode=mode)))
+
+
+@pytest.mark.parametrize("M,K,N,group_is_k", [(1, 128, 16, False), (3, 256, 8, False),
+                                              (5, 384, 6, False), (2, 256, 8, True),
+                                              (4, 384, 5, True)])
+def test_zero_points_and_column_scales_against_exact_integer_sum(M, K, N, group_is_k):
+    g = K if group_is_k else 128
+    A, q, s = draw(K, N, M, seed=200 + M * K + N, group=g)
+    z = draw_zeros(K, N, seed=200 + M, group=g)
+    E, exact, absum = oracle.exact_gemm(A, q, s, group=g, zeros=z)
+    assert np.array_equal(bits(oracle.gemm(A, q, s, group=g, mode="f64", zeros=z)), bits(E))
+    C32 = oracle.gemm(A, q, s, group=g, zeros=z).astype(np.float64)
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    x = np.abs(exact) + gamma * absum
+    ulp16 = 2.0 ** (np.maximum(np.floor(np.log2(np.maximum(x, 2.0 ** -30))), -14) - 10)
+    assert (np.abs(C32 - exact) <= gamma * absum + ulp16).all()
+
+
+def test_code_equal_to_zero_point_gives_zero():
+    K, N, M = 256, 32, 4
+    A, _, s = draw(K, N, M, seed=43)
+    z = draw_zeros(K, N, seed=43)
+    q = np.repeat(z, 128, axis=0)                 # q[k, n] = z[k // 128, n]
+    assert (bits(oracle.gemm(A, q, s, zeros=z)) & 0x7FFF == 0).all()
+
+
+@pytest.mark.parametrize("k_hot", [0, 5, 127, 128, 255])
+def test_one_hot_activation_with_zero_points(k_hot):
+    K, N = 256, 40
+    _, q, s = draw(K, N, 1, seed=44)
+    z = draw_zeros(K, N, seed=44)
+    A = np.zeros((1, K), dtype=np.float16)
+    A[0, k_hot] = 1.0
+    g = k_hot // 128
+    want = (s[g].astype(np.float64) * (q[k_hot].astype(np.float64) - z[g])).astype(np.float16)
+    assert same(oracle.gemm(A, q, s, zeros=z)[0], want)
+
+
+def test_shifting_codes_and_zero_points_together_changes_nothing():
+    # q - z is what matters: q + d, z + d (codes still 0..15) give the same C bit for bit
+    K, N, M = 256, 16, 3
+    rng = np.random.default_rng(45)
+    A, _, s = draw(K, N, M, seed=45)
+    q = rng.integers(0, 8, (K, N), dtype=np.uint8)
+    z = rng.integers(0, 8, (K // 128, N), dtype=np.uint8)
+    C0 = oracle.gemm(A, q, s, zeros=z)
+    for d in (1, 5, 8):
+        assert np.array_equal(bits(oracle.gemm(A, q + d, s, zeros=z + d)), bits(C0))
+
+
+def test_zero_points_act_only_inside_their_group():
+    K, N, M = 384, 8, 2
+    A, q, s = draw(K, N, M, seed=46)
+    z = draw_zeros(K, N, seed=46)
+    for g in range(K // 128):
+        A1 = np.zeros_like(A)
+        A1[:, 128 * g:128 * (g + 1)] = A[:, 128 * g:128 * (g + 1)]
+        z2 = z.copy()
+        z2[(g + 1) % 3] = (z2[(g + 1) % 3] + 3) % 16      # another group's zero points
+        assert np.array_equal(bits(oracle.gemm(A1, q, s, zeros=z)), bits(oracle.gemm(A1, q, s, zeros=z2)))
+
+
+def test_column_scale_equals_group_scales_all_equal():
+    # one scale per column (group = K) is the grouped form with the same scale in every group
+    K, N, M = 512, 24, 6
+    A, q, s1 = draw(K, N, M, seed=47, group=K)
+    z1 = draw_zeros(K, N, seed=47, group=K)
+    s128 = np.repeat(s1, K // 128, axis=0)
+    z128 = np.repeat(z1, K // 128, axis=0)
+    for mode in ("f32", "f64"):
+        assert np.array_equal(bits(oracle.gemm(A, q, s1, group=K, mode=mode)),
+                              bits(oracle.gemm(A, q, s128, group=128, mode=mode)))
+        assert np.array_equal(bits(oracle.gemm(A, q, s1, group=K, mode=mode, zeros=z1)),
+                              bits(oracle.gemm(A, q, s128, group=128, mode=mode, zeros=z128)))
+
+
+def test_column_scale_factors_out_of_the_sum():
+    # AB = (AQ) diag(s): with power-of-two column scales the scaling is exact, so scaling the
+    # unit-scale product by s gives the same bits
+    K, N, M = 512, 16, 4
+    A, q, _ = draw(K, N, M, seed=48, group=K)
+    z = draw_zeros(K, N, seed=48, group=K)
+    rng = np.random.default_rng(48)
+    s = rng.choice(np.array([0.25, 0.5, 2.0, 0.0078125], dtype=np.float16), (1, N))
+    one = np.ones((1, N), dtype=np.float16)
+    C1 = oracle.gemm(A, q, one, group=K, zeros=z).astype(np.float32)
+    Cs = oracle.gemm(A, q, s, group=K, zeros=z).astype(np.float32)
+    big = np.abs(C1) >= 2.0 ** -6                 # away from fp16 subnormals after scaling
+    assert np.array_equal((C1 * s.astype(np.float32))[big], Cs[big])
+
+
+def test_bad_zero_points_rejected():
+    K, N, M = 128, 16, 1
+    A, q, s = draw(K, N, M, seed=49)
+    z = np.full((1, N), 16, dtype=np.uint8)
+    with pytest.raises(ValueError):
+        oracle.gemm(A, q, s, zeros=z)

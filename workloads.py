@@ -75,6 +75,13 @@ def draw(K: int, N: int, M: int, seed: int = 0, sigma: float = 1.0, group: int =
     return A, q, s
 
 
+def draw_zeros(K: int, N: int, seed: int = 0, group: int = GROUP) -> np.ndarray:
+    """Zero points z ~ U{0..15} per (group, column), uint8 [K/group, N], from a stream of their
+    own (numpy.random.default_rng([seed, 1])), so the draws of ``draw`` are unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    return rng.integers(0, 16, size=(K // group, N), dtype=np.uint8)
+
+
 def draw_shape(shape: Shape, seed: int = 0, group: int = GROUP):
     """Inputs for every M of a shape: A has max(Ms) rows; M uses A[:M]."""
     return draw(shape.K, shape.N, max(shape.Ms), seed=seed, sigma=shape.sigma, group=group)
