@@ -13,10 +13,16 @@
  *   Interface shape: Marlin README page, usage section (an offline pack step that reorders
  *   weights and scales, then a multiply call on pre-packed data).
  *
+ * Two further formats (w4a16_pack / w4a16_pack_zp with w4a16_gemm_ex): one scale per column
+ * (group = K: deep-dive page, section "scale 为什么有时在内环乘，有时在末尾乘", AB = (AQ) diag(s),
+ * the scale applied once per output), and a zero point per group and column,
+ * Bhat[k][n] = s[g][n] * (q[k][n] - z[g][n]) with z a code 0..15 (the page's general affine
+ * form s_{g,n}(q_{k,n} - z_{g,n}), section "Marlin 要解决的精确问题").
+ *
  * Conventions for every entry point:
  *   - fp16 values travel as their IEEE binary16 bit patterns (uint16_t on the host side).
  *   - Matrices are dense row-major with no padding: A is M x K, C is M x N, codes K x N,
- *     scales (K/128) x N.
+ *     scales and zero points (K/group) x N.
  *   - Sizes are int; a negative size is W4A16_EINVAL.  All arguments are checked before
  *     anything runs; on an error nothing is written.
  *   - The library never takes ownership of a pointer and never allocates device memory.
@@ -32,13 +38,14 @@
 extern "C" {
 #endif
 
-#define W4A16_GROUP 128           /* rows per scale group (the only group size supported) */
+#define W4A16_GROUP 128           /* rows per scale group; group = K (one per column) also works */
 #define W4A16_N_ALIGN 64          /* N must be a multiple of this */
 
 typedef enum {
     W4A16_OK = 0,
-    W4A16_EINVAL = -1,            /* null pointer, negative size, a code above 15 */
-    W4A16_ESHAPE = -2,            /* group != 128, K not a positive multiple of 128,
+    W4A16_EINVAL = -1,            /* null pointer, negative size, a code or zero point
+                                     above 15, zero_points not 0 or 1 */
+    W4A16_ESHAPE = -2,            /* group not 128 or K, K not a positive multiple of 128,
                                      N not a multiple of 16 (pack) or 64 (gemm), or a
                                      size limit of w4a16_gemm exceeded */
     W4A16_EUNSUPPORTED = -3,      /* the current HIP device is not a gfx950 GPU */
@@ -57,10 +64,10 @@ const char *w4a16_status_string(int status);
  * reshuffled offline to be contiguous).
  *
  *   codes      [in]  uint8 [K*N], row-major (k, n), one code 0..15 per byte
- *   scales     [in]  fp16 bits [(K/128)*N], row-major (g, n)
- *   group      [in]  must be 128
+ *   scales     [in]  fp16 bits [(K/group)*N], row-major (g, n)
+ *   group      [in]  128, or K for one scale per column
  *   packed_out [out] uint32 [K*N/8]
- *   scales_out [out] fp16 bits [(K/128)*N]
+ *   scales_out [out] fp16 bits [(K/group)*N]
  *
  * Packed layout (the part of this ABI a caller may rely on; 4.125 bits per weight):
  *   The weight matrix is cut into blocks of 128 rows (one scale group) x 16 columns.  Block
@@ -70,13 +77,14 @@ const char *w4a16_status_string(int status);
  *   column 16j + (l mod 16), rows 128g + 32t + 8*(l div 16) + i for i = 0..7, code i in
  *   nibble p(i) (bits 4p..4p+3) with p = {0, 4, 1, 5, 2, 6, 3, 7}.
  *   Scales are grouped by Q consecutive slabs, Q = 4 if N is a multiple of 256, else 2 if N
- *   is a multiple of 128, else 1 (the slabs one wave of w4a16_gemm works on):
- *   scales_out[(((j div Q)*(K/128) + g)*16 + c)*Q + (j mod Q)] = scales[g][16j + c],
+ *   is a multiple of 128, else 1 (the slabs one wave of w4a16_gemm works on); with
+ *   Gs = K/group scale groups per column:
+ *   scales_out[(((j div Q)*Gs + g)*16 + c)*Q + (j mod Q)] = scales[g][16j + c],
  *   c = 0..15, so the Q scales of one column at one group are adjacent.
  *
  * Returns W4A16_OK, W4A16_EINVAL (null pointer, negative size, a code > 15) or
- * W4A16_ESHAPE (group != 128, K not a positive multiple of 128, N not a positive multiple
- * of 16).
+ * W4A16_ESHAPE (group not 128 or K, K not a positive multiple of 128, N not a positive
+ * multiple of 16).
  */
 int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int group,
                uint32_t *packed_out, uint16_t *scales_out);
@@ -87,6 +95,30 @@ int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int g
  */
 int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packed, int K, int N, int group,
                  uint8_t *codes_out, uint16_t *scales_out);
+
+/*
+ * w4a16_pack with a zero point per group and column (host, synchronous): the deep-dive
+ * page's general dequantisation s_{g,n}(q_{k,n} - z_{g,n}) (section "Marlin 要解决的精确问题").
+ *
+ *   zeros      [in]  uint8 [(K/group)*N], row-major (g, n), one code 0..15 per byte
+ *   params_out [out] fp16 bits [2*(K/group)*N]: per column and group its scale and its zero
+ *                    term, the fp16 value 1024 + z (bits 0x6400 | z) that the kernel's decode
+ *                    subtracts.  Layout: the Q scales of a column at one group, then its Q
+ *                    zero terms: params_out[i] = scales[g][16j + c] and
+ *                    params_out[i + Q] = 0x6400 | zeros[g][16j + c] with
+ *                    i = (((j div Q)*Gs + g)*16 + c)*2Q + (j mod Q).
+ * Other arguments, the code layout and the errors as w4a16_pack (a zero point above 15 is
+ * W4A16_EINVAL).
+ */
+int w4a16_pack_zp(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int K,
+                  int N, int group, uint32_t *packed_out, uint16_t *params_out);
+
+/*
+ * Exact inverse of w4a16_pack_zp (host, synchronous; tests and tooling).  W4A16_EINVAL also
+ * if a zero term is not of the form 0x6400 | z.
+ */
+int w4a16_unpack_zp(const uint32_t *packed, const uint16_t *params, int K, int N, int group,
+                    uint8_t *codes_out, uint16_t *scales_out, uint8_t *zeros_out);
 
 /*
  * Bytes of device workspace w4a16_gemm needs for this shape on the current device (a fixed
@@ -127,6 +159,22 @@ int w4a16_workspace_size(int M, int K, int N, size_t *bytes);
  */
 int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
                int M, int K, int N, void *workspace, void *stream);
+
+/*
+ * w4a16_gemm for every packed format (device, asynchronous on `stream`):
+ *   group        128, or K for one scale per column: the fp32 sum over all of K is
+ *                scaled once per output before C is written (deep-dive page, section
+ *                "scale 为什么有时在内环乘，有时在末尾乘": AB = (AQ) diag(s)).
+ *   zero_points  0: `params` are the scales from w4a16_pack, z = 8;
+ *                1: `params` are from w4a16_pack_zp (scale and zero term per column and
+ *                   group), Bhat = s (q - z).
+ * w4a16_gemm(...) is w4a16_gemm_ex(..., 128, 0, ...).  The workspace size does not depend on
+ * the format.  Other arguments, limits and errors as w4a16_gemm; a group other than 128 or K
+ * is W4A16_ESHAPE, zero_points other than 0 or 1 W4A16_EINVAL.
+ */
+int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params, void *C,
+                  int M, int K, int N, int group, int zero_points, void *workspace,
+                  void *stream);
 
 #ifdef __cplusplus
 }

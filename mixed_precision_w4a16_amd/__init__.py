@@ -7,6 +7,10 @@ when the compiled library is missing; there is no fallback path.
     packed, scales_p = pack(codes, scales)          # host, offline (numpy in, numpy out)
     packed_d, scales_d = to_device(packed, scales_p)
     C = gemm(A, packed_d, scales_d, N)              # A: fp16 [M, K] on the GPU
+
+Other formats: pack(codes, scales, group=K) for one scale per column, and
+pack(codes, scales, group, zeros=z) for zero points; pass the same group / zero_points to
+gemm.
 """
 from __future__ import annotations
 
@@ -47,10 +51,16 @@ _lib.w4a16_workspace_size.argtypes = [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t
 _lib.w4a16_workspace_size.restype = _i
 _lib.w4a16_gemm.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _p]
 _lib.w4a16_gemm.restype = _i
+_lib.w4a16_pack_zp.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p]
+_lib.w4a16_pack_zp.restype = _i
+_lib.w4a16_unpack_zp.argtypes = [_p, _p, _i, _i, _i, _p, _p, _p]
+_lib.w4a16_unpack_zp.restype = _i
+_lib.w4a16_gemm_ex.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]
+_lib.w4a16_gemm_ex.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
-EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_size",
-            "w4a16_gemm")
+EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
+            "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex")
 
 
 class W4A16Error(RuntimeError):
@@ -72,32 +82,53 @@ def library():
 
 # ------------------------------------------------------------------------------ host side
 
-def pack(codes: np.ndarray, scales: np.ndarray, group: int = GROUP):
-    """Offline reorder.  codes uint8 [K, N] (0..15), scales fp16 [K/group, N] ->
-    (packed uint32 [K*N/8], scales_packed fp16 [(K/group)*N])."""
+def pack(codes: np.ndarray, scales: np.ndarray, group: int = GROUP, zeros=None):
+    """Offline reorder.  codes uint8 [K, N] (0..15), scales fp16 [K/group, N] (group 128, or
+    K for one scale per column), zeros optional uint8 [K/group, N] (0..15) ->
+    (packed uint32 [K*N/8], params fp16: the scales [(K/group)*N], or scales and zero terms
+    [2*(K/group)*N] when zeros are given)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float16)
     K, N = codes.shape
+    if not group or K % group or scales.shape != (K // group, N):
+        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape} "
+                         f"with group {group}")
     packed = np.empty(K * N // 8, dtype=np.uint32)
-    scales_p = np.empty(scales.size, dtype=np.float16)
-    if scales.shape != (K // group if group else 0, N):
-        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
-    _check("w4a16_pack", _lib.w4a16_pack(codes.ctypes.data, scales.ctypes.data, K, N, group,
-                                         packed.ctypes.data, scales_p.ctypes.data))
-    return packed, scales_p
+    if zeros is None:
+        params = np.empty(scales.size, dtype=np.float16)
+        _check("w4a16_pack", _lib.w4a16_pack(codes.ctypes.data, scales.ctypes.data, K, N, group,
+                                             packed.ctypes.data, params.ctypes.data))
+    else:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        if zeros.shape != scales.shape:
+            raise ValueError(f"zeros shape {zeros.shape} != scales shape {scales.shape}")
+        params = np.empty(2 * scales.size, dtype=np.float16)
+        _check("w4a16_pack_zp", _lib.w4a16_pack_zp(codes.ctypes.data, scales.ctypes.data,
+                                                   zeros.ctypes.data, K, N, group,
+                                                   packed.ctypes.data, params.ctypes.data))
+    return packed, params
 
 
-def unpack(packed: np.ndarray, scales_p: np.ndarray, K: int, N: int, group: int = GROUP):
-    """Inverse of pack: (codes uint8 [K, N], scales fp16 [K/group, N])."""
+def unpack(packed: np.ndarray, params: np.ndarray, K: int, N: int, group: int = GROUP,
+           zero_points: bool = False):
+    """Inverse of pack: (codes uint8 [K, N], scales fp16 [K/group, N]), plus zeros uint8
+    [K/group, N] when zero_points."""
     packed = np.ascontiguousarray(packed, dtype=np.uint32)
-    scales_p = np.ascontiguousarray(scales_p, dtype=np.float16)
-    if packed.size != K * N // 8 or scales_p.size != (K // group) * N:
+    params = np.ascontiguousarray(params, dtype=np.float16)
+    per = 2 if zero_points else 1
+    if not group or K % group or packed.size != K * N // 8 or params.size != per * (K // group) * N:
         raise ValueError("size mismatch")
     codes = np.empty((K, N), dtype=np.uint8)
     scales = np.empty((K // group, N), dtype=np.float16)
-    _check("w4a16_unpack", _lib.w4a16_unpack(packed.ctypes.data, scales_p.ctypes.data, K, N,
-                                             group, codes.ctypes.data, scales.ctypes.data))
-    return codes, scales
+    if not zero_points:
+        _check("w4a16_unpack", _lib.w4a16_unpack(packed.ctypes.data, params.ctypes.data, K, N,
+                                                 group, codes.ctypes.data, scales.ctypes.data))
+        return codes, scales
+    zeros = np.empty((K // group, N), dtype=np.uint8)
+    _check("w4a16_unpack_zp", _lib.w4a16_unpack_zp(packed.ctypes.data, params.ctypes.data, K, N,
+                                                   group, codes.ctypes.data, scales.ctypes.data,
+                                                   zeros.ctypes.data))
+    return codes, scales, zeros
 
 
 # ------------------------------------------------------------------------------ device side
@@ -139,22 +170,26 @@ def new_workspace(M: int, K: int, N: int, device="cuda"):
     return torch.zeros(workspace_bytes(M, K, N), dtype=torch.uint8, device=device)
 
 
-def gemm(A, packed, scales, N: int, out=None, ws=None, stream=None):
-    """C[M, N] = A[M, K] @ dequant(packed, scales) on A's device and the current stream.
+def gemm(A, packed, params, N: int, out=None, ws=None, stream=None, group: int = GROUP,
+         zero_points: bool = False):
+    """C[M, N] = A[M, K] @ dequant(packed, params) on A's device and the current stream.
 
-    A: fp16 [M, K] contiguous CUDA tensor.  packed: int32 [K*N/8], scales: fp16 [(K/128)*N],
-    both from to_device(pack(...)).  out: optional fp16 [M, N] contiguous tensor.
+    A: fp16 [M, K] contiguous CUDA tensor.  packed: int32 [K*N/8], params: fp16, both from
+    to_device(pack(...)) with the same group and zeros-or-not.  out: optional fp16 [M, N]
+    contiguous tensor.
     """
     import torch
     if A.dtype != torch.float16 or not A.is_cuda or A.dim() != 2 or not A.is_contiguous():
         raise ValueError("A must be a contiguous fp16 CUDA tensor of shape [M, K]")
     M, K = A.shape
-    if packed.device != A.device or scales.device != A.device:
-        raise ValueError("packed and scales must be on A's device")
+    if packed.device != A.device or params.device != A.device:
+        raise ValueError("packed and params must be on A's device")
     if packed.dtype != torch.int32 or packed.numel() * 8 != K * N or not packed.is_contiguous():
         raise ValueError("packed must be a contiguous int32 tensor of K*N/8 words")
-    if scales.dtype != torch.float16 or scales.numel() * GROUP != K * N or not scales.is_contiguous():
-        raise ValueError("scales must be a contiguous fp16 tensor of (K/128)*N values")
+    per = 2 if zero_points else 1
+    if (not group or K % group or params.dtype != torch.float16
+            or params.numel() != per * (K // group) * N or not params.is_contiguous()):
+        raise ValueError("params must be a contiguous fp16 tensor as pack() returned it")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=A.device)
     elif (out.dtype != torch.float16 or out.shape != (M, N) or not out.is_contiguous()
@@ -167,7 +202,13 @@ def gemm(A, packed, scales, N: int, out=None, ws=None, stream=None):
             ws = workspace(M, K, N, A.device)
         if stream is None:
             stream = torch.cuda.current_stream(A.device)
-        _check("w4a16_gemm", _lib.w4a16_gemm(A.data_ptr(), packed.data_ptr(), scales.data_ptr(),
-                                             out.data_ptr(), M, K, N, ws.data_ptr(),
-                                             stream.cuda_stream))
+        if group == GROUP and not zero_points:
+            _check("w4a16_gemm", _lib.w4a16_gemm(A.data_ptr(), packed.data_ptr(),
+                                                 params.data_ptr(), out.data_ptr(), M, K, N,
+                                                 ws.data_ptr(), stream.cuda_stream))
+        else:
+            _check("w4a16_gemm_ex", _lib.w4a16_gemm_ex(A.data_ptr(), packed.data_ptr(),
+                                                       params.data_ptr(), out.data_ptr(), M, K,
+                                                       N, group, int(bool(zero_points)),
+                                                       ws.data_ptr(), stream.cuda_stream))
     return out

@@ -76,16 +76,28 @@ constexpr int kMaxWGs = static_cast<int>(kCounterBytes / sizeof(int));
 struct Params {
     const uint16_t *A;        // fp16 [M][K]
     const u4 *packed;         // 16-byte quads, 64 per 128x16 block
-    const uint16_t *scales;   // fp16 bits, 16 per block
+    const uint16_t *scales;   // fp16 bits: scales (and zero terms) in w4a16_pack(_zp) order
     uint16_t *C;              // fp16 [M][N]
     int *counters;            // kMaxWGs ints, zero between calls
     float *partials;          // 2 * W slots of Mt*Nt floats
     int M, K, N;
     int G;                    // K / 128: tiles per slice
+    int Gs;                   // scale groups per column: G, or 1 for one scale per column
     int P;                    // M sub-problems of Mt rows
     int W;                    // workgroups = stripes
     long long T;              // total tiles = (N / Nt) * P * G
 };
+
+// Packed format: zero points (per group and column, else the fixed 8) and where the scale
+// sits (per 128-row group, or one per column applied once at the end).
+template <bool ZP_, bool COL_>
+struct Fmt {
+    static constexpr bool ZP = ZP_;
+    static constexpr bool COL = COL_;
+    // the K loop needs per-tile parameters unless the scale is per column and z is fixed
+    static constexpr bool kTileParams = ZP_ || !COL_;
+};
+using FmtSym = Fmt<false, false>;
 
 // (a & m) | o in one VALU op.  gfx9 VOP3 encodings take no literal and read at most one
 // SGPR, so left to itself the compiler splits this into v_and + v_or; the "v" constraints
@@ -97,48 +109,58 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
     return r;
 }
 
-// 8 codes -> 8 fp16 values q - 8, in MFMA B-operand order (see pack.cpp for the nibbles).
-// 9 VALU ops per 8 weights: 4 mask-and-OR, 1 shift, 2 packed adds, 2 packed FMAs.
-__device__ __forceinline__ h8 dequant8(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic)
+// 8 codes -> 8 fp16 values q - z, in MFMA B-operand order (see pack.cpp for the nibbles).
+// 9 VALU ops per 8 weights: 4 mask-and-OR, 1 shift, 2 packed adds, 2 packed FMAs.  `zsub`
+// is 1024 + z and `zadd` is 960 - (1024 + z) = -(64 + z), both exact in fp16: the low nibbles
+// give 1024 + q, the high ones 1024 + 16q, so (1024 + q) - zsub and (1024 + 16q) / 16 + zadd
+// are q - z exactly.  The symmetric format passes z = 8: 1032 and -72.
+__device__ __forceinline__ h8 dequant8(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic,
+                                       h2 zsub, h2 zadd)
 {
     const uint32_t w8 = w >> 8;
     const uint32_t x0 = and_or(w, mlo, magic);     // k0, k1: fp16 1024 + q
     const uint32_t x1 = and_or(w, mhi, magic);     // k2, k3: fp16 1024 + 16 q
     const uint32_t x2 = and_or(w8, mlo, magic);    // k4, k5
     const uint32_t x3 = and_or(w8, mhi, magic);    // k6, k7
-    const h2 sub = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
     const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-    const h2 add = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
-    const h2 y0 = __builtin_bit_cast(h2, x0) - sub;                                // q - 8
-    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, add); // q - 8
-    const h2 y2 = __builtin_bit_cast(h2, x2) - sub;
-    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, add);
+    const h2 y0 = __builtin_bit_cast(h2, x0) - zsub;                                // q - z
+    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, zadd); // q - z
+    const h2 y2 = __builtin_bit_cast(h2, x2) - zsub;
+    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, zadd);
     h8 r;
     r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
     r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
     return r;
 }
 
-// 8 weights, decoded and scaled: fp16(s * (q - 8)), one rounding.
+// 8 weights, decoded and scaled: fp16(s * (q - z)), one rounding.
 __device__ __forceinline__ h8 dequant8_scaled(uint32_t w, h2 s, uint32_t mlo, uint32_t mhi,
-                                              uint32_t magic)
+                                              uint32_t magic, h2 zsub, h2 zadd)
 {
     const uint32_t w8 = w >> 8;
     const uint32_t x0 = and_or(w, mlo, magic);
     const uint32_t x1 = and_or(w, mhi, magic);
     const uint32_t x2 = and_or(w8, mlo, magic);
     const uint32_t x3 = and_or(w8, mhi, magic);
-    const h2 sub = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
     const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-    const h2 add = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
-    const h2 y0 = (__builtin_bit_cast(h2, x0) - sub) * s;
-    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, add) * s;
-    const h2 y2 = (__builtin_bit_cast(h2, x2) - sub) * s;
-    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, add) * s;
+    const h2 y0 = (__builtin_bit_cast(h2, x0) - zsub) * s;
+    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, zadd) * s;
+    const h2 y2 = (__builtin_bit_cast(h2, x2) - zsub) * s;
+    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, zadd) * s;
     h8 r;
     r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
     r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
     return r;
+}
+
+// Decode constants (zsub, zadd) of the symmetric format, z = 8.
+__device__ __forceinline__ h2 sym_zsub()
+{
+    return h2{static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+}
+__device__ __forceinline__ h2 sym_zadd()
+{
+    return h2{static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b)
@@ -194,7 +216,8 @@ template <int MB, int NBW, int WAVES = kWaves>
 __device__ __forceinline__ void load_cursor_set(const Params &p, int wave, LoadCursor &c)
 {
     c.wblk = (static_cast<uint32_t>(c.s) * (WAVES * NBW) + wave * NBW) * p.G + c.g;
-    c.sblk = (static_cast<uint32_t>(c.s) * WAVES + wave) * p.G + c.g;
+    // with one scale per column (Gs = 1) the parameters stay at group 0 for the whole slice
+    c.sblk = (static_cast<uint32_t>(c.s) * WAVES + wave) * p.Gs + (p.Gs == 1 ? 0 : c.g);
     c.a_soff = static_cast<uint32_t>(c.g) * (kGroup * 2);
 }
 
@@ -234,51 +257,81 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
         stage[(16 * mb + r) * 16 + (c ^ r)] = ar[mb];
 }
 
-// Scales of a wave's NBW slabs at one K step: w4a16_pack stores the NBW scales of a column
-// side by side (NBW = 4 / 2: 8 / 4 bytes per column), so one load per lane brings all of them;
-// with NBW = 1 a lane loads the aligned dword holding its column's scale and its neighbour's.
-// (A 16-bit load result would be re-copied across the loop back-edge.)
-template <int NBW>
-struct ScaleRegs {
-    static constexpr int n = NBW >= 2 ? NBW / 2 : 1;
+// Per-column parameters of a wave's NBW slabs at one K step (its "scale group" sblk):
+// w4a16_pack stores the NBW scales of a column side by side, w4a16_pack_zp the NBW scales then
+// the NBW zero terms, so one load per lane brings all of them: 2 NBW or 4 NBW bytes per
+// column.  The symmetric format with NBW = 1 loads the aligned dword holding its column's
+// scale and its neighbour's.  (A 16-bit load result would be re-copied across the loop
+// back-edge.)
+template <int NBW, bool ZP>
+struct ParamRegs {
+    static constexpr int n = ZP ? NBW : (NBW >= 2 ? NBW / 2 : 1);
 };
 
-template <int NBW>
-__device__ __forceinline__ void load_scales(__amdgpu_buffer_rsrc_t rS, int lane, uint32_t sblk,
-                                            uint32_t (&sc)[ScaleRegs<NBW>::n])
+template <int NBW, bool ZP>
+__device__ __forceinline__ void load_params(__amdgpu_buffer_rsrc_t rS, int lane, uint32_t sblk,
+                                            uint32_t (&pr)[ParamRegs<NBW, ZP>::n])
 {
-    const uint32_t so = __builtin_amdgcn_readfirstlane(sblk * (32u * (NBW >= 2 ? NBW : 1)));
-    if constexpr (NBW == 4) {
+    constexpr uint32_t per_group = 16u * 2u * (ZP ? 2 * NBW : (NBW >= 2 ? NBW : 1));
+    const uint32_t so = __builtin_amdgcn_readfirstlane(sblk * per_group);
+    constexpr int bytes = 4 * ParamRegs<NBW, ZP>::n;               // per lane
+    if constexpr (bytes == 16) {
+        const auto v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rS, (lane & 15) * 16, so, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pr[i] = v[i];
+    } else if constexpr (bytes == 8) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, (lane & 15) * 8, so, 0);
-        sc[0] = v[0];
-        sc[1] = v[1];
-    } else if constexpr (NBW == 2) {
-        sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 15) * 4, so, 0);
+        pr[0] = v[0];
+        pr[1] = v[1];
+    } else if constexpr (ZP || NBW == 2) {
+        pr[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 15) * 4, so, 0);
     } else {
-        sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, so, 0);
+        pr[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, so, 0);
     }
 }
 
 // fp16 bits of slab b's scale for this lane's column.
-template <int NBW>
-__device__ __forceinline__ uint16_t scale_bits(const uint32_t (&sc)[ScaleRegs<NBW>::n], int b,
-                                               int lane)
+template <int NBW, bool ZP>
+__device__ __forceinline__ uint16_t scale_bits(const uint32_t (&pr)[ParamRegs<NBW, ZP>::n],
+                                               int b, int lane)
 {
-    if constexpr (NBW >= 2)
-        return static_cast<uint16_t>(sc[b >> 1] >> ((b & 1) * 16));
+    if constexpr (ZP || NBW >= 2)
+        return static_cast<uint16_t>(pr[b >> 1] >> ((b & 1) * 16));
     else
-        return static_cast<uint16_t>(sc[0] >> ((lane & 1) * 16));
+        return static_cast<uint16_t>(pr[0] >> ((lane & 1) * 16));
 }
 
-// This wave's packed weight quads (1 KiB contiguous per slab) and scales.  With 16- and
-// 32-row tiles every weight byte is used once (M <= 32 is one row sub-problem), so it is
-// streamed non-temporally (evict first, the pages' evict_first hint) and A stays in the L2.
-// 64-row tiles can run several row sub-problems that re-read a slice's weights right away,
-// and measure faster with the weights left in the cache.
-template <int MB, int NBW>
+// Decode constants of slab b: (1024 + z, -(64 + z)) from the stored zero term, or those of
+// z = 8.
+template <int NBW, bool ZP>
+__device__ __forceinline__ void zero_consts(const uint32_t (&pr)[ParamRegs<NBW, ZP>::n], int b,
+                                            h2 &zsub, h2 &zadd)
+{
+    if constexpr (ZP) {
+        const int i = NBW + b;
+        const _Float16 zt =
+            __builtin_bit_cast(_Float16, static_cast<uint16_t>(pr[i >> 1] >> ((i & 1) * 16)));
+        zsub = h2{zt, zt};
+        const h2 k960 = {static_cast<_Float16>(960.0f), static_cast<_Float16>(960.0f)};
+        zadd = k960 - zsub;
+    } else {
+        zsub = sym_zsub();
+        zadd = sym_zadd();
+    }
+}
+
+// This wave's packed weight quads (1 KiB contiguous per slab) and, if the format needs them
+// per K step, its parameters.  With 16- and 32-row tiles every weight byte is used once
+// (M <= 32 is one row sub-problem), so it is streamed non-temporally (evict first, the
+// pages' evict_first hint) and A stays in the L2.  64-row tiles can run several row
+// sub-problems that re-read a slice's weights right away, and measure faster with the weights
+// left in the cache.
+template <int MB, int NBW, class F>
 __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
                                        int G, int lane, uint32_t wblk, uint32_t sblk,
-                                       u4 (&wq)[NBW], uint32_t (&sc)[ScaleRegs<NBW>::n])
+                                       u4 (&wq)[NBW], uint32_t (&pr)[ParamRegs<NBW, F::ZP>::n])
 {
     constexpr int policy = MB <= 2 ? kNonTemporal : 0;
 #pragma unroll
@@ -287,40 +340,49 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
         wq[b] = __builtin_bit_cast(
             u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, policy));
     }
-    load_scales<NBW>(rS, lane, sblk, sc);
+    if constexpr (F::kTileParams)
+        load_params<NBW, F::ZP>(rS, lane, sblk, pr);
 }
 
-// Where the group scale is applied.  Small tiles (MB <= 2) keep (q - 8) exact: the MFMA
-// sums A * (q - 8) over the group in fp32 and the fp32 partial is scaled once per output
+// Where the scale is applied.  One scale per column: not in the K loop at all; the fp32 sum
+// of A * (q - z) over the whole K range is scaled once at the slice's end (slice_end), the
+// pages' AB = (AQ) diag(s).  Per group, small tiles (MB <= 2) keep (q - z) exact: the MFMA
+// sums A * (q - z) over the group in fp32 and the fp32 partial is scaled once per output
 // (4 FMAs per 16x16 tile per group).  With 64 or more rows the per-tile FMAs and the partial
-// registers cost more than scaling the weights: each dequantised pair is multiplied by the
+// registers cost more than scaling the weights: each decoded pair is multiplied by the
 // column's scale in fp16 (one packed multiply per two weights, the pages' own order:
 // dequantise, scale, then MMA) and the MFMA accumulates straight into the output sum.  The
-// rounding of s * (q - 8) to fp16 is below 2^-11 relative per weight.
-template <int MB>
+// rounding of s * (q - z) to fp16 is below 2^-11 relative per weight.
+template <int MB, class F>
 struct ScaleMode {
-    static constexpr bool kWeights = MB >= 4;
+    static constexpr bool kWeights = !F::COL && MB >= 4;
+    static constexpr bool kPartial = !F::COL && MB < 4;
 };
 
-template <int MB, int NBW>
+template <int MB, int NBW, class F>
 __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4 (&wq)[NBW],
-                                             const uint32_t (&sc)[ScaleRegs<NBW>::n],
+                                             const uint32_t (&pr)[ParamRegs<NBW, F::ZP>::n],
                                              f4 (&acc)[MB][NBW], uint32_t mlo, uint32_t mhi,
                                              uint32_t magic)
 {
-    // Scales first: converting them here ends the loaded registers' live range before the
-    // next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
+    // Parameters first: converting them here ends the loaded registers' live range before
+    // the next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
     float sf[NBW];
-    h2 s2[NBW];
+    h2 s2[NBW], zsub[NBW], zadd[NBW];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
-        if constexpr (ScaleMode<MB>::kWeights) {
-            const _Float16 sh = __builtin_bit_cast(_Float16, scale_bits<NBW>(sc, b, lane));
+        if constexpr (ScaleMode<MB, F>::kWeights) {
+            const _Float16 sh = __builtin_bit_cast(_Float16, scale_bits<NBW, F::ZP>(pr, b, lane));
             s2[b] = h2{sh, sh};
             asm volatile("" : "+v"(s2[b]));
-        } else {
-            sf[b] = half_bits_to_float(scale_bits<NBW>(sc, b, lane));
+        } else if constexpr (ScaleMode<MB, F>::kPartial) {
+            sf[b] = half_bits_to_float(scale_bits<NBW, F::ZP>(pr, b, lane));
             asm volatile("" : "+v"(sf[b]));
+        }
+        zero_consts<NBW, F::ZP>(pr, b, zsub[b], zadd[b]);
+        if constexpr (F::ZP) {
+            asm volatile("" : "+v"(zsub[b]));
+            asm volatile("" : "+v"(zadd[b]));
         }
     }
     // A fragments from LDS: row lane%16 of each sub-tile, k = 32t + 8(lane/16) .. +7.
@@ -332,12 +394,16 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
         for (int t = 0; t < 4; ++t)
             a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
 
-    if constexpr (ScaleMode<MB>::kWeights) {
+    if constexpr (!ScaleMode<MB, F>::kPartial) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
-                const h8 bw = dequant8_scaled(wq[b][t], s2[b], mlo, mhi, magic);
+                h8 bw;
+                if constexpr (ScaleMode<MB, F>::kWeights)
+                    bw = dequant8_scaled(wq[b][t], s2[b], mlo, mhi, magic, zsub[b], zadd[b]);
+                else
+                    bw = dequant8(wq[b][t], mlo, mhi, magic, zsub[b], zadd[b]);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bw, acc[mb][b],
@@ -350,30 +416,30 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
             for (int mb = 0; mb < MB; ++mb)
                 asm volatile("" : "+v"(acc[mb][b]));    // finish the update here
         return;
-    }
-
-    f4 part[MB][NBW];
+    } else {
+        f4 part[MB][NBW];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-            const h8 bw = dequant8(wq[b][t], mlo, mhi, magic);
+            for (int b = 0; b < NBW; ++b) {
+                const h8 bw = dequant8(wq[b][t], mlo, mhi, magic, zsub[b], zadd[b]);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const f4 cin = (t == 0) ? f4{0.f, 0.f, 0.f, 0.f} : part[mb][b];
-                part[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bw, cin, 0, 0, 0);
+                for (int mb = 0; mb < MB; ++mb) {
+                    const f4 cin = (t == 0) ? f4{0.f, 0.f, 0.f, 0.f} : part[mb][b];
+                    part[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bw, cin, 0, 0, 0);
+                }
             }
         }
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[mb][b][r] = __builtin_fmaf(sf[b], part[mb][b][r], acc[mb][b][r]);
+                asm volatile("" : "+v"(acc[mb][b]));    // finish the update here
+            }
     }
-#pragma unroll
-    for (int b = 0; b < NBW; ++b)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[mb][b][r] = __builtin_fmaf(sf[b], part[mb][b][r], acc[mb][b][r]);
-            asm volatile("" : "+v"(acc[mb][b]));        // finish the update here
-        }
 }
 
 // Opaque copy of a uniform value: offsets derived from it are computed where they are used.
@@ -527,19 +593,34 @@ __device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rs
     write_c<MB, NBW, WAVES>(p, rC, wave, lane, sigma, acc);
 }
 
-// End of a slice (or of the stripe) for the running accumulators.  Three cases:
+// End of a slice (or of the stripe) for the running accumulators.  With one scale per
+// column the accumulators hold the sum of A * (q - z) over the stripe's K range; they are
+// scaled here, once per output (pieces of a split slice are scaled before they are summed:
+// the scale is the same for all of them).  Then three cases:
 //  * the stripe computed the whole slice: write C;
 //  * the stripe entered the slice part-way (so it is the slice it started in): store the
 //    piece to slot 0 and record it in `nonown`;
 //  * the stripe holds the slice's first tile but not its last (so this is its last tile):
 //    it is the slice's owner and keeps its piece in the accumulators for settle().
-template <int MB, int NBW, int WAVES = kWaves>
+template <int MB, int NBW, class F, int WAVES = kWaves>
 __device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_t rP,
-                                          __amdgpu_buffer_rsrc_t rC, int stripe, long long t0,
-                                          long long t, long long sigma, int wave, int lane,
-                                          const f4 (&acc)[MB][NBW], long long &nonown,
-                                          long long &own)
+                                          __amdgpu_buffer_rsrc_t rC, __amdgpu_buffer_rsrc_t rS,
+                                          int stripe, long long t0, long long t, long long sigma,
+                                          int wave, int lane, f4 (&acc)[MB][NBW],
+                                          long long &nonown, long long &own)
 {
+    if constexpr (F::COL) {
+        const long long sl = sigma / p.P;
+        uint32_t pr[ParamRegs<NBW, F::ZP>::n];
+        load_params<NBW, F::ZP>(rS, lane, static_cast<uint32_t>(sl) * WAVES + wave, pr);
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const float sc = half_bits_to_float(scale_bits<NBW, F::ZP>(pr, b, lane));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb][b] *= sc;
+        }
+    }
     const long long s0 = sigma * p.G;
     if (t0 <= s0 && t == s0 + p.G - 1) {
         write_c<MB, NBW, WAVES>(p, rC, wave, lane, sigma, acc);
@@ -634,7 +715,7 @@ __device__ __forceinline__ void settle(const Params &p, __amdgpu_buffer_rsrc_t r
     }
 }
 
-template <int MB, int NBW>
+template <int MB, int NBW, class F>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
 {
     using TL = Tile<MB, NBW>;
@@ -660,8 +741,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
     const __amdgpu_buffer_rsrc_t rW =
         make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
-    const __amdgpu_buffer_rsrc_t rS =
-        make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(
+        p.scales, static_cast<uint32_t>(static_cast<size_t>(p.Gs) * p.N * (F::ZP ? 4 : 2)));
     const __amdgpu_buffer_rsrc_t rP =
         make_rsrc(p.partials, static_cast<uint32_t>(2u * p.W * TL::kSlotFloats * 4u));
     const __amdgpu_buffer_rsrc_t rC =
@@ -701,7 +782,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
             ++lt;
             ++lc.g;
             ++lc.wblk;
-            ++lc.sblk;
+            if constexpr (!F::COL)
+                ++lc.sblk;
             lc.a_soff += kGroup * 2;
             if (lc.g == p.G) {         // next slice (uniform, rare)
                 lc.g = 0;
@@ -727,16 +809,16 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     // is not needed yet: each weight tile has one whole tile of compute to arrive in.
     u4 ar[MB];
     u4 wq0[NBW], wq1[NBW];
-    uint32_t sc0[ScaleRegs<NBW>::n], sc1[ScaleRegs<NBW>::n];
+    uint32_t sc0[ParamRegs<NBW, F::ZP>::n], sc1[ParamRegs<NBW, F::ZP>::n];
     int st_cp = 0, st_st = 1;             // ring stages being computed from / stored to
     auto next_stage = [](int x) { return x == TL::kStages - 1 ? 0 : x + 1; };
 
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0)
-    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq0, sc0);        // W(t0)
+    load_w<MB, NBW, F>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq0, sc0);        // W(t0)
     store_a<MB>(lds, tid, ar);                                // stage 0
     step_load();
     load_a<MB>(rA, a_voff, lc.a_soff, ar);                   // A(t0+1)
-    load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq1, sc1);        // W(t0+1)
+    load_w<MB, NBW, F>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq1, sc1);        // W(t0+1)
     step_load();                                              // lc -> t0+2
 
     // End of a tile: at a slice's end, hand the accumulators to slice_end.  The stripe's last
@@ -747,7 +829,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
             return;
         }
         if (g == p.G - 1) {
-            slice_end<MB, NBW>(p, rP, rC, stripe, t0, t, sigma, wave, lane, acc, nonown, own);
+            slice_end<MB, NBW, F>(p, rP, rC, rS, stripe, t0, t, sigma, wave, lane, acc, nonown,
+                                  own);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -770,11 +853,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
-        compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
-        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq0, sc0);    // W(t+2)
+        load_w<MB, NBW, F>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq0, sc0);    // W(t+2)
         step_load();
         st_cp = st_st;
         st_st = next_stage(st_st);
@@ -782,21 +865,21 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
-        compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq1, sc1, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq1, sc1, acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
-        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq1, sc1);    // W(t+2)
+        load_w<MB, NBW, F>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq1, sc1);    // W(t+2)
         step_load();
         st_cp = st_st;
         st_st = next_stage(st_st);
     }
     if (t < t1) {
         __syncthreads();
-        compute_tile<MB, NBW>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
         end_of_tile();
     }
-    slice_end<MB, NBW>(p, rP, rC, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
+    slice_end<MB, NBW, F>(p, rP, rC, rS, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
     settle<MB, NBW>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
 }
 
@@ -862,28 +945,41 @@ __device__ __forceinline__ void wide_dma_a(const Params &p, __amdgpu_buffer_rsrc
 }
 
 // One 128-row K step of the wave's 128 x 64 output block.  Per 32-k MFMA step the four B
-// fragments are decoded first; then each A fragment (row block mb) is read from LDS once and
-// used by four MFMAs.
+// fragments are decoded (and, with per-group scales, scaled) first; then each A fragment
+// (row block mb) is read from LDS once and used by four MFMAs.
+template <class F>
 __device__ __forceinline__ void wide_compute(const u4 *stage, int lane,
                                              const u4 (&wq)[kWideNBW],
-                                             const uint32_t (&sc)[ScaleRegs<kWideNBW>::n],
+                                             const uint32_t (&pr)[ParamRegs<kWideNBW, F::ZP>::n],
                                              f4 (&acc)[kWideMB][kWideNBW], uint32_t mlo,
                                              uint32_t mhi, uint32_t magic)
 {
-    h2 s2[kWideNBW];
+    h2 s2[kWideNBW], zsub[kWideNBW], zadd[kWideNBW];
 #pragma unroll
     for (int b = 0; b < kWideNBW; ++b) {
-        const _Float16 sh = __builtin_bit_cast(_Float16, scale_bits<kWideNBW>(sc, b, lane));
-        s2[b] = h2{sh, sh};
-        asm volatile("" : "+v"(s2[b]));
+        if constexpr (!F::COL) {
+            const _Float16 sh =
+                __builtin_bit_cast(_Float16, scale_bits<kWideNBW, F::ZP>(pr, b, lane));
+            s2[b] = h2{sh, sh};
+            asm volatile("" : "+v"(s2[b]));
+        }
+        zero_consts<kWideNBW, F::ZP>(pr, b, zsub[b], zadd[b]);
+        if constexpr (F::ZP) {
+            asm volatile("" : "+v"(zsub[b]));
+            asm volatile("" : "+v"(zadd[b]));
+        }
     }
     const int row = lane & 15, quad = lane >> 4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         h8 bw[kWideNBW];
 #pragma unroll
-        for (int b = 0; b < kWideNBW; ++b)
-            bw[b] = dequant8_scaled(wq[b][t], s2[b], mlo, mhi, magic);
+        for (int b = 0; b < kWideNBW; ++b) {
+            if constexpr (F::COL)
+                bw[b] = dequant8(wq[b][t], mlo, mhi, magic, zsub[b], zadd[b]);
+            else
+                bw[b] = dequant8_scaled(wq[b][t], s2[b], mlo, mhi, magic, zsub[b], zadd[b]);
+        }
 #pragma unroll
         for (int mb = 0; mb < kWideMB; ++mb) {
             const h8 a = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
@@ -900,13 +996,13 @@ constexpr int vmcnt_imm(int n)
     return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-template <int WAVES, int STAGES>
+template <int WAVES, int STAGES, class F>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(Params p)
 {
     using TL = Tile<kWideMB, kWideNBW, WAVES>;
     constexpr int MB = kWideMB, NBW = kWideNBW;
     constexpr int ND = 32 / WAVES;             // A DMAs per wave per tile
-    constexpr int NW = NBW + 1;                // weight + scale loads per wave per tile
+    constexpr int NW = NBW + (F::kTileParams ? 1 : 0);   // weight + parameter loads per tile
     // The stages are separate arrays: with distinct objects the compiler can tell that the
     // reads of one stage do not depend on a DMA into another (it waits for pending LDS DMA
     // before any LDS read that may alias it).
@@ -936,8 +1032,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
         make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
     const __amdgpu_buffer_rsrc_t rW =
         make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
-    const __amdgpu_buffer_rsrc_t rS =
-        make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(
+        p.scales, static_cast<uint32_t>(static_cast<size_t>(p.Gs) * p.N * (F::ZP ? 4 : 2)));
     const __amdgpu_buffer_rsrc_t rP =
         make_rsrc(p.partials, static_cast<uint32_t>(2u * p.W * TL::kSlotFloats * 4u));
     const __amdgpu_buffer_rsrc_t rC =
@@ -976,7 +1072,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
             ++lt;
             ++lc.g;
             ++lc.wblk;
-            ++lc.sblk;
+            if constexpr (!F::COL)
+                ++lc.sblk;
             lc.a_soff += kGroup * 2;
             if (lc.g == p.G) {
                 lc.g = 0;
@@ -991,7 +1088,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
     // Weight buffers, one per stage: tile i uses stage and buffer i % STAGES.
     u4 wq[STAGES][NBW];
-    uint32_t sc[STAGES][ScaleRegs<NBW>::n];
+    uint32_t sc[STAGES][ParamRegs<NBW, F::ZP>::n];
 
     // Issue the loads of the tile at the load position into stage / buffer k, the DMAs first
     // (the asm and scheduling barriers keep that order), and move the cursor on.
@@ -1000,7 +1097,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
         wide_dma_a<WAVES>(p, rA, stage(k), wave, lane, a_rowoff());
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_w<MB, NBW>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq[K], sc[K]);
+        load_w<MB, NBW, F>(rW, rS, p.G, lane, lc.wblk, lc.sblk, wq[K], sc[K]);
         advance();
     };
 
@@ -1010,8 +1107,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
             return;
         }
         if (g == p.G - 1) {
-            slice_end<MB, NBW, WAVES>(p, rP, rC, stripe, t0, t, sigma, wave, lane, acc, nonown,
-                                      own);
+            slice_end<MB, NBW, F, WAVES>(p, rP, rC, rS, stripe, t0, t, sigma, wave, lane, acc,
+                                         nonown, own);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1039,7 +1136,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitA));
         __syncthreads();
         issue(std::integral_constant<int, (K + STAGES - 1) % STAGES>{});
-        wide_compute(stage(k), lane, wq[K], sc[K], acc, mlo, mhi, magic);
+        wide_compute<F>(stage(k), lane, wq[K], sc[K], acc, mlo, mhi, magic);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
@@ -1064,7 +1161,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
     // The last tiles' re-read DMAs may still be writing LDS: let them land before the
     // workgroup's LDS can be handed to another workgroup.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    slice_end<MB, NBW, WAVES>(p, rP, rC, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
+    slice_end<MB, NBW, F, WAVES>(p, rP, rC, rS, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown,
+                                 own);
     settle<MB, NBW, WAVES>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
 }
 
@@ -1174,19 +1272,40 @@ size_t workspace_for(const Config &c)
     return kCounterBytes + 2 * static_cast<size_t>(c.W) * slot;
 }
 
-template <int MB, int NBW>
+template <int MB, int NBW, class F>
 hipError_t launch(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_kernel<MB, NBW>), dim3(p.W), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((w4a16_gemm_kernel<MB, NBW, F>), dim3(p.W), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int WAVES, int STAGES>
+template <int WAVES, int STAGES, class F>
 hipError_t launch_wide(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_wide_kernel<WAVES, STAGES>), dim3(p.W), dim3(64 * WAVES), 0,
+    hipLaunchKernelGGL((w4a16_gemm_wide_kernel<WAVES, STAGES, F>), dim3(p.W), dim3(64 * WAVES), 0,
                        stream, p);
     return hipGetLastError();
+}
+
+// The kernel for this configuration and format.
+template <class F>
+int dispatch(const Config &c, const Params &p, hipStream_t s)
+{
+    hipError_t e;
+    switch (c.MB * 10 + c.NBW) {
+    case 11: e = launch<1, 1, F>(p, s); break;
+    case 12: e = launch<1, 2, F>(p, s); break;
+    case 14: e = launch<1, 4, F>(p, s); break;
+    case 21: e = launch<2, 1, F>(p, s); break;
+    case 22: e = launch<2, 2, F>(p, s); break;
+    case 24: e = launch<2, 4, F>(p, s); break;
+    case 41: e = launch<4, 1, F>(p, s); break;
+    case 42: e = launch<4, 2, F>(p, s); break;
+    case 44: e = launch<4, 4, F>(p, s); break;
+    case kWideMB * 10 + kWideNBW: e = launch_wide<kWaves, 2, F>(p, s); break;
+    default: return W4A16_EHIP;
+    }
+    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
 }
 
 }  // namespace
@@ -1206,14 +1325,17 @@ extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
     return W4A16_OK;
 }
 
-extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
-                          int M, int K, int N, void *workspace, void *stream)
+extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params,
+                             void *C, int M, int K, int N, int group, int zero_points,
+                             void *workspace, void *stream)
 {
-    if (!A || !packed || !scales || !C || !workspace)
+    if (!A || !packed || !params || !C || !workspace || (zero_points != 0 && zero_points != 1))
         return W4A16_EINVAL;
     int rc = check_gemm_shape(M, K, N);
     if (rc != W4A16_OK)
         return rc;
+    if (group != kGroup && group != K)
+        return W4A16_ESHAPE;
     DeviceInfo d;
     rc = current_device(&d);
     if (rc != W4A16_OK)
@@ -1222,10 +1344,12 @@ extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t 
         return W4A16_OK;
 
     const Config c = choose_config(M, K, N, d.cus);
+    // K = 128 makes the two scale granularities the same thing; take the grouped path
+    const bool col = group != kGroup;
     Params p;
     p.A = static_cast<const uint16_t *>(A);
     p.packed = reinterpret_cast<const u4 *>(packed);
-    p.scales = scales;
+    p.scales = params;
     p.C = static_cast<uint16_t *>(C);
     p.counters = static_cast<int *>(workspace);
     p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
@@ -1233,24 +1357,19 @@ extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t 
     p.K = K;
     p.N = N;
     p.G = c.G;
+    p.Gs = col ? 1 : c.G;
     p.P = c.P;
     p.W = c.W;
     p.T = c.T;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    switch (c.MB * 10 + c.NBW) {
-    case 11: e = launch<1, 1>(p, s); break;
-    case 12: e = launch<1, 2>(p, s); break;
-    case 14: e = launch<1, 4>(p, s); break;
-    case 21: e = launch<2, 1>(p, s); break;
-    case 22: e = launch<2, 2>(p, s); break;
-    case 24: e = launch<2, 4>(p, s); break;
-    case 41: e = launch<4, 1>(p, s); break;
-    case 42: e = launch<4, 2>(p, s); break;
-    case 44: e = launch<4, 4>(p, s); break;
-    case kWideMB * 10 + kWideNBW: e = launch_wide<kWaves, 2>(p, s); break;
-    default: return W4A16_EHIP;
-    }
-    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
+    if (zero_points)
+        return col ? dispatch<Fmt<true, true>>(c, p, s) : dispatch<Fmt<true, false>>(c, p, s);
+    return col ? dispatch<Fmt<false, true>>(c, p, s) : dispatch<FmtSym>(c, p, s);
+}
+
+extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
+                          int M, int K, int N, void *workspace, void *stream)
+{
+    return w4a16_gemm_ex(A, packed, scales, C, M, K, N, kGroup, 0, workspace, stream);
 }

@@ -35,10 +35,17 @@ size_t slabs_per_scale_group(size_t N)
     return N % 256 == 0 ? 4 : (N % 128 == 0 ? 2 : 1);
 }
 
-// Position in scales_out of scale (g, column 16j + c).
+// Position in scales_out of scale (g, column 16j + c); G = scale groups per column.
 size_t scale_index(size_t j, size_t g, size_t c, size_t G, size_t Q)
 {
     return (((j / Q) * G + g) * 16 + c) * Q + j % Q;
+}
+
+// Position in params_out (w4a16_pack_zp) of scale (g, column 16j + c); its zero term follows
+// Q places later: each column's Q scales, then its Q zero terms.
+size_t param_index(size_t j, size_t g, size_t c, size_t G, size_t Q)
+{
+    return (((j / Q) * G + g) * 16 + c) * 2 * Q + j % Q;
 }
 
 int check_shape(const void *a, const void *b, const void *c, const void *d, int K, int N,
@@ -46,27 +53,16 @@ int check_shape(const void *a, const void *b, const void *c, const void *d, int 
 {
     if (!a || !b || !c || !d || K < 0 || N < 0)
         return W4A16_EINVAL;
-    if (group != W4A16_GROUP || K == 0 || N == 0 || K % W4A16_GROUP || N % 16)
+    if (K == 0 || N == 0 || K % W4A16_GROUP || N % 16 || (group != W4A16_GROUP && group != K))
         return W4A16_ESHAPE;
     return W4A16_OK;
 }
 
-}  // namespace
-
-extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int group,
-                          uint32_t *packed_out, uint16_t *scales_out)
+// Reorder the codes into the block layout (shared by both pack calls).
+void pack_codes(const uint8_t *codes, size_t nk, size_t nn, uint32_t *packed_out)
 {
-    int rc = check_shape(codes, scales, packed_out, scales_out, K, N, group);
-    if (rc != W4A16_OK)
-        return rc;
-    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
-    for (size_t i = 0; i < nk * nn; ++i)
-        if (codes[i] > 15)
-            return W4A16_EINVAL;
-
     const size_t G = nk / W4A16_GROUP;
     const size_t slabs = nn / 16;
-    const size_t Q = slabs_per_scale_group(nn);
     for (size_t j = 0; j < slabs; ++j) {
         for (size_t g = 0; g < G; ++g) {
             uint32_t *blk = packed_out + (j * G + g) * 256;
@@ -80,23 +76,14 @@ extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, i
                     blk[4 * l + t] = w;
                 }
             }
-            for (size_t c = 0; c < 16; ++c)
-                scales_out[scale_index(j, g, c, G, Q)] = scales[g * nn + j * 16 + c];
         }
     }
-    return W4A16_OK;
 }
 
-extern "C" int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packed, int K, int N,
-                            int group, uint8_t *codes_out, uint16_t *scales_out)
+void unpack_codes(const uint32_t *packed, size_t nk, size_t nn, uint8_t *codes_out)
 {
-    int rc = check_shape(packed, scales_packed, codes_out, scales_out, K, N, group);
-    if (rc != W4A16_OK)
-        return rc;
-    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
     const size_t G = nk / W4A16_GROUP;
     const size_t slabs = nn / 16;
-    const size_t Q = slabs_per_scale_group(nn);
     for (size_t j = 0; j < slabs; ++j) {
         for (size_t g = 0; g < G; ++g) {
             const uint32_t *blk = packed + (j * G + g) * 256;
@@ -110,10 +97,111 @@ extern "C" int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packe
                             static_cast<uint8_t>((w >> (4 * kNibble[i])) & 0xF);
                 }
             }
-            for (size_t c = 0; c < 16; ++c)
-                scales_out[g * nn + j * 16 + c] = scales_packed[scale_index(j, g, c, G, Q)];
         }
     }
+}
+
+bool codes_valid(const uint8_t *v, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        if (v[i] > 15)
+            return false;
+    return true;
+}
+
+// fp16 bits of 1024 + z (exact: the spacing of fp16 at 1024 is 1).
+uint16_t zero_term(uint8_t z)
+{
+    return static_cast<uint16_t>(0x6400 | z);
+}
+
+}  // namespace
+
+extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int group,
+                          uint32_t *packed_out, uint16_t *scales_out)
+{
+    int rc = check_shape(codes, scales, packed_out, scales_out, K, N, group);
+    if (rc != W4A16_OK)
+        return rc;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    if (!codes_valid(codes, nk * nn))
+        return W4A16_EINVAL;
+    pack_codes(codes, nk, nn, packed_out);
+    const size_t Gs = nk / static_cast<size_t>(group);
+    const size_t Q = slabs_per_scale_group(nn);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < Gs; ++g)
+            for (size_t c = 0; c < 16; ++c)
+                scales_out[scale_index(j, g, c, Gs, Q)] = scales[g * nn + j * 16 + c];
+    return W4A16_OK;
+}
+
+extern "C" int w4a16_pack_zp(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                             int K, int N, int group, uint32_t *packed_out, uint16_t *params_out)
+{
+    int rc = check_shape(codes, scales, packed_out, params_out, K, N, group);
+    if (rc != W4A16_OK)
+        return rc;
+    if (!zeros)
+        return W4A16_EINVAL;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    const size_t Gs = nk / static_cast<size_t>(group);
+    if (!codes_valid(codes, nk * nn) || !codes_valid(zeros, Gs * nn))
+        return W4A16_EINVAL;
+    pack_codes(codes, nk, nn, packed_out);
+    const size_t Q = slabs_per_scale_group(nn);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < Gs; ++g)
+            for (size_t c = 0; c < 16; ++c) {
+                const size_t i = param_index(j, g, c, Gs, Q);
+                params_out[i] = scales[g * nn + j * 16 + c];
+                params_out[i + Q] = zero_term(zeros[g * nn + j * 16 + c]);
+            }
+    return W4A16_OK;
+}
+
+extern "C" int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packed, int K, int N,
+                            int group, uint8_t *codes_out, uint16_t *scales_out)
+{
+    int rc = check_shape(packed, scales_packed, codes_out, scales_out, K, N, group);
+    if (rc != W4A16_OK)
+        return rc;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    unpack_codes(packed, nk, nn, codes_out);
+    const size_t Gs = nk / static_cast<size_t>(group);
+    const size_t Q = slabs_per_scale_group(nn);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < Gs; ++g)
+            for (size_t c = 0; c < 16; ++c)
+                scales_out[g * nn + j * 16 + c] = scales_packed[scale_index(j, g, c, Gs, Q)];
+    return W4A16_OK;
+}
+
+extern "C" int w4a16_unpack_zp(const uint32_t *packed, const uint16_t *params, int K, int N,
+                               int group, uint8_t *codes_out, uint16_t *scales_out,
+                               uint8_t *zeros_out)
+{
+    int rc = check_shape(packed, params, codes_out, scales_out, K, N, group);
+    if (rc != W4A16_OK)
+        return rc;
+    if (!zeros_out)
+        return W4A16_EINVAL;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    const size_t Gs = nk / static_cast<size_t>(group);
+    const size_t Q = slabs_per_scale_group(nn);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < Gs; ++g)
+            for (size_t c = 0; c < 16; ++c)
+                if ((params[param_index(j, g, c, Gs, Q) + Q] & 0xFFF0) != 0x6400)
+                    return W4A16_EINVAL;          // not a zero term written by w4a16_pack_zp
+    unpack_codes(packed, nk, nn, codes_out);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < Gs; ++g)
+            for (size_t c = 0; c < 16; ++c) {
+                const size_t i = param_index(j, g, c, Gs, Q);
+                scales_out[g * nn + j * 16 + c] = params[i];
+                zeros_out[g * nn + j * 16 + c] = static_cast<uint8_t>(params[i + Q] & 0xF);
+            }
     return W4A16_OK;
 }
 
@@ -123,9 +211,9 @@ extern "C" const char *w4a16_status_string(int status)
     case W4A16_OK:
         return "ok";
     case W4A16_EINVAL:
-        return "invalid argument (null pointer, negative size or code above 15)";
+        return "invalid argument (null pointer, negative size, code or zero point above 15)";
     case W4A16_ESHAPE:
-        return "unsupported shape (group must be 128, K a positive multiple of 128, "
+        return "unsupported shape (group must be 128 or K, K a positive multiple of 128, "
                "N a positive multiple of 64)";
     case W4A16_EUNSUPPORTED:
         return "current HIP device is not a gfx950 GPU";

@@ -150,3 +150,91 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
     assert lib.w4a16_workspace_size(16, 1000, 1024, ctypes.byref(n)) == w4.ESHAPE
     assert lib.w4a16_workspace_size(16, 1024, 1024, None) == w4.EINVAL
     assert n.value == 7
+
+
+# ------------------------------------------------------------------ one scale per column, zero points
+
+def params_layout_reference(scales, zeros):
+    """w4a16_pack_zp's params exactly as include/w4a16.h states it: per column and group its
+    scale, then its zero term 0x6400 | z, grouped by Q slabs."""
+    Gs, N = scales.shape
+    Q = 4 if N % 256 == 0 else (2 if N % 128 == 0 else 1)
+    s = scales.view(np.uint16).reshape(Gs, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2)  # [u][g][c][b]
+    z = (0x6400 | zeros.astype(np.uint16)).reshape(Gs, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2)
+    return np.concatenate([s, z], axis=3).reshape(-1)
+
+
+@pytest.mark.parametrize("K,N,col", [(256, 64, False), (384, 256, False), (256, 128, True),
+                                     (512, 48, True), (128, 16, False)])
+def test_pack_zp_matches_documented_layout(K, N, col):
+    from workloads import draw_zeros
+    g = K if col else 128
+    _, q, s = draw(K, N, 1, seed=K + N, group=g)
+    z = draw_zeros(K, N, seed=K, group=g)
+    packed, params = w4.pack(q, s, group=g, zeros=z)
+    ref_p, _ = layout_reference(q, np.zeros((K // 128, N), np.float16))
+    assert np.array_equal(packed, ref_p)
+    assert np.array_equal(params.view(np.uint16), params_layout_reference(s, z))
+
+
+@pytest.mark.parametrize("K,N", [(256, 64), (640, 208), (1024, 512)])
+def test_column_scale_pack_round_trip_and_layout(K, N):
+    _, q, s = draw(K, N, 1, seed=K * 3 + N, group=K)
+    packed, sp = w4.pack(q, s, group=K)
+    Q = 4 if N % 256 == 0 else (2 if N % 128 == 0 else 1)
+    ref = s.view(np.uint16).reshape(1, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2).reshape(-1)
+    assert np.array_equal(sp.view(np.uint16), ref)
+    q2, s2 = w4.unpack(packed, sp, K, N, group=K)
+    assert np.array_equal(q2, q) and np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+
+
+@pytest.mark.parametrize("K,N,col", [(256, 64, False), (640, 208, True), (1024, 512, False)])
+def test_zero_point_pack_round_trip_is_bit_exact(K, N, col):
+    rng = np.random.default_rng(K + N)
+    g = K if col else 128
+    s = rng.uniform(0.005, 0.02, (K // g, N)).astype(np.float16)
+    for q in _patterns(K, N, rng):
+        for z in (rng.integers(0, 16, (K // g, N), dtype=np.uint8),
+                  np.zeros((K // g, N), np.uint8), np.full((K // g, N), 15, np.uint8)):
+            packed, params = w4.pack(q, s, group=g, zeros=z)
+            q2, s2, z2 = w4.unpack(packed, params, K, N, group=g, zero_points=True)
+            assert np.array_equal(q2, q) and np.array_equal(z2, z)
+            assert np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+
+
+def test_new_pack_calls_reject_bad_arguments():
+    lib = w4.library()
+    K, N = 256, 32
+    q = np.zeros((K, N), dtype=np.uint8)
+    s = np.ones((2, N), dtype=np.float16)
+    z = np.full((2, N), 8, dtype=np.uint8)
+    out = np.zeros(K * N // 8, dtype=np.uint32)
+    po = np.zeros(4 * N, dtype=np.float16)
+    P = lambda a: a.ctypes.data
+    assert lib.w4a16_pack_zp(P(q), P(s), None, K, N, 128, P(out), P(po)) == w4.EINVAL
+    assert lib.w4a16_pack_zp(P(q), P(s), P(z), K, N, 64, P(out), P(po)) == w4.ESHAPE
+    assert lib.w4a16_pack(P(q), P(s), K, N, 512, P(out), P(po)) == w4.ESHAPE      # not 128 or K
+    assert lib.w4a16_pack(P(q), P(s), K, N, K, P(out), P(po)) == w4.OK            # group = K
+    z[1, 3] = 16
+    assert lib.w4a16_pack_zp(P(q), P(s), P(z), K, N, 128, P(out), P(po)) == w4.EINVAL
+    # unpack_zp refuses parameters that were not written as zero terms
+    z[1, 3] = 2
+    assert lib.w4a16_pack_zp(P(q), P(s), P(z), K, N, 128, P(out), P(po)) == w4.OK
+    bad = po.copy()
+    bad.view(np.uint16)[1] = 0x3C00
+    qo = np.zeros((K, N), np.uint8)
+    so = np.zeros((2, N), np.float16)
+    zo = np.zeros((2, N), np.uint8)
+    assert lib.w4a16_unpack_zp(P(out), P(bad), K, N, 128, P(qo), P(so), P(zo)) == w4.EINVAL
+    assert lib.w4a16_unpack_zp(P(out), P(po), K, N, 128, P(qo), P(so), None) == w4.EINVAL
+
+
+def test_gemm_ex_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(16)
+    assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1024, 1024, 128, 2, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1024, 1024, 128, -1, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm_ex(None, d, d, d, 16, 1024, 1024, 128, 0, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1024, 1024, 256, 0, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1024, 1024, 0, 1, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1000, 1024, 1000, 0, d, None) == w4.ESHAPE

@@ -280,3 +280,106 @@ def _sampled_check(shape, seed=0, ncols=48):
                          ids=lambda sh: sh.name)
 def test_full_size_workloads_sampled(shape):
     _sampled_check(shape)
+
+
+# ------------------------------------------------------------------ other packed formats
+# One scale per column (group = K) and zero points per group and column (w4a16_pack_zp,
+# w4a16_gemm_ex), against the oracle with the same group and zero points.
+
+from workloads import draw_zeros  # noqa: E402
+
+FORMATS = {"column": (True, False), "zeros": (False, True), "column_zeros": (True, True)}
+
+
+class FmtWeights:
+    def __init__(self, q, s, group, zeros=None):
+        self.K, self.N = q.shape
+        self.group, self.zp = group, zeros is not None
+        packed, params = w4.pack(q, s, group=group, zeros=zeros)
+        self.packed, self.params = w4.to_device(packed, params)
+
+    def run(self, A, ws=None):
+        Ad = torch.from_numpy(np.ascontiguousarray(A)).cuda()
+        C = w4.gemm(Ad, self.packed, self.params, self.N, ws=ws, group=self.group,
+                    zero_points=self.zp)
+        torch.cuda.synchronize()
+        return C.cpu().numpy()
+
+
+def fmt_case(fmt, K, N, M, seed):
+    col, zp = FORMATS[fmt]
+    g = K if col else 128
+    A, q, s = draw(K, N, M, seed=seed, group=g)
+    z = draw_zeros(K, N, seed=seed, group=g) if zp else None
+    return A, q, s, g, z
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (16, 2048, 1024), (33, 1024, 320),
+                                   (64, 4096, 192), (130, 2048, 1024), (300, 1024, 768),
+                                   (16, 18432, 512), (128, 9216, 256), (5, 384, 64)])
+def test_formats_against_oracle(fmt, M, K, N):
+    A, q, s, g, z = fmt_case(fmt, K, N, M, seed=M + K + N)
+    C = FmtWeights(q, s, g, z).run(A)
+    check(C, oracle.gemm(A, q, s, group=g, zeros=z), f"{fmt} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("M", [3, 40, 129])
+def test_formats_one_hot_rows_are_bit_exact(fmt, M):
+    # row m is 1 at k_m: C[m, :] = fp16(s * (q[k_m] - z)) exactly (one rounding)
+    K, N = 384, 256
+    A, q, s, g, z = fmt_case(fmt, K, N, M, seed=60 + M)
+    A[:] = 0
+    ks = [(7 * m + 3) % K for m in range(M)]
+    for m, k in enumerate(ks):
+        A[m, k] = 1.0
+    C = FmtWeights(q, s, g, z).run(A)
+    for m, k in enumerate(ks):
+        zz = 8 if z is None else z[k // g].astype(np.float64)
+        w = s[k // g].astype(np.float64) * (q[k].astype(np.float64) - zz)
+        assert same(C[m], w.astype(np.float16)), (fmt, m, k)
+
+
+@pytest.mark.parametrize("col", [False, True])
+@pytest.mark.parametrize("M", [16, 64, 128])
+def test_code_equal_to_zero_point_gives_zero_on_gpu(col, M):
+    K, N = 1024, 512
+    g = K if col else 128
+    A, _, s = draw(K, N, M, seed=70, group=g)
+    z = draw_zeros(K, N, seed=70, group=g)
+    q = np.repeat(z, g, axis=0)
+    assert (bits(FmtWeights(q, s, g, z).run(A)) & 0x7FFF == 0).all()
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_formats_repeat_bit_for_bit_with_split_slices(fmt):
+    K, N, M = 18432, 512, 128
+    A, q, s, g, z = fmt_case(fmt, K, N, M, seed=71)
+    W = FmtWeights(q, s, g, z)
+    first = W.run(A)
+    check(first, oracle.gemm(A, q, s, group=g, zeros=z), f"{fmt} K={K} N={N} M={M}")
+    for _ in range(2):
+        assert np.array_equal(bits(W.run(A, ws=w4.new_workspace(M, K, N))), bits(first))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_formats_full_size_72kx18k_sampled(fmt):
+    K, N = LARGE.shapes[0].K, LARGE.shapes[0].N
+    Ms = [1, 16, 64, 128]
+    A, q, s, g, z = fmt_case(fmt, K, N, max(Ms), seed=0)
+    W = FmtWeights(q, s, g, z)
+    rng = np.random.default_rng(72)
+    cols = np.unique(np.concatenate([[0, 15, 16, N - 1], rng.choice(N, 40, replace=False)]))
+    qc, sc = np.ascontiguousarray(q[:, cols]), np.ascontiguousarray(s[:, cols])
+    zc = None if z is None else np.ascontiguousarray(z[:, cols])
+    del q
+    gc.collect()
+    ref = oracle.gemm(A, qc, sc, group=g, zeros=zc)
+    for M in Ms:
+        C = W.run(A[:M])
+        assert np.isfinite(C).all()
+        check(C[:, cols], ref[:M], f"{fmt} 72k x 18k M={M} ({len(cols)} sampled columns)")
+    del W
+    torch.cuda.empty_cache()
