@@ -64,6 +64,13 @@ def algorithmic_bytes(M, K, N):
     return 2 * M * K + K * N // 2 + K * N // 64 + 2 * M * N
 
 
+def format_bytes(M, K, N, group, zero_points):
+    """Algorithmic bytes of one call in a given packed format: A, codes, the stored per-group
+    parameters (fp16 scale, plus the fp16 zero term with zero points) and C."""
+    per_col = (K // group) * 2 * (2 if zero_points else 1)
+    return 2 * M * K + K * N // 2 + per_col * N + 2 * M * N
+
+
 def fp16_weight_bytes(M, K, N):
     return 2 * M * K + 2 * K * N + 2 * M * N
 
@@ -92,6 +99,53 @@ def cpu_baseline(A, q, s, Ms, ncols, nthreads):
                       f"(the same draws as the GPU run); {dt:.1f} s of CPU time"}
 
 
+FORMATS = (("column", True, False), ("zeros", False, True), ("column_zeros", True, True))
+FORMAT_MS = (1, 16, 64, 128)
+
+
+def time_formats(w4, torch, dev, A, Ad, q, s, K, N, steps, warmup, copies, stream, sym_us):
+    """Per-call time of the other packed formats on the same codes: one scale per column
+    (group = K; the first row of scale groups serves as that column's scale), zero points per
+    group and column, and both.  Same launch path and event timing as the main sweep."""
+    from workloads import draw_zeros
+    rows = []
+    for name, col, zp in FORMATS:
+        group = K if col else GROUP
+        sf = np.ascontiguousarray(s[:1]) if col else s
+        z = draw_zeros(K, N, seed=0, group=group) if zp else None
+        packed, params = w4.pack(q, sf, group=group, zeros=z)
+        pd, sd = w4.to_device(packed, params, dev)
+        del packed, params
+        cps = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(copies - 1)]
+        for M in FORMAT_MS:
+            out = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = w4.new_workspace(M, K, N, dev)
+            evs = []
+            for i in range(warmup + steps):
+                p_, s_ = cps[i % len(cps)]
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                w4.gemm(Ad[:M], p_, s_, N, out=out, ws=ws, stream=stream, group=group,
+                        zero_points=zp)
+                e1.record(stream)
+                if i >= warmup:
+                    evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+            D = format_bytes(M, K, N, group, zp)
+            rows.append({"format": name, "group": group, "zero_points": zp, "M": M,
+                         "us": round(us, 2), "GBps": round(D / us / 1e3, 1),
+                         "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4),
+                         "TFLOPs": round(flops(M, K, N) / us / 1e6, 2),
+                         "time_vs_group128_symmetric": round(us / sym_us[M], 3)})
+            log(f"{name:13s} M={M:4d} {us:8.1f} us  {D / us / 1e3:7.0f} GB/s  "
+                f"x{us / sym_us[M]:.3f} of the group-128 symmetric time")
+        del cps, pd, sd
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +155,8 @@ def main():
                     help="columns of the CPU-baseline sample (0 skips it)")
     ap.add_argument("--copies", type=int, default=2,
                     help="weight copies rotated between calls so no call hits the MALL")
+    ap.add_argument("--format-steps", type=int, default=20,
+                    help="timed calls per M for each other packed format (0 skips them)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
@@ -214,6 +270,11 @@ def main():
                 "mean_launch_us": round(us, 2)}
 
     kernels = [roof(*k) for k in KERNELS]
+    formats = None
+    if args.format_steps > 0:
+        formats = time_formats(w4, torch, dev, A, Ad, q, s, K, N, args.format_steps,
+                               max(2, args.warmup // 4), args.copies, stream,
+                               {row["M"]: row["us"] for row in sweep})
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -225,6 +286,7 @@ def main():
         "roofline": kernels[0],
         "roofline_by_kernel": kernels,
         "sweep": sweep,
+        "formats": formats,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }

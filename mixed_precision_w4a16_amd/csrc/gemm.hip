@@ -259,44 +259,65 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
 
 // Per-column parameters of a wave's NBW slabs at one K step (its "scale group" sblk):
 // w4a16_pack stores the NBW scales of a column side by side, w4a16_pack_zp the NBW scales then
-// the NBW zero terms, so one load per lane brings all of them: 2 NBW or 4 NBW bytes per
-// column.  The symmetric format with NBW = 1 loads the aligned dword holding its column's
+// the NBW zero terms (ZP), so one load per lane brings what a step needs: 2 NBW or 4 NBW bytes
+// per column.  The symmetric format with NBW = 1 loads the aligned dword holding its column's
 // scale and its neighbour's.  (A 16-bit load result would be re-copied across the loop
-// back-edge.)
-template <int NBW, bool ZP>
-struct ParamRegs {
-    static constexpr int n = ZP ? NBW : (NBW >= 2 ? NBW / 2 : 1);
+// back-edge.)  With one scale per column and zero points the K loop needs only the zero terms
+// and the epilogue only the scales, so those loads bring just that part: a dword of a load
+// whose value is never read would be handed to the next instruction that needs a register,
+// and writing a register a load has not yet filled waits for every load in flight.
+enum class Part { Scales, Both, Zeros };
+
+template <int NBW, bool ZP, Part PT>
+struct PRegs {
+    static constexpr int n = PT == Part::Both ? NBW : (NBW >= 2 ? NBW / 2 : 1);
 };
 
-template <int NBW, bool ZP>
-__device__ __forceinline__ void load_params(__amdgpu_buffer_rsrc_t rS, int lane, uint32_t sblk,
-                                            uint32_t (&pr)[ParamRegs<NBW, ZP>::n])
+// What the K loop loads per step for format F (nothing, if kTileParams is false).
+template <class F>
+constexpr Part tile_part()
 {
+    return F::ZP ? (F::COL ? Part::Zeros : Part::Both) : Part::Scales;
+}
+
+template <int NBW, class F>
+using TileRegs = PRegs<NBW, F::ZP, tile_part<F>()>;
+
+template <int NBW, bool ZP, Part PT>
+__device__ __forceinline__ void load_params(__amdgpu_buffer_rsrc_t rS, int lane, uint32_t sblk,
+                                            uint32_t (&pr)[PRegs<NBW, ZP, PT>::n])
+{
+    static_assert(ZP || PT == Part::Scales, "the stream without zero points holds scales only");
     constexpr uint32_t per_group = 16u * 2u * (ZP ? 2 * NBW : (NBW >= 2 ? NBW : 1));
     const uint32_t so = __builtin_amdgcn_readfirstlane(sblk * per_group);
-    constexpr int bytes = 4 * ParamRegs<NBW, ZP>::n;               // per lane
-    if constexpr (bytes == 16) {
-        const auto v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rS, (lane & 15) * 16, so, 0));
+    constexpr int n = PRegs<NBW, ZP, PT>::n;                       // dwords per lane
+    uint32_t off;
+    if constexpr (ZP)      // column c at 4 NBW c bytes; its zero terms 2 NBW bytes further
+        off = (lane & 15) * (4 * NBW) + (PT == Part::Zeros && NBW >= 2 ? 2 * NBW : 0);
+    else if constexpr (NBW >= 2)
+        off = (lane & 15) * (2 * NBW);
+    else
+        off = (lane & 14) * 2;
+    if constexpr (n == 4) {
+        const auto v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, so, 0));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             pr[i] = v[i];
-    } else if constexpr (bytes == 8) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, (lane & 15) * 8, so, 0);
+    } else if constexpr (n == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, off, so, 0);
         pr[0] = v[0];
         pr[1] = v[1];
-    } else if constexpr (ZP || NBW == 2) {
-        pr[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 15) * 4, so, 0);
     } else {
-        pr[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, (lane & 14) * 2, so, 0);
+        pr[0] = __builtin_amdgcn_raw_buffer_load_b32(rS, off, so, 0);
     }
 }
 
-// fp16 bits of slab b's scale for this lane's column.
-template <int NBW, bool ZP>
-__device__ __forceinline__ uint16_t scale_bits(const uint32_t (&pr)[ParamRegs<NBW, ZP>::n],
+// fp16 bits of slab b's scale for this lane's column (the scales come first in a load).
+template <int NBW, bool ZP, Part PT>
+__device__ __forceinline__ uint16_t scale_bits(const uint32_t (&pr)[PRegs<NBW, ZP, PT>::n],
                                                int b, int lane)
 {
+    static_assert(PT != Part::Zeros, "no scales in this load");
     if constexpr (ZP || NBW >= 2)
         return static_cast<uint16_t>(pr[b >> 1] >> ((b & 1) * 16));
     else
@@ -304,13 +325,14 @@ __device__ __forceinline__ uint16_t scale_bits(const uint32_t (&pr)[ParamRegs<NB
 }
 
 // Decode constants of slab b: (1024 + z, -(64 + z)) from the stored zero term, or those of
-// z = 8.
-template <int NBW, bool ZP>
-__device__ __forceinline__ void zero_consts(const uint32_t (&pr)[ParamRegs<NBW, ZP>::n], int b,
+// z = 8.  The zero term is half NBW + b of a load of both parts, half b of a zero-term load
+// (NBW >= 2), the upper half of the scale-and-zero dword (NBW = 1).
+template <int NBW, bool ZP, Part PT>
+__device__ __forceinline__ void zero_consts(const uint32_t (&pr)[PRegs<NBW, ZP, PT>::n], int b,
                                             h2 &zsub, h2 &zadd)
 {
     if constexpr (ZP) {
-        const int i = NBW + b;
+        const int i = PT == Part::Both ? NBW + b : (NBW >= 2 ? b : 1);
         const _Float16 zt =
             __builtin_bit_cast(_Float16, static_cast<uint16_t>(pr[i >> 1] >> ((i & 1) * 16)));
         zsub = h2{zt, zt};
@@ -331,7 +353,7 @@ __device__ __forceinline__ void zero_consts(const uint32_t (&pr)[ParamRegs<NBW, 
 template <int MB, int NBW, class F>
 __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
                                        int G, int lane, uint32_t wblk, uint32_t sblk,
-                                       u4 (&wq)[NBW], uint32_t (&pr)[ParamRegs<NBW, F::ZP>::n])
+                                       u4 (&wq)[NBW], uint32_t (&pr)[TileRegs<NBW, F>::n])
 {
     constexpr int policy = MB <= 2 ? kNonTemporal : 0;
 #pragma unroll
@@ -341,7 +363,7 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
             u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, policy));
     }
     if constexpr (F::kTileParams)
-        load_params<NBW, F::ZP>(rS, lane, sblk, pr);
+        load_params<NBW, F::ZP, tile_part<F>()>(rS, lane, sblk, pr);
 }
 
 // Where the scale is applied.  One scale per column: not in the K loop at all; the fp32 sum
@@ -361,7 +383,7 @@ struct ScaleMode {
 
 template <int MB, int NBW, class F>
 __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4 (&wq)[NBW],
-                                             const uint32_t (&pr)[ParamRegs<NBW, F::ZP>::n],
+                                             const uint32_t (&pr)[TileRegs<NBW, F>::n],
                                              f4 (&acc)[MB][NBW], uint32_t mlo, uint32_t mhi,
                                              uint32_t magic)
 {
@@ -372,14 +394,15 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         if constexpr (ScaleMode<MB, F>::kWeights) {
-            const _Float16 sh = __builtin_bit_cast(_Float16, scale_bits<NBW, F::ZP>(pr, b, lane));
+            const _Float16 sh =
+                __builtin_bit_cast(_Float16, scale_bits<NBW, F::ZP, tile_part<F>()>(pr, b, lane));
             s2[b] = h2{sh, sh};
             asm volatile("" : "+v"(s2[b]));
         } else if constexpr (ScaleMode<MB, F>::kPartial) {
-            sf[b] = half_bits_to_float(scale_bits<NBW, F::ZP>(pr, b, lane));
+            sf[b] = half_bits_to_float(scale_bits<NBW, F::ZP, tile_part<F>()>(pr, b, lane));
             asm volatile("" : "+v"(sf[b]));
         }
-        zero_consts<NBW, F::ZP>(pr, b, zsub[b], zadd[b]);
+        zero_consts<NBW, F::ZP, tile_part<F>()>(pr, b, zsub[b], zadd[b]);
         if constexpr (F::ZP) {
             asm volatile("" : "+v"(zsub[b]));
             asm volatile("" : "+v"(zadd[b]));
@@ -611,11 +634,13 @@ __device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_
 {
     if constexpr (F::COL) {
         const long long sl = sigma / p.P;
-        uint32_t pr[ParamRegs<NBW, F::ZP>::n];
-        load_params<NBW, F::ZP>(rS, lane, static_cast<uint32_t>(sl) * WAVES + wave, pr);
+        uint32_t pr[PRegs<NBW, F::ZP, Part::Scales>::n];
+        load_params<NBW, F::ZP, Part::Scales>(rS, lane, static_cast<uint32_t>(sl) * WAVES + wave,
+                                              pr);
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
-            const float sc = half_bits_to_float(scale_bits<NBW, F::ZP>(pr, b, lane));
+            const float sc =
+                half_bits_to_float(scale_bits<NBW, F::ZP, Part::Scales>(pr, b, lane));
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 acc[mb][b] *= sc;
@@ -809,7 +834,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     // is not needed yet: each weight tile has one whole tile of compute to arrive in.
     u4 ar[MB];
     u4 wq0[NBW], wq1[NBW];
-    uint32_t sc0[ParamRegs<NBW, F::ZP>::n], sc1[ParamRegs<NBW, F::ZP>::n];
+    uint32_t sc0[TileRegs<NBW, F>::n], sc1[TileRegs<NBW, F>::n];
     int st_cp = 0, st_st = 1;             // ring stages being computed from / stored to
     auto next_stage = [](int x) { return x == TL::kStages - 1 ? 0 : x + 1; };
 
@@ -950,7 +975,7 @@ __device__ __forceinline__ void wide_dma_a(const Params &p, __amdgpu_buffer_rsrc
 template <class F>
 __device__ __forceinline__ void wide_compute(const u4 *stage, int lane,
                                              const u4 (&wq)[kWideNBW],
-                                             const uint32_t (&pr)[ParamRegs<kWideNBW, F::ZP>::n],
+                                             const uint32_t (&pr)[TileRegs<kWideNBW, F>::n],
                                              f4 (&acc)[kWideMB][kWideNBW], uint32_t mlo,
                                              uint32_t mhi, uint32_t magic)
 {
@@ -959,11 +984,12 @@ __device__ __forceinline__ void wide_compute(const u4 *stage, int lane,
     for (int b = 0; b < kWideNBW; ++b) {
         if constexpr (!F::COL) {
             const _Float16 sh =
-                __builtin_bit_cast(_Float16, scale_bits<kWideNBW, F::ZP>(pr, b, lane));
+                __builtin_bit_cast(_Float16,
+                                   scale_bits<kWideNBW, F::ZP, tile_part<F>()>(pr, b, lane));
             s2[b] = h2{sh, sh};
             asm volatile("" : "+v"(s2[b]));
         }
-        zero_consts<kWideNBW, F::ZP>(pr, b, zsub[b], zadd[b]);
+        zero_consts<kWideNBW, F::ZP, tile_part<F>()>(pr, b, zsub[b], zadd[b]);
         if constexpr (F::ZP) {
             asm volatile("" : "+v"(zsub[b]));
             asm volatile("" : "+v"(zadd[b]));
@@ -1088,7 +1114,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
     // Weight buffers, one per stage: tile i uses stage and buffer i % STAGES.
     u4 wq[STAGES][NBW];
-    uint32_t sc[STAGES][ParamRegs<NBW, F::ZP>::n];
+    uint32_t sc[STAGES][TileRegs<NBW, F>::n];
 
     // Issue the loads of the tile at the load position into stage / buffer k, the DMAs first
     // (the asm and scheduling barriers keep that order), and move the cursor on.
