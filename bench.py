@@ -12,6 +12,11 @@ the eight calls and about half the sweep's time; HBM-bound, so achieved = its al
 bytes per launch / its mean launch time.  `roofline_by_kernel` gives the same for every kernel
 of the sweep, the 128-row (M = 128) kernel against the fp16 MFMA peak.
 
+Also reported, outside `value`: `formats`, the per-call time of the other packed formats
+(one scale per column, zero points, both) on the same weight at M = 1, 16, 64, 128, timed
+call by call alternately with the group-128 symmetric format; `repack`, the load-time
+conversion of a checkpoint-style packed weight of the same size into the multiply's layout.
+
 Prints one JSON line on stdout.  Single GPU only.
 """
 from __future__ import annotations
@@ -103,12 +108,14 @@ FORMATS = (("column", True, False), ("zeros", False, True), ("column_zeros", Tru
 FORMAT_MS = (1, 16, 64, 128)
 
 
-def time_formats(w4, torch, dev, A, Ad, q, s, K, N, steps, warmup, copies, stream, sym_us):
+def time_formats(w4, torch, dev, Ad, q, s, K, N, steps, warmup, copies, stream, sym):
     """Per-call time of the other packed formats on the same codes: one scale per column
     (group = K; the first row of scale groups serves as that column's scale), zero points per
-    group and column, and both.  Same launch path and event timing as the main sweep."""
+    group and column, and both.  The calls of all four formats (the group-128 symmetric one
+    included, `sym` = its rotated weight copies) alternate call by call, so every format is
+    timed in the same clock and power state."""
     from workloads import draw_zeros
-    rows = []
+    fmts = [("group128_symmetric", GROUP, False, sym)]
     for name, col, zp in FORMATS:
         group = K if col else GROUP
         sf = np.ascontiguousarray(s[:1]) if col else s
@@ -116,12 +123,15 @@ def time_formats(w4, torch, dev, A, Ad, q, s, K, N, steps, warmup, copies, strea
         packed, params = w4.pack(q, sf, group=group, zeros=z)
         pd, sd = w4.to_device(packed, params, dev)
         del packed, params
-        cps = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(copies - 1)]
-        for M in FORMAT_MS:
-            out = torch.empty((M, N), dtype=torch.float16, device=dev)
-            ws = w4.new_workspace(M, K, N, dev)
-            evs = []
-            for i in range(warmup + steps):
+        fmts.append((name, group, zp, [(pd, sd)] + [(pd.clone(), sd.clone())
+                                                     for _ in range(copies - 1)]))
+    rows = []
+    for M in FORMAT_MS:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = w4.new_workspace(M, K, N, dev)
+        evs = {name: [] for name, *_ in fmts}
+        for i in range(warmup + steps):
+            for name, group, zp, cps in fmts:
                 p_, s_ = cps[i % len(cps)]
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -130,18 +140,57 @@ def time_formats(w4, torch, dev, A, Ad, q, s, K, N, steps, warmup, copies, strea
                         zero_points=zp)
                 e1.record(stream)
                 if i >= warmup:
-                    evs.append((e0, e1))
-            torch.cuda.synchronize()
-            us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+                    evs[name].append((e0, e1))
+        torch.cuda.synchronize()
+        us = {name: float(np.mean([a.elapsed_time(b) for a, b in e])) * 1e3
+              for name, e in evs.items()}
+        for name, group, zp, _ in fmts:
             D = format_bytes(M, K, N, group, zp)
             rows.append({"format": name, "group": group, "zero_points": zp, "M": M,
-                         "us": round(us, 2), "GBps": round(D / us / 1e3, 1),
-                         "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4),
-                         "TFLOPs": round(flops(M, K, N) / us / 1e6, 2),
-                         "time_vs_group128_symmetric": round(us / sym_us[M], 3)})
-            log(f"{name:13s} M={M:4d} {us:8.1f} us  {D / us / 1e3:7.0f} GB/s  "
-                f"x{us / sym_us[M]:.3f} of the group-128 symmetric time")
-        del cps, pd, sd
+                         "us": round(us[name], 2), "GBps": round(D / us[name] / 1e3, 1),
+                         "hbm_frac": round(D / us[name] / 1e3 / HBM_PEAK_GBPS, 4),
+                         "TFLOPs": round(flops(M, K, N) / us[name] / 1e6, 2),
+                         "time_vs_group128_symmetric":
+                             round(us[name] / us["group128_symmetric"], 3)})
+            log(f"{name:19s} M={M:4d} {us[name]:8.1f} us  {D / us[name] / 1e3:7.0f} GB/s  "
+                f"x{us[name] / us['group128_symmetric']:.3f}")
+    del fmts
+    torch.cuda.empty_cache()
+    return rows
+
+
+def time_repack(w4, torch, dev, K, N, steps, stream):
+    """Load-time repack (w4a16_repack) of the same-sized weight with zero points, from words
+    packed along K and along N: random words (every 32-bit word is 8 valid codes).  Bytes:
+    codes read and written (K*N/2 each), scales and packed zero points read, scales and zero
+    terms written."""
+    G = K // GROUP
+    g = torch.Generator(device=dev).manual_seed(0)
+    rows = []
+    for name, layout, shape in (("along_k", w4.PACKED_ALONG_K, (K // 8, N)),
+                                ("along_n", w4.PACKED_ALONG_N, (K, N // 8))):
+        qw = torch.randint(-2**31, 2**31 - 1, shape, dtype=torch.int32, device=dev, generator=g)
+        qz = torch.randint(-2**31, 2**31 - 1, (G, N // 8), dtype=torch.int32, device=dev,
+                           generator=g)
+        sc = (torch.rand((G, N), device=dev, generator=g) * 0.015 + 0.005).half()
+        order = None if layout == w4.PACKED_ALONG_K else [0, 2, 4, 6, 1, 3, 5, 7]
+        evs = []
+        for i in range(2 + steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            out = w4.repack(qw, sc, K, N, layout, qzeros=qz, order=order, stream=stream)
+            e1.record(stream)
+            if i >= 2:
+                evs.append((e0, e1))
+            del out
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        D = K * N // 2 * 2 + G * N * 2 + G * N // 2 + G * N * 4
+        rows.append({"source": name, "zero_points": True, "us": round(us, 1),
+                     "GBps": round(D / us / 1e3, 1), "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4)})
+        log(f"repack {name}: {us:8.1f} us  {D / us / 1e3:7.0f} GB/s")
+        del qw, qz, sc
         torch.cuda.empty_cache()
     return rows
 
@@ -270,11 +319,11 @@ def main():
                 "mean_launch_us": round(us, 2)}
 
     kernels = [roof(*k) for k in KERNELS]
+    repack = time_repack(w4, torch, dev, K, N, 10, stream) if args.format_steps > 0 else None
     formats = None
     if args.format_steps > 0:
-        formats = time_formats(w4, torch, dev, A, Ad, q, s, K, N, args.format_steps,
-                               max(2, args.warmup // 4), args.copies, stream,
-                               {row["M"]: row["us"] for row in sweep})
+        formats = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
+                               max(2, args.warmup // 4), args.copies, stream, copies)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -287,6 +336,7 @@ def main():
         "roofline_by_kernel": kernels,
         "sweep": sweep,
         "formats": formats,
+        "repack": repack,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }

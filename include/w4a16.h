@@ -41,6 +41,10 @@ extern "C" {
 #define W4A16_GROUP 128           /* rows per scale group; group = K (one per column) also works */
 #define W4A16_N_ALIGN 64          /* N must be a multiple of this */
 
+/* Source arrangements for w4a16_repack (8 codes per 32-bit word). */
+#define W4A16_PACKED_ALONG_K 0    /* word (r, n) of [K/8][N]: rows 8r..8r+7 of column n */
+#define W4A16_PACKED_ALONG_N 1    /* word (k, c) of [K][N/8]: columns 8c..8c+7 of row k */
+
 typedef enum {
     W4A16_OK = 0,
     W4A16_EINVAL = -1,            /* null pointer, negative size, a code or zero point
@@ -175,6 +179,45 @@ int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, vo
 int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params, void *C,
                   int M, int K, int N, int group, int zero_points, void *workspace,
                   void *stream);
+
+/*
+ * Device-side load-time conversion of checkpoint-style packed tensors into the layouts of
+ * w4a16_pack (qzeros NULL) or w4a16_pack_zp (device, asynchronous on `stream`).  The pages'
+ * load step that turns a GPTQ/AWQ-style checkpoint into the kernel's layout: it only moves
+ * codes, it never changes one (deep-dive page, section "直接生成 MMA 所需的寄存器 fragment", and
+ * the deployment section on checkpoint formats, which differ in nibble order, scale
+ * arrangement and zero-point convention).
+ *
+ *   qweight    [in]  device uint32, the codes, 8 per word:
+ *                    W4A16_PACKED_ALONG_K: [K/8][N], word (r, n) holds rows 8r..8r+7 of
+ *                      column n, row 8r + i in bits 4i..4i+3;
+ *                    W4A16_PACKED_ALONG_N: [K][N/8], word (k, c) holds columns 8c..8c+7 of
+ *                      row k, column 8c + order[i] in bits 4i..4i+3.
+ *   src_layout [in]  W4A16_PACKED_ALONG_K or W4A16_PACKED_ALONG_N
+ *   order      [in]  host uint8[8], a permutation of 0..7, or NULL for 0, 1, ..., 7: the
+ *                    column offset that nibble i holds in every word packed along N
+ *                    (qweight with W4A16_PACKED_ALONG_N, and qzeros)
+ *   scales     [in]  device fp16 bits [(K/group)][N], row-major (g, n)
+ *   qzeros     [in]  device uint32 [(K/group)][N/8] packed along N (word (g, c): zero points
+ *                    z of columns 8c..8c+7 at group g, each a code 0..15 taken as stored),
+ *                    or NULL for the symmetric format (z = 8)
+ *   group      [in]  128, or K for one scale per column
+ *   packed_out [out] device uint32 [K*N/8]: exactly w4a16_pack's packed_out for these codes
+ *   params_out [out] device fp16 bits: qzeros NULL: [(K/group)*N], w4a16_pack's scales_out;
+ *                    else [2*(K/group)*N], w4a16_pack_zp's params_out
+ * Then call w4a16_gemm_ex with the same group and zero_points = (qzeros != NULL).
+ *
+ * Outputs must not overlap the inputs.  Alignment: packed_out 16 bytes, qweight and qzeros
+ * 4, scales and params_out 2 (any hipMalloc pointer is aligned).
+ * Errors: W4A16_EINVAL (null pointer other than order / qzeros, negative size, unknown
+ * src_layout, order not a permutation of 0..7, misaligned pointer), W4A16_ESHAPE (as
+ * w4a16_pack: group not 128 or K, K not a positive multiple of 128, N not a positive multiple
+ * of 16; or a grid too large to launch), W4A16_EUNSUPPORTED (current device is not gfx950),
+ * W4A16_EHIP (launch failure).  Arguments are checked before any device call.
+ */
+int w4a16_repack(const uint32_t *qweight, int src_layout, const uint8_t *order,
+                 const uint16_t *scales, const uint32_t *qzeros, int K, int N, int group,
+                 uint32_t *packed_out, uint16_t *params_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,8 @@ when the compiled library is missing; there is no fallback path.
 
 Other formats: pack(codes, scales, group=K) for one scale per column, and
 pack(codes, scales, group, zeros=z) for zero points; pass the same group / zero_points to
-gemm.
+gemm.  repack(...) converts checkpoint-style packed tensors already on the GPU into the same
+layout on the GPU.
 """
 from __future__ import annotations
 
@@ -57,10 +58,14 @@ _lib.w4a16_unpack_zp.argtypes = [_p, _p, _i, _i, _i, _p, _p, _p]
 _lib.w4a16_unpack_zp.restype = _i
 _lib.w4a16_gemm_ex.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]
 _lib.w4a16_gemm_ex.restype = _i
+_lib.w4a16_repack.argtypes = [_p, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p]
+_lib.w4a16_repack.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
 EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
-            "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex")
+            "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
+            "w4a16_repack")
 
 
 class W4A16Error(RuntimeError):
@@ -212,3 +217,47 @@ def gemm(A, packed, params, N: int, out=None, ws=None, stream=None, group: int =
                                                        N, group, int(bool(zero_points)),
                                                        ws.data_ptr(), stream.cuda_stream))
     return out
+
+
+def repack(qweight, scales, K: int, N: int, layout: int, group: int = GROUP, qzeros=None,
+           order=None, stream=None):
+    """Device-side load-time conversion (w4a16_repack) -> (packed int32 [K*N/8], params fp16).
+
+    qweight: int32 CUDA tensor holding the uint32 words, [K/8, N] for PACKED_ALONG_K or
+    [K, N/8] for PACKED_ALONG_N.  scales: fp16 [K/group, N].  qzeros: optional int32
+    [K/group, N/8] packed along N.  order: optional 8 column offsets, nibble i of a word packed
+    along N holding offset order[i].  Pass the same group and zero_points=(qzeros is not None)
+    to gemm.
+    """
+    import torch
+    dev = qweight.device
+    want = (K // 8, N) if layout == PACKED_ALONG_K else (K, N // 8)
+    if (qweight.dtype != torch.int32 or not qweight.is_cuda or not qweight.is_contiguous()
+            or tuple(qweight.shape) != want):
+        raise ValueError(f"qweight must be a contiguous int32 CUDA tensor of shape {want}")
+    if (not group or K % group or scales.dtype != torch.float16 or scales.device != dev
+            or not scales.is_contiguous() or tuple(scales.shape) != (K // group, N)):
+        raise ValueError("scales must be a contiguous fp16 tensor [K/group, N] on qweight's device")
+    zp = 0
+    if qzeros is not None:
+        if (qzeros.dtype != torch.int32 or qzeros.device != dev or not qzeros.is_contiguous()
+                or tuple(qzeros.shape) != (K // group, N // 8)):
+            raise ValueError("qzeros must be a contiguous int32 tensor [K/group, N/8] on "
+                             "qweight's device")
+        zp = qzeros.data_ptr()
+    order_buf = None
+    if order is not None:
+        order_buf = np.ascontiguousarray(order, dtype=np.uint8)
+        if order_buf.shape != (8,):
+            raise ValueError("order must hold 8 entries")
+    packed = torch.empty(K * N // 8, dtype=torch.int32, device=dev)
+    params = torch.empty((2 if qzeros is not None else 1) * (K // group) * N,
+                         dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        _check("w4a16_repack", _lib.w4a16_repack(
+            qweight.data_ptr(), int(layout),
+            None if order_buf is None else order_buf.ctypes.data, scales.data_ptr(), zp or None,
+            K, N, group, packed.data_ptr(), params.data_ptr(), stream.cuda_stream))
+    return packed, params

@@ -59,6 +59,7 @@
 #include <type_traits>
 
 #include "w4a16.h"
+#include "device.h"
 
 namespace {
 
@@ -1194,36 +1195,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
 // ------------------------------------------------------------------------------- host side
 
-struct DeviceInfo {
-    bool queried = false;
-    bool gfx950 = false;
-    int cus = 0;
-};
-
-std::mutex g_dev_mu;
-DeviceInfo g_dev[64];
-
-int current_device(DeviceInfo *out)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return W4A16_EHIP;
-    std::lock_guard<std::mutex> lk(g_dev_mu);
-    DeviceInfo &d = g_dev[dev];
-    if (!d.queried) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
-            return W4A16_EHIP;
-        const char *a = prop.gcnArchName;
-        d.gfx950 = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
-                   a[5] == '0' && (a[6] == '\0' || a[6] == ':');
-        d.cus = prop.multiProcessorCount;
-        d.queried = true;
-    }
-    *out = d;
-    return d.gfx950 ? W4A16_OK : W4A16_EUNSUPPORTED;
-}
-
 struct Config {
     int MB, NBW;     // M sub-tiles of 16 rows; 16-column slabs per wave
     int waves;       // waves per workgroup
@@ -1335,6 +1306,39 @@ int dispatch(const Config &c, const Params &p, hipStream_t s)
 }
 
 }  // namespace
+
+namespace w4a16_detail {
+
+namespace {
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+}  // namespace
+
+int current_device(DeviceInfo *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return W4A16_EHIP;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.queried) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return W4A16_EHIP;
+        const char *a = prop.gcnArchName;
+        d.gfx950 = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
+                   a[5] == '0' && (a[6] == '\0' || a[6] == ':');
+        d.cus = prop.multiProcessorCount;
+        d.queried = true;
+    }
+    *out = d;
+    return d.gfx950 ? W4A16_OK : W4A16_EUNSUPPORTED;
+}
+
+}  // namespace w4a16_detail
+
+using w4a16_detail::current_device;
+using w4a16_detail::DeviceInfo;
 
 extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
 {

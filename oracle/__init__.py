@@ -11,6 +11,8 @@ Two independent implementations live here:
   FP32 accumulators, FP16 only at write-out).  ``mode="f64"`` is the diagnostic truth.
 * ``exact_gemm`` below: exact integer arithmetic on the dyadic values, correctly rounded to
   fp16 by its own routine.  It is slow and only for tiny shapes; it pins the C code.
+* ``decode_along_k`` / ``decode_along_n``: checkpoint-style packed words (8 codes per word,
+  along K or along N in a given nibble order) to codes, what the load-time repack must move.
 
 The operation (MARLIN paper, arXiv 2408.11743, sec. 3.4 "Kernel Design"; deep-dive page,
 section "Marlin 要解决的精确问题"):  C = A * Bhat,  Bhat[k, n] = s[k // group, n] * (q[k, n] - z),
@@ -225,3 +227,43 @@ def exact_gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128,
             exact[m, n] = tot / float(1 << _SHIFT)
             absum[m, n] = tabs / float(1 << _SHIFT)
     return out.view(np.float16), exact, absum
+
+
+# --------------------------------------------------------------------------------------------
+# Checkpoint-style packed words -> codes.  Checkpoints labelled alike (INT4, group 128) differ
+# in nibble order and arrangement, and converting one for the kernel moves codes without
+# changing any (deep-dive page, section "直接生成 MMA 所需的寄存器 fragment" and the
+# deployment section on checkpoint formats).  These are the plain definitions of the two
+# arrangements the library's load-time repack takes: 8 codes per 32-bit word, nibble i in bits
+# 4i..4i+3.
+
+def _words(a, shape) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint32).reshape(shape)
+
+
+def decode_along_k(qweight, K: int, N: int) -> np.ndarray:
+    """Codes uint8 [K, N] from words [K/8, N]: word (r, n) holds rows 8r..8r+7 of column n,
+    row 8r + i in nibble i."""
+    w = _words(qweight, (K // 8, N))
+    codes = np.empty((K, N), dtype=np.uint8)
+    for i in range(8):
+        codes[i::8, :] = (w >> np.uint32(4 * i)) & np.uint32(15)
+    return codes
+
+
+def check_order(order) -> list:
+    order = list(range(8)) if order is None else [int(o) for o in order]
+    if sorted(order) != list(range(8)):
+        raise ValueError(f"order {order} is not a permutation of 0..7")
+    return order
+
+
+def decode_along_n(qweight, rows: int, N: int, order=None) -> np.ndarray:
+    """Codes uint8 [rows, N] from words [rows, N/8]: word (k, c) holds columns 8c..8c+7 of row
+    k, column 8c + order[i] in nibble i (order None: 0..7)."""
+    order = check_order(order)
+    w = _words(qweight, (rows, N // 8))
+    codes = np.empty((rows, N), dtype=np.uint8)
+    for i in range(8):
+        codes[:, order[i]::8] = (w >> np.uint32(4 * i)) & np.uint32(15)
+    return codes

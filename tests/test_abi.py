@@ -12,12 +12,12 @@ import numpy as np
 import pytest
 
 import mixed_precision_w4a16_amd as w4
+from layouts import NIBBLE, layout_reference, params_layout_reference
 from workloads import ALL, draw
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "paper_constants.json")
-NIBBLE = [0, 4, 1, 5, 2, 6, 3, 7]
 
 
 def declared_functions():
@@ -37,24 +37,6 @@ def test_library_exports_every_declared_function():
 def test_status_strings():
     for st in (w4.OK, w4.EINVAL, w4.ESHAPE, w4.EUNSUPPORTED, w4.EHIP, 12345):
         assert w4.library().w4a16_status_string(st)
-
-
-def layout_reference(codes, scales):
-    """The packed layout exactly as include/w4a16.h states it, written with numpy indexing."""
-    K, N = codes.shape
-    G = K // 128
-    packed = np.zeros((N // 16, G, 64, 4), dtype=np.uint32)
-    l = np.arange(64)
-    for t in range(4):
-        for i in range(8):
-            k = (np.arange(G)[:, None] * 128 + 32 * t + 8 * (l[None, :] // 16) + i)   # [G, 64]
-            for j in range(N // 16):
-                n = 16 * j + (l % 16)
-                packed[j, :, :, t] |= codes[k, n[None, :]].astype(np.uint32) << np.uint32(4 * NIBBLE[i])
-    Q = 4 if N % 256 == 0 else (2 if N % 128 == 0 else 1)
-    # [g][slab group u][slab b in group][c] -> [u][g][c][b]
-    sp = scales.reshape(G, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2).reshape(-1)
-    return packed.reshape(-1), sp
 
 
 @pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (384, 48), (1024, 1024), (256, 384),
@@ -154,16 +136,6 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
 
 # ------------------------------------------------------------------ one scale per column, zero points
 
-def params_layout_reference(scales, zeros):
-    """w4a16_pack_zp's params exactly as include/w4a16.h states it: per column and group its
-    scale, then its zero term 0x6400 | z, grouped by Q slabs."""
-    Gs, N = scales.shape
-    Q = 4 if N % 256 == 0 else (2 if N % 128 == 0 else 1)
-    s = scales.view(np.uint16).reshape(Gs, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2)  # [u][g][c][b]
-    z = (0x6400 | zeros.astype(np.uint16)).reshape(Gs, N // (16 * Q), Q, 16).transpose(1, 0, 3, 2)
-    return np.concatenate([s, z], axis=3).reshape(-1)
-
-
 @pytest.mark.parametrize("K,N,col", [(256, 64, False), (384, 256, False), (256, 128, True),
                                      (512, 48, True), (128, 16, False)])
 def test_pack_zp_matches_documented_layout(K, N, col):
@@ -238,3 +210,28 @@ def test_gemm_ex_rejects_bad_arguments_before_any_device_call():
     assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1024, 1024, 256, 0, d, None) == w4.ESHAPE
     assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1024, 1024, 0, 1, d, None) == w4.ESHAPE
     assert lib.w4a16_gemm_ex(d, d, d, d, 16, 1000, 1024, 1000, 0, d, None) == w4.ESHAPE
+
+
+def test_repack_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(256)
+    K, N = 1024, 512
+    ok_order = (ctypes.c_uint8 * 8)(0, 2, 4, 6, 1, 3, 5, 7)
+    dup = (ctypes.c_uint8 * 8)(0, 1, 2, 3, 4, 5, 6, 6)
+    big = (ctypes.c_uint8 * 8)(0, 1, 2, 3, 4, 5, 6, 8)
+    R = lib.w4a16_repack
+    assert R(None, 0, None, d, None, K, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, 0, None, None, None, K, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, 0, None, d, None, K, N, 128, None, d, None) == w4.EINVAL
+    assert R(d, 0, None, d, None, K, N, 128, d, None, None) == w4.EINVAL
+    assert R(d, 2, None, d, None, K, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, -1, None, d, None, K, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, 1, dup, d, None, K, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, 1, big, d, None, K, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, 0, None, d, None, -128, N, 128, d, d, None) == w4.EINVAL
+    assert R(d, 0, None, d, None, K, N, 128, ctypes.c_void_p(264), d, None) == w4.EINVAL  # 8-aligned out
+    assert R(d, 0, None, d, ctypes.c_void_p(258), K, N, 128, d, d, None) == w4.EINVAL      # 2-aligned zeros
+    assert R(d, 1, ok_order, d, None, 1000, N, 128, d, d, None) == w4.ESHAPE
+    assert R(d, 1, ok_order, d, None, K, 520, 128, d, d, None) == w4.ESHAPE
+    assert R(d, 0, None, d, None, K, N, 256, d, d, None) == w4.ESHAPE
+    assert R(d, 0, None, d, None, 0, N, 128, d, d, None) == w4.ESHAPE

@@ -398,3 +398,61 @@ def test_bad_zero_points_rejected():
     z = np.full((1, N), 16, dtype=np.uint8)
     with pytest.raises(ValueError):
         oracle.gemm(A, q, s, zeros=z)
+
+
+# ------------------------------------------------------------------ checkpoint-style words
+
+def test_decode_along_k_literal_words():
+    # word (0, 0) = 0x76543210: rows 0..7 of column 0 hold 0..7; word (0, 1) rows 8..15 -> 8..15
+    w = np.array([[0x76543210, 0xFEDCBA98]], dtype=np.uint32)
+    codes = oracle.decode_along_k(w, 8, 2)
+    assert codes[:, 0].tolist() == list(range(8))
+    assert codes[:, 1].tolist() == list(range(8, 16))
+
+
+def test_decode_along_n_literal_words():
+    w = np.array([[0x76543210], [0x01234567]], dtype=np.uint32)
+    assert oracle.decode_along_n(w, 2, 8).tolist() == [list(range(8)), list(range(7, -1, -1))]
+    # nibble i holds column order[i]: with (0, 2, 4, 6, 1, 3, 5, 7) the nibbles 0..7 of
+    # 0x76543210 land in columns 0, 2, 4, 6, 1, 3, 5, 7
+    got = oracle.decode_along_n(w[:1], 1, 8, order=(0, 2, 4, 6, 1, 3, 5, 7))
+    assert got.tolist() == [[0, 4, 1, 5, 2, 6, 3, 7]]
+
+
+@pytest.mark.parametrize("along", ["k", "n"])
+def test_decode_single_nibble_probes(along):
+    # one nibble set to 15 at a time: exactly one code is 15, at the position the definition
+    # names; every other code is 0.
+    K, N = 16, 16
+    order = (3, 1, 7, 5, 0, 2, 6, 4)
+    shape = (K // 8, N) if along == "k" else (K, N // 8)
+    for a in range(shape[0]):
+        for b in range(shape[1]):
+            for i in range(8):
+                w = np.zeros(shape, dtype=np.uint32)
+                w[a, b] = np.uint32(15) << np.uint32(4 * i)
+                if along == "k":
+                    codes = oracle.decode_along_k(w, K, N)
+                    where = (8 * a + i, b)
+                else:
+                    codes = oracle.decode_along_n(w, K, N, order=order)
+                    where = (a, 8 * b + order[i])
+                assert codes[where] == 15 and int(codes.sum()) == 15, (a, b, i)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_inverts_nibble_by_nibble_encoders(seed):
+    from layouts import encode_along_k, encode_along_n
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 16, (64, 48), dtype=np.uint8)
+    order = rng.permutation(8)
+    assert np.array_equal(oracle.decode_along_k(encode_along_k(codes), 64, 48), codes)
+    assert np.array_equal(oracle.decode_along_n(encode_along_n(codes, order), 64, 48, order), codes)
+    assert np.array_equal(oracle.decode_along_n(encode_along_n(codes), 64, 48), codes)
+
+
+def test_decode_rejects_orders_that_are_not_permutations():
+    w = np.zeros((1, 1), dtype=np.uint32)
+    for bad in [(0, 1, 2, 3, 4, 5, 6, 6), (0, 1, 2, 3, 4, 5, 6, 8), (0, 1, 2)]:
+        with pytest.raises(ValueError):
+            oracle.decode_along_n(w, 1, 8, order=bad)
