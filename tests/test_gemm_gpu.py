@@ -383,3 +383,29 @@ def test_formats_full_size_72kx18k_sampled(fmt):
         check(C[:, cols], ref[:M], f"{fmt} 72k x 18k M={M} ({len(cols)} sampled columns)")
     del W
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ nothing written past C
+
+@pytest.mark.parametrize("fmt", ["group128", "zeros"])
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (3, 2048, 256), (15, 1024, 1024),
+                                   (17, 1024, 512), (33, 1024, 512), (63, 2048, 256),
+                                   (65, 1024, 1024), (100, 1024, 512), (129, 2048, 1024),
+                                   (200, 1024, 768), (1, 18432, 512)])
+def test_no_write_past_the_rows_of_c(M, K, N, fmt):
+    # C is the head of a larger buffer whose tail covers every row a padded tile could
+    # address (up to 128 rows past M); the tail must keep its fill pattern.
+    zp = fmt == "zeros"
+    A, q, s = draw(K, N, M, seed=M + N)
+    z = draw_zeros(K, N, seed=M) if zp else None
+    packed, params = w4.to_device(*w4.pack(q, s, zeros=z))
+    Ad = torch.from_numpy(A).cuda()
+    pad = 128 * ((M + 127) // 128) + 128
+    buf = torch.full((pad * N + M * N,), -7.0, dtype=torch.float16, device="cuda")
+    C = buf[:M * N].view(M, N)
+    w4.gemm(Ad, packed, params, N, out=C, zero_points=zp)
+    torch.cuda.synchronize()
+    tail = buf[M * N:]
+    bad = int((tail != -7.0).sum())
+    assert bad == 0, f"{bad} fp16 values written past C (M={M}, N={N})"
+    check(C.cpu().numpy(), oracle.gemm(A, q, s, zeros=z), f"{fmt} M={M} K={K} N={N}")
