@@ -7,9 +7,10 @@ bytes per call: D = 2MK (A) + KN/2 (codes) + KN/64 (scales) + 2MN (C); flops F =
 Roofline per call: T_bound = max(D / 8 TB/s, F / 2.5 PFLOP/s); fp16-weight byte bound
 D16 = 2MK + 2KN + 2MN (the MARLIN paper's uncompressed reference point).
 
-`roofline` covers the dominant kernel: the 16-row tile kernel that serves M = 1..16, five of
-the eight calls and about half the sweep's time; HBM-bound, so achieved = its algorithmic
-bytes per launch / its mean launch time.  `roofline_by_kernel` gives the same for every kernel
+`roofline` covers the dominant kernel: the whole-K-workgroup kernel that serves M = 1..16
+(nine 16-column slabs per workgroup on this weight), five of the eight calls and about half
+the sweep's time; HBM-bound, so achieved = its algorithmic bytes per launch / its mean
+launch time.  `roofline_by_kernel` gives the same for every kernel
 of the sweep, the 128-row (M = 128) kernel against the fp16 MFMA peak.
 
 Also reported, outside `value`: `formats`, the per-call time of the other packed formats
@@ -39,11 +40,11 @@ GROUP = 128
 CALIB_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
 
-# The kernel each M of the sweep runs (the library picks it from M: 16-row tiles up to
-# M = 16, 32-row up to 32, 64-row up to 64, then 128-row tiles on this shape), and the roof
-# that bounds it.
+# The kernel each M of the sweep runs (the library picks it from M: workgroups that own nine
+# 16-column slabs over all of K up to M = 16, 32-row tiles up to 32, 64-row up to 64, then
+# 128-row tiles on this shape), and the roof that bounds it.
 KERNELS = [
-    ("w4a16_gemm_kernel<1,4> (16-row tiles)", (1, 2, 4, 8, 16), "hbm"),
+    ("w4a16_gemm_skinny_kernel<9> (whole-K workgroups, 9 slabs)", (1, 2, 4, 8, 16), "hbm"),
     ("w4a16_gemm_kernel<2,4> (32-row tiles)", (32,), "hbm"),
     ("w4a16_gemm_kernel<4,4> (64-row tiles)", (64,), "hbm"),
     ("w4a16_gemm_wide_kernel<4,2> (128-row tiles)", (128,), "mfma"),

@@ -50,6 +50,9 @@
 //   co-residency assumption is needed.
 // * M > 64 runs a second kernel with 128-row tiles (w4a16_gemm_wide_kernel, further down):
 //   every weight tile meets a whole 128-row block of A, A is brought into LDS by DMA.
+// * M <= 16 runs a third kernel (w4a16_gemm_skinny_kernel, further down) on most shapes: a
+//   workgroup owns a few 16-column slabs over all of K and its four waves split K, so no
+//   output is shared between workgroups and the reduction above is not needed.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -1193,6 +1196,291 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
     settle<MB, NBW, WAVES>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
 }
 
+// ------------------------------------------------------------------------- skinny kernel
+//
+// `w4a16_gemm_skinny_kernel<NS, F>`, M <= 16, N a multiple of 256.  The weight stream bounds
+// the product, and the stripe scheme's split slices cost a store, a counter and a read at the
+// very end, when every stripe finishes at once (on small weights that chain is most of the
+// time).  Here a workgroup owns NS consecutive 16-column slabs over the whole K range, so no
+// output is shared between workgroups.  Its four waves split the K tiles into four contiguous
+// runs; each streams all NS slabs over its run (NS KiB of weights per tile, double-buffered),
+// and the four fp32 partial sums meet in LDS at the end in a fixed order (the in-block
+// reduction of warp partial sums the deep-dive page describes in "让多个 warp 计算同一个输出
+// tile 的部分和").  A needs no LDS: each wave loads its A fragments (16 bytes per lane per 32-k
+// step) straight into the MFMA operand registers, rows at or past M falling outside the buffer
+// (zero, no memory access).  No per-tile barrier.
+//
+// Parameters: with N a multiple of 256 the parameter stream groups four slabs, so per K step a
+// column holds 4 scales (and 4 zero terms) of a group in 8 (16) contiguous bytes.  A
+// workgroup's NS slabs start at j0 and touch at most (NS + 6) / 4 groups; one load per group
+// brings the lane's column, and the halves of slabs j0 .. j0 + NS - 1 are picked out by two
+// uniform selects per dword (j0 % 4 is the same for the whole workgroup).
+//
+// The tiles after a wave's run are still "loaded" (every iteration issues the same loads),
+// from an offset outside every buffer: no memory traffic, and the compiler never meets a join
+// where it would have to wait for everything.
+constexpr uint32_t kOutside = 0x80000000u;   // above every buffer the skinny kernel reads
+
+template <int NS>
+struct SkinnyGroups {
+    static constexpr int n = (NS + 6) / 4;   // parameter groups NS slabs can touch
+    static constexpr int nh = (NS + 1) / 2;  // dwords holding NS halves
+    // tile buffers; deeper rings for few slabs measured no faster (the A loads, four per tile,
+    // dominate the instruction stream there)
+    static constexpr int depth = 2;
+};
+
+template <int NS, class F>
+struct SkinnyBuf {
+    u4 w[NS];                                // weight quads, one per slab
+    h8 a[4];                                 // A fragments of the 4 32-k steps
+    uint32_t p[F::COL ? 1 : SkinnyGroups<NS>::n][F::ZP ? 4 : 2];   // per-group parameters
+};
+
+template <int NS, class F>
+__global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p)
+{
+    using SG = SkinnyGroups<NS>;
+    constexpr int NG = SG::n, NH = SG::nh;
+    constexpr uint32_t PB = F::ZP ? 16 : 8;              // bytes per column, group and K step
+    __shared__ f4 red[kWaves * NS * 64];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15;
+    const int S = p.N >> 4;                              // slabs
+    const int U = S >> 2;                                // parameter groups
+    const int j0 = blockIdx.x * NS;                      // the workgroup's first slab
+    const int u0 = j0 >> 2, r = j0 & 3;
+    const int g0 = p.G * wave / kWaves;                  // this wave's run of K tiles
+    const int g1 = p.G * (wave + 1) / kWaves;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(
+        p.scales, static_cast<uint32_t>(static_cast<size_t>(p.Gs) * p.N * (F::ZP ? 4 : 2)));
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
+
+    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+
+    // byte offset of parameter block (group u, scale group gs); the lane's column adds c * PB
+    auto par_soff = [&](int u, int gs) __attribute__((always_inline)) {
+        return (static_cast<uint32_t>(u) * p.Gs + gs) * (16u * PB);
+    };
+    const uint32_t v_par = static_cast<uint32_t>(c) * PB;
+    // A operand: row c, k = 8 * (lane / 16) of each 32-k step
+    const uint32_t v_a = (static_cast<uint32_t>(c) * p.K + 8 * (lane >> 4)) * 2;
+    auto slab = [&](int i) __attribute__((always_inline)) {
+        const int j = j0 + i;
+        return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
+    };
+
+    auto load = [&](SkinnyBuf<NS, F> &b, int g) __attribute__((always_inline)) {
+        const bool live = g < g1;
+        const uint32_t vw = live ? static_cast<uint32_t>(lane) * 16 : kOutside;
+        const uint32_t va = live ? v_a : kOutside;
+        const uint32_t vp = live ? v_par : kOutside;
+        const int gg = live ? g : g1 - 1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            b.a[t] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rA, va, static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            b.w[i] = __builtin_bit_cast(
+                u4, __builtin_amdgcn_raw_buffer_load_b128(
+                        rW, vw, (static_cast<uint32_t>(slab(i)) * p.G + gg) * 1024u, kNonTemporal));
+        if constexpr (!F::COL) {
+#pragma unroll
+            for (int k = 0; k < NG; ++k) {
+                const int u = u0 + k < U ? u0 + k : U - 1;
+                if constexpr (F::ZP) {
+                    const u4 v = __builtin_bit_cast(
+                        u4, __builtin_amdgcn_raw_buffer_load_b128(rS, vp, par_soff(u, gg), 0));
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        b.p[k][d] = v[d];
+                } else {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, vp, par_soff(u, gg), 0);
+                    b.p[k][0] = v[0];
+                    b.p[k][1] = v[1];
+                }
+            }
+        }
+    };
+
+    // Halves r .. r + NS - 1 of the concatenated groups (part 0: scales, 1: zero terms), two
+    // per dword: dword m of the result holds slabs 2m and 2m + 1.
+    const bool sel_dw = (r & 2) != 0, sel_half = (r & 1) != 0;     // uniform
+    auto pick = [&](const uint32_t (&pg)[NG][F::ZP ? 4 : 2], int part, uint32_t (&out)[NH])
+        __attribute__((always_inline)) {
+        auto D = [&](int m) __attribute__((always_inline)) {
+            m = m < 2 * NG ? m : 2 * NG - 1;           // past the last half needed
+            return pg[m >> 1][2 * part + (m & 1)];
+        };
+        uint32_t e[NH + 1];
+#pragma unroll
+        for (int m = 0; m <= NH; ++m)
+            e[m] = sel_dw ? D(m + 1) : D(m);
+#pragma unroll
+        for (int m = 0; m < NH; ++m)
+            out[m] = sel_half ? __builtin_amdgcn_alignbit(e[m + 1], e[m], 16) : e[m];
+    };
+
+    // One scale per column: the half of slab j at group 0 (part 1: its zero term), and its
+    // position in the dword that holds it.
+    auto col_param = [&](int j, int part) __attribute__((always_inline)) {
+        const uint32_t half = (static_cast<uint32_t>(j >> 2) * 16u + c) * (PB / 2) + 4u * part +
+                              static_cast<uint32_t>(j & 3);
+        const uint32_t dw = __builtin_amdgcn_raw_buffer_load_b32(rS, (half >> 1) * 4, 0, 0);
+        return static_cast<uint16_t>(dw >> (16 * (half & 1)));
+    };
+
+    // With one scale per column and zero points the zero terms are the same for every tile.
+    uint16_t zcol[(F::ZP && F::COL) ? NS : 1];
+    if constexpr (F::ZP && F::COL) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            zcol[i] = col_param(slab(i), 1);
+    }
+
+    f4 acc[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+        acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const SkinnyBuf<NS, F> &b) __attribute__((always_inline)) {
+        float sf[NS];
+        h2 zsub[NS], zadd[NS];
+        uint32_t sh[NH], zh[NH];
+        if constexpr (!F::COL) {
+            pick(b.p, 0, sh);
+            if constexpr (F::ZP)
+                pick(b.p, 1, zh);
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if constexpr (!F::COL) {
+                sf[i] = half_bits_to_float(static_cast<uint16_t>(sh[i >> 1] >> (16 * (i & 1))));
+                asm volatile("" : "+v"(sf[i]));
+            }
+            if constexpr (F::ZP) {
+                uint16_t zb;
+                if constexpr (F::COL)
+                    zb = zcol[i];
+                else
+                    zb = static_cast<uint16_t>(zh[i >> 1] >> (16 * (i & 1)));
+                const _Float16 zt = __builtin_bit_cast(_Float16, zb);
+                zsub[i] = h2{zt, zt};
+                const h2 k960 = {static_cast<_Float16>(960.0f), static_cast<_Float16>(960.0f)};
+                zadd[i] = k960 - zsub[i];
+                asm volatile("" : "+v"(zsub[i]));
+                asm volatile("" : "+v"(zadd[i]));
+            } else {
+                zsub[i] = sym_zsub();
+                zadd[i] = sym_zadd();
+            }
+        }
+        if constexpr (F::COL) {
+            // one scale per column: sum A * (q - z) over the whole K range, scale at the end
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        b.a[t], dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]), acc[i],
+                        0, 0, 0);
+        } else {
+            // per group: the exact sum of A * (q - z) over the group, then one scale per output
+            f4 part[NS];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    const f4 cin = t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : part[i];
+                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        b.a[t], dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]), cin, 0,
+                        0, 0);
+                }
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[i][q] = __builtin_fmaf(sf[i], part[i][q], acc[i][q]);
+                asm volatile("" : "+v"(acc[i]));
+            }
+        }
+    };
+
+    if (g0 < g1) {
+        // D buffers, tile i in buffer i % D, so D - 1 tiles of weights are in flight while one
+        // is computed.  Whole rounds of D tiles run in a
+        // loop with one exit (a loop the compiler can leave from several places gets an edge on
+        // which the last loads issued are the buffer about to be used, and then waits for every
+        // load in flight); the remaining tiles follow.  The empty asm statements fence memory,
+        // so each buffer's loads are issued right after the compute that frees it and are not
+        // sunk toward their use.
+        constexpr int D = SkinnyGroups<NS>::depth;
+        SkinnyBuf<NS, F> b[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load(b[d], g0 + d);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int rounds = (g1 - g0) / D;
+        int g = g0;
+        for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                compute(b[d]);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                load(b[d], g + d + D);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            g += D;
+        }
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (g + d < g1)
+                compute(b[d]);
+        // the loads past the run touch no memory, but their registers are still written
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // The four waves' partial sums meet in LDS; wave w then finishes slabs w, w + 4, ...
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+        red[(wave * NS + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    const uint32_t v_c = (static_cast<uint32_t>(4 * (lane >> 4)) * p.N + c) * 2;
+    const uint32_t rowN = opaque(static_cast<uint32_t>(p.N) * 2);
+#pragma unroll
+    for (int i0 = 0; i0 < NS; i0 += kWaves) {
+        const int i = i0 + wave;
+        if (i < NS && j0 + i < S) {
+            f4 v = red[(0 * NS + i) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                v += red[(w * NS + i) * 64 + lane];
+            if constexpr (F::COL)
+                v *= half_bits_to_float(col_param(j0 + i, 0));
+            uint32_t srow = static_cast<uint32_t>(j0 + i) * 32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(v[q]), rC, v_c, srow, 0);
+                srow += rowN;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------- host side
 
 struct Config {
@@ -1200,7 +1488,31 @@ struct Config {
     int waves;       // waves per workgroup
     int P, S, G, W;
     long long T;
+    int NS;          // > 0: the skinny kernel, NS slabs per workgroup (W workgroups)
 };
+
+constexpr int kSkinnyMaxNS = 10;
+
+// Skinny kernel (M <= 16, N a multiple of 256): NS = the fewest slabs per workgroup that keep
+// the workgroups within two per CU, so every workgroup streams as many bytes as possible at
+// once.  With one slab per workgroup four of a wave's six loads per tile are A fragments;
+// there the stripe kernel measures faster once K runs long (28672 x 8192: 31 vs 33 us at
+// M = 1), while on every shorter or wider weight measured the skinny kernel is faster
+// (1.1x to 4x).  Its dead loads point 2 GiB past the buffer starts, so the weights and A
+// must lie below that.
+int skinny_slabs(int M, int K, int N, int cus)
+{
+    if (M > 16 || N % 256)
+        return 0;
+    const long long S = N / 16;
+    const long long per = 2LL * cus;
+    const long long ns = (S + per - 1) / per;
+    if (ns > kSkinnyMaxNS || (ns == 1 && K / kGroup > 128) ||
+        static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
+        static_cast<uint64_t>(16) * static_cast<uint64_t>(K) * 2 >= kOutside)
+        return 0;
+    return static_cast<int>(ns);
+}
 
 int check_gemm_shape(int M, int K, int N)
 {
@@ -1260,11 +1572,16 @@ Config choose_config(int M, int K, int N, int cus)
     c.S = N / (16 * c.waves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
     c.W = choose_stripes(c.T, cus, per_cu);
+    c.NS = skinny_slabs(M, K, N, cus);
+    if (c.NS > 0)
+        c.W = (N / 16 + c.NS - 1) / c.NS;
     return c;
 }
 
 size_t workspace_for(const Config &c)
 {
+    if (c.NS > 0)
+        return kCounterBytes;          // the skinny kernel shares nothing between workgroups
     const size_t slot = static_cast<size_t>(16 * c.MB) * (16 * c.waves * c.NBW) * sizeof(float);
     return kCounterBytes + 2 * static_cast<size_t>(c.W) * slot;
 }
@@ -1284,11 +1601,41 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int NS, class F>
+hipError_t launch_skinny(const Params &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<NS, F>), dim3(p.W), dim3(kThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+template <class F>
+hipError_t dispatch_skinny(int ns, const Params &p, hipStream_t s)
+{
+    switch (ns) {
+    case 1: return launch_skinny<1, F>(p, s);
+    case 2: return launch_skinny<2, F>(p, s);
+    case 3: return launch_skinny<3, F>(p, s);
+    case 4: return launch_skinny<4, F>(p, s);
+    case 5: return launch_skinny<5, F>(p, s);
+    case 6: return launch_skinny<6, F>(p, s);
+    case 7: return launch_skinny<7, F>(p, s);
+    case 8: return launch_skinny<8, F>(p, s);
+    case 9: return launch_skinny<9, F>(p, s);
+    case 10: return launch_skinny<10, F>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 // The kernel for this configuration and format.
 template <class F>
 int dispatch(const Config &c, const Params &p, hipStream_t s)
 {
     hipError_t e;
+    if (c.NS > 0) {
+        e = dispatch_skinny<F>(c.NS, p, s);
+        return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
+    }
     switch (c.MB * 10 + c.NBW) {
     case 11: e = launch<1, 1, F>(p, s); break;
     case 12: e = launch<1, 2, F>(p, s); break;

@@ -409,3 +409,47 @@ def test_no_write_past_the_rows_of_c(M, K, N, fmt):
     bad = int((tail != -7.0).sum())
     assert bad == 0, f"{bad} fp16 values written past C (M={M}, N={N})"
     check(C.cpu().numpy(), oracle.gemm(A, q, s, zeros=z), f"{fmt} M={M} K={K} N={N}")
+
+
+# ------------------------------------------------------------------ M <= 16: whole-K workgroups
+
+# N chosen for 2, 3, 4 and 9 slabs per workgroup (16640: 1040 slabs in 347 workgroups of
+# three, the last holding two; first slabs at every offset mod 4), K = 128..384 so that some
+# waves of a workgroup get no K tile at all.
+SKINNY_SHAPES = [(128, 9216), (256, 16640), (384, 26880), (1024, 16640), (4096, 8448),
+                 (2048, 73728), (640, 12544)]
+
+
+@pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
+@pytest.mark.parametrize("K,N", SKINNY_SHAPES)
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_whole_k_workgroups_against_oracle(M, K, N, fmt):
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=M + K + N)
+        W, g, z = FmtWeights(q, s, 128), 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=M + K + N)
+        W = FmtWeights(q, s, g, z)
+    C = W.run(A)
+    check(C, oracle.gemm(A, q, s, group=g, zeros=z), f"{fmt} M={M} K={K} N={N}")
+    # bitwise repeatable: the four waves' sums meet in a fixed order
+    assert np.array_equal(bits(W.run(A)), bits(C))
+
+
+@pytest.mark.parametrize("fmt", ["group128", "zeros", "column_zeros"])
+def test_whole_k_workgroups_one_hot_rows_are_bit_exact(fmt):
+    K, N, M = 512, 16640, 16
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=90)
+        g, z = 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=90)
+    A[:] = 0
+    ks = [0, 7, 127, 128, 200, 255, 256, 300, 383, 384, 385, 450, 500, 510, 511, 64]
+    for m, k in enumerate(ks):
+        A[m, k] = 1.0
+    C = FmtWeights(q, s, g, z).run(A)
+    for m, k in enumerate(ks):
+        zz = 8 if z is None else z[k // g].astype(np.float64)
+        w = s[k // g].astype(np.float64) * (q[k].astype(np.float64) - zz)
+        assert same(C[m], w.astype(np.float16)), (fmt, m, k)
