@@ -16,7 +16,9 @@ of the sweep, the 128-row (M = 128) kernel against the fp16 MFMA peak.
 Also reported, outside `value`: `formats`, the per-call time of the other packed formats
 (one scale per column, zero points, both) on the same weight at M = 1, 16, 64, 128, timed
 call by call alternately with the group-128 symmetric format; `repack`, the load-time
-conversion of a checkpoint-style packed weight of the same size into the multiply's layout.
+conversion of a checkpoint-style packed weight of the same size into the multiply's layout;
+`sparse_24`, the 2:4-sparse path on the same weight with two of every four codes pruned, at
+every M, alternated call by call with the dense path.
 
 Prints one JSON line on stdout.  Single GPU only.
 """
@@ -156,6 +158,60 @@ def time_formats(w4, torch, dev, Ad, q, s, K, N, steps, warmup, copies, stream, 
             log(f"{name:19s} M={M:4d} {us[name]:8.1f} us  {D / us[name] / 1e3:7.0f} GB/s  "
                 f"x{us[name] / us['group128_symmetric']:.3f}")
     del fmts
+    torch.cuda.empty_cache()
+    return rows
+
+
+def sparse_bytes(M, K, N):
+    """Algorithmic bytes of one 2:4-sparse call: A, kept codes and their positions (3 bits
+    per weight), scales, C."""
+    return 2 * M * K + K * N * 3 // 8 + K * N // 64 + 2 * M * N
+
+
+def time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, steps, warmup, copies, stream, dense):
+    """The 2:4-sparse path (w4a16_pack_24 / w4a16_gemm_24) on the same codes with two of
+    every four along K pruned, every M of the sweep; each call alternated with a dense call
+    on the original codes, so both are timed in the same clock and power state.  TFLOP/s
+    counts the dense product's 2MKN."""
+    from workloads import sparsify_24
+    t = time.perf_counter()
+    qs = sparsify_24(q, seed=0)
+    packed, sp = w4.pack_24(qs, s)
+    del qs
+    log(f"2:4 weights drawn and packed in {time.perf_counter() - t:.1f} s")
+    pd, sd = w4.to_device(packed, sp, dev)
+    del packed, sp
+    cps = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(copies - 1)]
+    rows = []
+    for M in Ms:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = w4.new_workspace(M, K, N, dev)
+        ev_s, ev_d = [], []
+        for i in range(warmup + steps):
+            for kind in ("sparse", "dense"):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                if kind == "sparse":
+                    p_, s_ = cps[i % len(cps)]
+                    w4.gemm_24(Ad[:M], p_, s_, N, out=out, stream=stream)
+                else:
+                    p_, s_ = dense[i % len(dense)]
+                    w4.gemm(Ad[:M], p_, s_, N, out=out, ws=ws, stream=stream)
+                e1.record(stream)
+                if i >= warmup:
+                    (ev_s if kind == "sparse" else ev_d).append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev_s])) * 1e3
+        usd = float(np.mean([a.elapsed_time(b) for a, b in ev_d])) * 1e3
+        D = sparse_bytes(M, K, N)
+        rows.append({"M": M, "us": round(us, 2), "GBps": round(D / us / 1e3, 1),
+                     "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4),
+                     "TFLOPs_dense_equivalent": round(flops(M, K, N) / us / 1e6, 2),
+                     "dense_us": round(usd, 2), "speedup_vs_dense": round(usd / us, 3)})
+        log(f"2:4 sparse M={M:4d} {us:8.1f} us  {D / us / 1e3:7.0f} GB/s "
+            f"({D / us / 1e3 / HBM_PEAK_GBPS:5.1%} HBM)  dense {usd:8.1f} us  x{usd / us:.3f}")
+    del cps, pd, sd
     torch.cuda.empty_cache()
     return rows
 
@@ -321,6 +377,10 @@ def main():
 
     kernels = [roof(*k) for k in KERNELS]
     repack = time_repack(w4, torch, dev, K, N, 10, stream) if args.format_steps > 0 else None
+    sparse = None
+    if args.format_steps > 0:
+        sparse = time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, args.format_steps,
+                             max(2, args.warmup // 4), args.copies, stream, copies)
     formats = None
     if args.format_steps > 0:
         formats = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
@@ -338,6 +398,7 @@ def main():
         "sweep": sweep,
         "formats": formats,
         "repack": repack,
+        "sparse_24": sparse,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }

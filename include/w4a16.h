@@ -181,6 +181,47 @@ int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params,
                   void *stream);
 
 /*
+ * 2:4-sparse weights (Sparse-MARLIN: MARLIN paper sec. 1 "Contribution" and sec. 2.1.1, the
+ * 2:4 format of two non-zeros in every 4 consecutive weights with their positions as
+ * metadata; deep-dive page, Sparse-MARLIN section: 4-bit non-zeros plus 2-bit positions, the
+ * product computed as (B^T A^T)^T).  Group-128 scales, zero point 8: a weight is zero when its
+ * code is 8, and every aligned group of 4 rows of a column may hold at most 2 other codes.
+ *
+ * w4a16_pack_24 (host, synchronous): codes uint8 [K*N] (row-major (k, n), 0..15, 2:4 along K
+ * as above), scales fp16 bits [(K/128)*N] -> packed_out uint32 [K*N*3/32], scales_out fp16
+ * bits [(K/128)*N] (the layout of w4a16_pack's scales_out).
+ * Packed layout: blocks of 128 rows x 16 columns, block (j, g) -- columns 16j..16j+15, rows
+ * 128g..128g+127 -- is 192 consecutive words starting at word (j*(K/128) + g)*192.  Lane
+ * l = 0..63 owns words 3l, 3l+1, 3l+2: column 16j + (l mod 16); word 3l + s (s = 0, 1) holds
+ * the two kept codes of each group of four rows 128g + 64s + 16*(l div 16) + 4p + 0..3,
+ * p = 0..3, in row order -- kept code e = 2p + i (i = 0, 1) in nibble q(e), q = {0, 4, 1, 5,
+ * 2, 6, 3, 7} -- and word 3l + 2 holds their positions in the group (0..3), code e of word
+ * 3l + s in bits 16s + 2e .. 16s + 2e + 1.  Kept positions are the non-zero weights, completed
+ * by the lowest other positions (which then hold code 8).  3.125 bits per weight with scales.
+ * Returns W4A16_OK, W4A16_EINVAL (null pointer, negative size, a code above 15, a group with
+ * more than 2 codes other than 8) or W4A16_ESHAPE (as w4a16_pack with group 128).
+ */
+int w4a16_pack_24(const uint8_t *codes, const uint16_t *scales, int K, int N,
+                  uint32_t *packed_out, uint16_t *scales_out);
+
+/*
+ * Exact inverse of w4a16_pack_24 (host, synchronous; tests and tooling): codes at pruned
+ * positions come back as 8.  W4A16_EINVAL also if a group's two positions are not increasing.
+ */
+int w4a16_unpack_24(const uint32_t *packed, const uint16_t *scales_packed, int K, int N,
+                    uint8_t *codes_out, uint16_t *scales_out);
+
+/*
+ * C = A * Bhat with 2:4-sparse Bhat from w4a16_pack_24 (device, asynchronous on `stream`).
+ * A, C, alignment and the size limits as w4a16_gemm; packed and scales as w4a16_pack_24 wrote
+ * them (device copies).  No workspace.  N must be a multiple of 256, and K*N*3/8 and 128*K
+ * below 2^31 bytes.  M == 0 is a no-op.  Errors: W4A16_EINVAL (null pointer, negative size),
+ * W4A16_ESHAPE (shape or limit), W4A16_EUNSUPPORTED (not gfx950), W4A16_EHIP (launch failure).
+ */
+int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
+                  int M, int K, int N, void *stream);
+
+/*
  * Device-side load-time conversion of checkpoint-style packed tensors into the layouts of
  * w4a16_pack (qzeros NULL) or w4a16_pack_zp (device, asynchronous on `stream`).  The pages'
  * load step that turns a GPTQ/AWQ-style checkpoint into the kernel's layout: it only moves

@@ -11,7 +11,7 @@ when the compiled library is missing; there is no fallback path.
 Other formats: pack(codes, scales, group=K) for one scale per column, and
 pack(codes, scales, group, zeros=z) for zero points; pass the same group / zero_points to
 gemm.  repack(...) converts checkpoint-style packed tensors already on the GPU into the same
-layout on the GPU.
+layout on the GPU.  2:4-sparse weights: pack_24(codes, scales) and gemm_24(A, packed, scales, N).
 """
 from __future__ import annotations
 
@@ -60,12 +60,18 @@ _lib.w4a16_gemm_ex.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]
 _lib.w4a16_gemm_ex.restype = _i
 _lib.w4a16_repack.argtypes = [_p, _i, _p, _p, _p, _i, _i, _i, _p, _p, _p]
 _lib.w4a16_repack.restype = _i
+_lib.w4a16_pack_24.argtypes = [_p, _p, _i, _i, _p, _p]
+_lib.w4a16_pack_24.restype = _i
+_lib.w4a16_unpack_24.argtypes = [_p, _p, _i, _i, _p, _p]
+_lib.w4a16_unpack_24.restype = _i
+_lib.w4a16_gemm_24.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p]
+_lib.w4a16_gemm_24.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
 EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
             "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
-            "w4a16_repack")
+            "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24")
 
 
 class W4A16Error(RuntimeError):
@@ -261,3 +267,63 @@ def repack(qweight, scales, K: int, N: int, layout: int, group: int = GROUP, qze
             None if order_buf is None else order_buf.ctypes.data, scales.data_ptr(), zp or None,
             K, N, group, packed.data_ptr(), params.data_ptr(), stream.cuda_stream))
     return packed, params
+
+
+# ------------------------------------------------------------------------------ 2:4 sparse
+
+def pack_24(codes: np.ndarray, scales: np.ndarray):
+    """Offline reorder of 2:4-sparse weights (group 128, zero point 8).  codes uint8 [K, N]
+    with at most 2 codes other than 8 in every aligned group of 4 rows of a column ->
+    (packed uint32 [K*N*3/32], scales fp16 [(K/128)*N])."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float16)
+    K, N = codes.shape
+    if K % GROUP or scales.shape != (K // GROUP, N):
+        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
+    packed = np.empty(K * N * 3 // 32, dtype=np.uint32)
+    sp = np.empty(scales.size, dtype=np.float16)
+    _check("w4a16_pack_24", _lib.w4a16_pack_24(codes.ctypes.data, scales.ctypes.data, K, N,
+                                               packed.ctypes.data, sp.ctypes.data))
+    return packed, sp
+
+
+def unpack_24(packed: np.ndarray, scales_p: np.ndarray, K: int, N: int):
+    """Inverse of pack_24: (codes uint8 [K, N] with 8 at pruned positions, scales fp16)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    scales_p = np.ascontiguousarray(scales_p, dtype=np.float16)
+    if K % GROUP or packed.size != K * N * 3 // 32 or scales_p.size != (K // GROUP) * N:
+        raise ValueError("size mismatch")
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty((K // GROUP, N), dtype=np.float16)
+    _check("w4a16_unpack_24", _lib.w4a16_unpack_24(packed.ctypes.data, scales_p.ctypes.data, K,
+                                                   N, codes.ctypes.data, scales.ctypes.data))
+    return codes, scales
+
+
+def gemm_24(A, packed, scales, N: int, out=None, stream=None):
+    """C[M, N] = A @ Bhat for 2:4-sparse Bhat from to_device(pack_24(...))."""
+    import torch
+    if A.dtype != torch.float16 or not A.is_cuda or A.dim() != 2 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous fp16 CUDA tensor of shape [M, K]")
+    M, K = A.shape
+    if packed.device != A.device or scales.device != A.device:
+        raise ValueError("packed and scales must be on A's device")
+    if packed.dtype != torch.int32 or packed.numel() * 32 != K * N * 3 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous int32 tensor of K*N*3/32 words")
+    if (K % GROUP or scales.dtype != torch.float16 or scales.numel() != (K // GROUP) * N
+            or not scales.is_contiguous()):
+        raise ValueError("scales must be a contiguous fp16 tensor as pack_24() returned it")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    elif (out.dtype != torch.float16 or out.shape != (M, N) or not out.is_contiguous()
+          or out.device != A.device):
+        raise ValueError("out must be a contiguous fp16 tensor [M, N] on A's device")
+    if M == 0:
+        return out
+    with torch.cuda.device(A.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        _check("w4a16_gemm_24", _lib.w4a16_gemm_24(A.data_ptr(), packed.data_ptr(),
+                                                   scales.data_ptr(), out.data_ptr(), M, K, N,
+                                                   stream.cuda_stream))
+    return out

@@ -68,6 +68,7 @@ namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16 __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
@@ -1481,6 +1482,213 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
     }
 }
 
+// ------------------------------------------------------------------ 2:4-sparse weights
+//
+// `w4a16_gemm_sparse_kernel<MB, NS>`: the product with weights that keep 2 of every 4 along K
+// (w4a16_pack_24; group-128 scales, zero point 8), on gfx950's structured-sparse matrix
+// instruction v_smfmac_f32_16x16x64_f16.  Its first operand is the sparse one (16 rows x 64 k
+// held as the 32 kept values with a 2-bit position each), so the product is computed
+// transposed, C^T = Bhat^T A^T, as Sparse-MARLIN rewrites AB as (B^T A^T)^T for the same
+// reason (deep-dive page, Sparse-MARLIN section): output columns are the instruction's rows,
+// tokens its columns.  Operand layout, measured on the hardware: sparse-operand lane l holds
+// row l % 16 and the kept values of the four groups of four in k = 16(l/16) .. +15 (value e
+// of group e/2, its position in bits 2e..2e+1 of the index register); dense-operand lane l
+// holds column l % 16 with k = 8(l/16) + 0..7 in halves 0..7 and 32 + 8(l/16) + 0..7 in halves
+// 8..15 -- the A fragments of two consecutive 32-k steps of the dense kernels; result lane l
+// holds rows 4(l/16) + 0..3 of column l % 16.
+//
+// Structure as the whole-K kernel above: a workgroup owns NS slabs over all of K, its four
+// waves split the K tiles, partial sums meet in LDS in a fixed order.  A lane's 12 bytes per
+// 128 x 16 block are one 96-bit load: the kept codes of the block's two 64-k steps (8 per
+// word, decoded by the dense kernels' mask-and-OR) and their positions.  The decoded values are
+// scaled in fp16 (the lane's sparse-operand row is an output column, so its own column scale
+// applies; one rounding of s * (q - 8), as in the 64- and 128-row dense tiles).  MB blocks of
+// 16 rows per launch; the host runs larger M as several launches.
+template <int MB, int NS>
+struct SparseBuf {
+    uint32_t w[NS][3];                       // kept codes of the two 64-k steps, positions
+    h8 a[MB][4];                             // A fragments of each 16-row block
+    uint32_t p[SkinnyGroups<NS>::n][2];      // four scales of the lane's column per group
+};
+
+template <int MB, int NS>
+__global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p)
+{
+    using SG = SkinnyGroups<NS>;
+    constexpr int NG = SG::n, NH = SG::nh;
+    __shared__ f4 red[kWaves * MB * NS * 64];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15;
+    const int S = p.N >> 4;                              // slabs
+    const int U = S >> 2;                                // parameter groups
+    const int j0 = blockIdx.x * NS;
+    const int u0 = j0 >> 2, r = j0 & 3;
+    const int g0 = p.G * wave / kWaves;
+    const int g1 = p.G * (wave + 1) / kWaves;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(
+        p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N * 3 / 8));
+    const __amdgpu_buffer_rsrc_t rS =
+        make_rsrc(p.scales, static_cast<uint32_t>(static_cast<size_t>(p.G) * p.N * 2));
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
+
+    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+    const uint32_t v_par = static_cast<uint32_t>(c) * 8;
+    // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step
+    uint32_t v_a[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        v_a[mb] = (static_cast<uint32_t>(16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
+    auto slab = [&](int i) __attribute__((always_inline)) {
+        const int j = j0 + i;
+        return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
+    };
+
+    auto load = [&](SparseBuf<MB, NS> &b, int g) __attribute__((always_inline)) {
+        const bool live = g < g1;
+        const uint32_t vw = live ? static_cast<uint32_t>(lane) * 12 : kOutside;
+        const uint32_t vp = live ? v_par : kOutside;
+        const int gg = live ? g : g1 - 1;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                b.a[mb][t] = __builtin_bit_cast(
+                    h8, __builtin_amdgcn_raw_buffer_load_b128(
+                            rA, live ? v_a[mb] : kOutside,
+                            static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b96(
+                rW, vw, (static_cast<uint32_t>(slab(i)) * p.G + gg) * 768u, kNonTemporal);
+            b.w[i][0] = v[0];
+            b.w[i][1] = v[1];
+            b.w[i][2] = v[2];
+        }
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const int u = u0 + k < U ? u0 + k : U - 1;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+                rS, vp, (static_cast<uint32_t>(u) * p.G + gg) * 128u, 0);
+            b.p[k][0] = v[0];
+            b.p[k][1] = v[1];
+        }
+    };
+
+    // scale halves of slabs j0 .. j0 + NS - 1 (two per dword), as in the whole-K kernel
+    const bool sel_dw = (r & 2) != 0, sel_half = (r & 1) != 0;
+    auto pick = [&](const uint32_t (&pg)[NG][2], uint32_t (&out)[NH]) __attribute__((always_inline)) {
+        auto D = [&](int m) __attribute__((always_inline)) {
+            m = m < 2 * NG ? m : 2 * NG - 1;
+            return pg[m >> 1][m & 1];
+        };
+        uint32_t e[NH + 1];
+#pragma unroll
+        for (int m = 0; m <= NH; ++m)
+            e[m] = sel_dw ? D(m + 1) : D(m);
+#pragma unroll
+        for (int m = 0; m < NH; ++m)
+            out[m] = sel_half ? __builtin_amdgcn_alignbit(e[m + 1], e[m], 16) : e[m];
+    };
+
+    f4 acc[MB][NS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const SparseBuf<MB, NS> &b) __attribute__((always_inline)) {
+        uint32_t sh[NH];
+        pick(b.p, sh);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const _Float16 sv = __builtin_bit_cast(
+                _Float16, static_cast<uint16_t>(sh[i >> 1] >> (16 * (i & 1))));
+            const h2 s2 = {sv, sv};
+            const h8 x0 = dequant8_scaled(b.w[i][0], s2, mlo, mhi, magic, sym_zsub(), sym_zadd());
+            const h8 x1 = dequant8_scaled(b.w[i][1], s2, mlo, mhi, magic, sym_zsub(), sym_zadd());
+            const int idx0 = static_cast<int>(b.w[i][2]);
+            const int idx1 = static_cast<int>(b.w[i][2] >> 16);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const h16 d0 = __builtin_shufflevector(b.a[mb][0], b.a[mb][1], 0, 1, 2, 3, 4, 5,
+                                                       6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                const h16 d1 = __builtin_shufflevector(b.a[mb][2], b.a[mb][3], 0, 1, 2, 3, 4, 5,
+                                                       6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                acc[mb][i] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(x0, d0, acc[mb][i], idx0,
+                                                                      0, 0);
+                acc[mb][i] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(x1, d1, acc[mb][i], idx1,
+                                                                      0, 0);
+            }
+        }
+    };
+
+    if (g0 < g1) {
+        // two buffers, one exit, memory fences: as the whole-K kernel (see there)
+        SparseBuf<MB, NS> b[2];
+        load(b[0], g0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load(b[1], g0 + 1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int rounds = (g1 - g0) >> 1;
+        int g = g0;
+        for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                compute(b[d]);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                load(b[d], g + d + 2);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            g += 2;
+        }
+        if (g < g1)
+            compute(b[0]);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // The four waves' partial sums meet in LDS; wave w finishes slabs w, w + 4, ...  Result
+    // lane l holds output columns 16j + 4(l/16) + 0..3 of row 16 mb + l % 16: 8 bytes of C.
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            red[((wave * MB + mb) * NS + i) * 64 + lane] = acc[mb][i];
+    __syncthreads();
+#pragma unroll
+    for (int i0 = 0; i0 < NS; i0 += kWaves) {
+        const int i = i0 + wave;
+        if (i < NS && j0 + i < S) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                f4 v = red[((0 * MB + mb) * NS + i) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w)
+                    v += red[((w * MB + mb) * NS + i) * 64 + lane];
+                const uint32_t lo = static_cast<uint32_t>(float_to_half_bits(v[0])) |
+                                    (static_cast<uint32_t>(float_to_half_bits(v[1])) << 16);
+                const uint32_t hi = static_cast<uint32_t>(float_to_half_bits(v[2])) |
+                                    (static_cast<uint32_t>(float_to_half_bits(v[3])) << 16);
+                typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+                const uint32_t voff = (static_cast<uint32_t>(16 * mb + c) * p.N + 16 * (j0 + i) +
+                                       4 * (lane >> 4)) * 2;
+                __builtin_amdgcn_raw_buffer_store_b64(u2{lo, hi}, rC, voff, 0, 0);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------- host side
 
 struct Config {
@@ -1743,6 +1951,92 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     if (zero_points)
         return col ? dispatch<Fmt<true, true>>(c, p, s) : dispatch<Fmt<true, false>>(c, p, s);
     return col ? dispatch<Fmt<false, true>>(c, p, s) : dispatch<FmtSym>(c, p, s);
+}
+
+namespace {
+
+template <int MB, int NS>
+hipError_t launch_sparse(const Params &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((w4a16_gemm_sparse_kernel<MB, NS>), dim3(p.W), dim3(kThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+// Most slabs per workgroup each row-block count allows without spilling (1, 2, 4 blocks of
+// 16 rows hold 4, 8, 16 A registers per 32-k step and buffer).
+constexpr int kSparseMaxNS[3] = {8, 6, 3};
+
+hipError_t dispatch_sparse(int mb, int ns, const Params &p, hipStream_t s)
+{
+    switch (mb * 16 + ns) {
+    case 17: return launch_sparse<1, 1>(p, s);
+    case 18: return launch_sparse<1, 2>(p, s);
+    case 19: return launch_sparse<1, 3>(p, s);
+    case 20: return launch_sparse<1, 4>(p, s);
+    case 21: return launch_sparse<1, 5>(p, s);
+    case 22: return launch_sparse<1, 6>(p, s);
+    case 23: return launch_sparse<1, 7>(p, s);
+    case 24: return launch_sparse<1, 8>(p, s);
+    case 33: return launch_sparse<2, 1>(p, s);
+    case 34: return launch_sparse<2, 2>(p, s);
+    case 35: return launch_sparse<2, 3>(p, s);
+    case 36: return launch_sparse<2, 4>(p, s);
+    case 37: return launch_sparse<2, 5>(p, s);
+    case 38: return launch_sparse<2, 6>(p, s);
+    case 65: return launch_sparse<4, 1>(p, s);
+    case 66: return launch_sparse<4, 2>(p, s);
+    case 67: return launch_sparse<4, 3>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+extern "C" int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16_t *scales,
+                             void *C, int M, int K, int N, void *stream)
+{
+    if (!A || !packed || !scales || !C || M < 0 || K < 0 || N < 0)
+        return W4A16_EINVAL;
+    int rc = check_gemm_shape(M, K, N);
+    if (rc != W4A16_OK)
+        return rc;
+    // 256-column parameter groups; the dead loads point 2 GiB past the buffer starts
+    if (N % 256 || static_cast<uint64_t>(K) * static_cast<uint64_t>(N) * 3 / 8 >= kOutside ||
+        static_cast<uint64_t>(64) * static_cast<uint64_t>(K) * 2 >= kOutside)
+        return W4A16_ESHAPE;
+    DeviceInfo d;
+    rc = current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    if (M == 0)
+        return W4A16_OK;
+    const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int S = N / 16;
+    const int per = 2 * d.cus;
+    int ns = (S + per - 1) / per;
+    const int nsmax = kSparseMaxNS[mb == 1 ? 0 : (mb == 2 ? 1 : 2)];
+    if (ns > nsmax)
+        ns = nsmax;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // rows in launches of 16 * mb
+    for (int r0 = 0; r0 < M; r0 += 16 * mb) {
+        Params p{};
+        p.A = static_cast<const uint16_t *>(A) + static_cast<size_t>(r0) * K;
+        p.packed = reinterpret_cast<const u4 *>(packed);
+        p.scales = scales;
+        p.C = static_cast<uint16_t *>(C) + static_cast<size_t>(r0) * N;
+        p.M = M - r0 < 16 * mb ? M - r0 : 16 * mb;
+        p.K = K;
+        p.N = N;
+        p.G = K / kGroup;
+        p.Gs = p.G;
+        p.P = 1;
+        p.W = (S + ns - 1) / ns;
+        if (dispatch_sparse(mb, ns, p, s) != hipSuccess)
+            return W4A16_EHIP;
+    }
+    return W4A16_OK;
 }
 
 extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,

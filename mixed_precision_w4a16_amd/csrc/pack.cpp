@@ -115,6 +115,97 @@ uint16_t zero_term(uint8_t z)
     return static_cast<uint16_t>(0x6400 | z);
 }
 
+// 2:4-sparse layout (w4a16_pack_24): per 128 x 16 block, lane l (0..63) owns 3 words at
+// 3l: column 16j + l % 16; word 3l + s (s = 0, 1) holds the 8 kept codes of rows
+// 128g + 64s + 16(l / 16) + 0..15 (two per group of four rows, in row order: kept code e of
+// group e / 2, in nibble kNibble[e]); word 3l + 2 holds their positions in the group, 2 bits
+// each, code e of step s at bits 16s + 2e.
+constexpr size_t kSparseBlockWords = 192;
+
+// Kept positions of the group of four codes c[0..3]: the nonzero weights (code != 8) in row
+// order, completed by the lowest other positions.  False if more than two are nonzero.
+bool kept_pair(const uint8_t (&c)[4], int (&pos)[2])
+{
+    int n = 0;
+    for (int i = 0; i < 4; ++i)
+        if (c[i] != 8) {
+            if (n == 2)
+                return false;
+            pos[n++] = i;
+        }
+    for (int i = 0; i < 4 && n < 2; ++i)      // lowest positions not yet taken
+        if (n == 0 || pos[0] != i)
+            pos[n++] = i;
+    if (pos[0] > pos[1]) {
+        const int t = pos[0];
+        pos[0] = pos[1];
+        pos[1] = t;
+    }
+    return true;
+}
+
+bool pack_codes_24(const uint8_t *codes, size_t nk, size_t nn, uint32_t *packed_out)
+{
+    const size_t G = nk / W4A16_GROUP;
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < G; ++g) {
+            uint32_t *blk = packed_out + (j * G + g) * kSparseBlockWords;
+            for (int l = 0; l < 64; ++l) {
+                const size_t n = j * 16 + (l & 15);
+                uint32_t idx = 0;
+                for (int s = 0; s < 2; ++s) {
+                    uint32_t w = 0;
+                    for (int p = 0; p < 4; ++p) {
+                        const size_t k4 = g * W4A16_GROUP + 64 * s + 16 * (l >> 4) + 4 * p;
+                        uint8_t c[4];
+                        for (int i = 0; i < 4; ++i)
+                            c[i] = codes[(k4 + i) * nn + n];
+                        int pos[2];
+                        if (!kept_pair(c, pos))
+                            return false;
+                        for (int i = 0; i < 2; ++i) {
+                            const int e = 2 * p + i;
+                            w |= static_cast<uint32_t>(c[pos[i]]) << (4 * kNibble[e]);
+                            idx |= static_cast<uint32_t>(pos[i]) << (16 * s + 2 * e);
+                        }
+                    }
+                    blk[3 * l + s] = w;
+                }
+                blk[3 * l + 2] = idx;
+            }
+        }
+    return true;
+}
+
+bool unpack_codes_24(const uint32_t *packed, size_t nk, size_t nn, uint8_t *codes_out)
+{
+    const size_t G = nk / W4A16_GROUP;
+    for (size_t i = 0; i < nk * nn; ++i)
+        codes_out[i] = 8;
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < G; ++g) {
+            const uint32_t *blk = packed + (j * G + g) * kSparseBlockWords;
+            for (int l = 0; l < 64; ++l) {
+                const size_t n = j * 16 + (l & 15);
+                const uint32_t idx = blk[3 * l + 2];
+                for (int s = 0; s < 2; ++s)
+                    for (int p = 0; p < 4; ++p) {
+                        const size_t k4 = g * W4A16_GROUP + 64 * s + 16 * (l >> 4) + 4 * p;
+                        const int e0 = 2 * p;
+                        const uint32_t p0 = (idx >> (16 * s + 2 * e0)) & 3;
+                        const uint32_t p1 = (idx >> (16 * s + 2 * e0 + 2)) & 3;
+                        if (p0 >= p1)
+                            return false;      // not written by w4a16_pack_24
+                        codes_out[(k4 + p0) * nn + n] = static_cast<uint8_t>(
+                            (blk[3 * l + s] >> (4 * kNibble[e0])) & 0xF);
+                        codes_out[(k4 + p1) * nn + n] = static_cast<uint8_t>(
+                            (blk[3 * l + s] >> (4 * kNibble[e0 + 1])) & 0xF);
+                    }
+            }
+        }
+    return true;
+}
+
 }  // namespace
 
 extern "C" int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int group,
@@ -205,13 +296,50 @@ extern "C" int w4a16_unpack_zp(const uint32_t *packed, const uint16_t *params, i
     return W4A16_OK;
 }
 
+extern "C" int w4a16_pack_24(const uint8_t *codes, const uint16_t *scales, int K, int N,
+                             uint32_t *packed_out, uint16_t *scales_out)
+{
+    int rc = check_shape(codes, scales, packed_out, scales_out, K, N, W4A16_GROUP);
+    if (rc != W4A16_OK)
+        return rc;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    if (!codes_valid(codes, nk * nn) || !pack_codes_24(codes, nk, nn, packed_out))
+        return W4A16_EINVAL;
+    const size_t G = nk / W4A16_GROUP;
+    const size_t Q = slabs_per_scale_group(nn);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < G; ++g)
+            for (size_t c = 0; c < 16; ++c)
+                scales_out[scale_index(j, g, c, G, Q)] = scales[g * nn + j * 16 + c];
+    return W4A16_OK;
+}
+
+extern "C" int w4a16_unpack_24(const uint32_t *packed, const uint16_t *scales_packed, int K,
+                               int N, uint8_t *codes_out, uint16_t *scales_out)
+{
+    int rc = check_shape(packed, scales_packed, codes_out, scales_out, K, N, W4A16_GROUP);
+    if (rc != W4A16_OK)
+        return rc;
+    const size_t nk = static_cast<size_t>(K), nn = static_cast<size_t>(N);
+    if (!unpack_codes_24(packed, nk, nn, codes_out))
+        return W4A16_EINVAL;
+    const size_t G = nk / W4A16_GROUP;
+    const size_t Q = slabs_per_scale_group(nn);
+    for (size_t j = 0; j < nn / 16; ++j)
+        for (size_t g = 0; g < G; ++g)
+            for (size_t c = 0; c < 16; ++c)
+                scales_out[g * nn + j * 16 + c] = scales_packed[scale_index(j, g, c, G, Q)];
+    return W4A16_OK;
+}
+
 extern "C" const char *w4a16_status_string(int status)
 {
     switch (status) {
     case W4A16_OK:
         return "ok";
     case W4A16_EINVAL:
-        return "invalid argument (null pointer, negative size, code or zero point above 15)";
+        return "invalid argument (null pointer, negative size, code or zero point above 15, or "
+               "more than 2 non-zero weights in a group of 4 for the 2:4-sparse format)";
     case W4A16_ESHAPE:
         return "unsupported shape (group must be 128 or K, K a positive multiple of 128, "
                "N a positive multiple of 64)";

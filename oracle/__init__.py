@@ -14,6 +14,11 @@ Two independent implementations live here:
 * ``decode_along_k`` / ``decode_along_n``: checkpoint-style packed words (8 codes per word,
   along K or along N in a given nibble order) to codes, what the load-time repack must move.
 
+2:4-sparse weights (MARLIN paper, sec. 1 "Contribution" and sec. 2.1.1: of every 4 consecutive
+weights along K two are zero; Sparse-MARLIN section of the deep-dive page) need no routine of
+their own: the product is the same definition with the pruned weights zero, i.e. code 8 in the
+symmetric format, and ``gemm`` computes it from those dense codes.
+
 The operation (MARLIN paper, arXiv 2408.11743, sec. 3.4 "Kernel Design"; deep-dive page,
 section "Marlin 要解决的精确问题"):  C = A * Bhat,  Bhat[k, n] = s[k // group, n] * (q[k, n] - z),
 z = 8 (symmetric) or a zero-point code z[k // group, n] in 0..15 (the page's general affine

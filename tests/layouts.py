@@ -63,3 +63,29 @@ def encode_along_n(codes, order=None):
     for i in range(8):
         w |= c[:, :, order[i]].astype(np.uint32) << np.uint32(4 * i)
     return w
+
+
+def layout_reference_24(codes):
+    """w4a16_pack_24's words as the header states them: per 128 x 16 block, lane l's three
+    words -- kept codes of the two 64-row halves, then their positions."""
+    K, N = codes.shape
+    G = K // 128
+    out = np.zeros((N // 16, G, 64, 3), dtype=np.uint32)
+    for j in range(N // 16):
+        for g in range(G):
+            for l in range(64):
+                n = 16 * j + l % 16
+                for s in range(2):
+                    w = 0
+                    for p in range(4):
+                        k4 = 128 * g + 64 * s + 16 * (l // 16) + 4 * p
+                        grp = [int(codes[k4 + i, n]) for i in range(4)]
+                        keep = [i for i in range(4) if grp[i] != 8]
+                        keep += [i for i in range(4) if i not in keep][:2 - len(keep)]
+                        keep.sort()
+                        for i, pos in enumerate(keep):
+                            e = 2 * p + i
+                            w |= grp[pos] << (4 * NIBBLE[e])
+                            out[j, g, l, 2] |= np.uint32(pos << (16 * s + 2 * e))
+                    out[j, g, l, s] = w
+    return out.reshape(-1)

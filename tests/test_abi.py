@@ -23,7 +23,7 @@ GOLDEN = os.path.join(ROOT, "tests", "golden", "paper_constants.json")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -235,3 +235,83 @@ def test_repack_rejects_bad_arguments_before_any_device_call():
     assert R(d, 1, ok_order, d, None, K, 520, 128, d, d, None) == w4.ESHAPE
     assert R(d, 0, None, d, None, K, N, 256, d, d, None) == w4.ESHAPE
     assert R(d, 0, None, d, None, 0, N, 128, d, d, None) == w4.ESHAPE
+
+
+# ------------------------------------------------------------------ 2:4-sparse weights
+
+def _sparse_cases(K, N, seed):
+    from workloads import sparsify_24
+    _, q, s = draw(K, N, 1, seed=seed)
+    q = sparsify_24(q, seed)
+    # some groups with fewer non-zeros: one, and none at all
+    q[0:4, 0] = [8, 8, 3, 8]
+    q[4:8, 1] = [8, 8, 8, 8]
+    q[8:12, 2] = [15, 8, 8, 0]
+    return q, s
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (384, 48), (1024, 256)])
+def test_pack_24_matches_documented_layout(K, N):
+    q, s = _sparse_cases(K, N, K + N)
+    packed, sp = w4.pack_24(q, s)
+    from layouts import layout_reference_24
+    assert np.array_equal(packed, layout_reference_24(q))
+    assert np.array_equal(sp.view(np.uint16), layout_reference(q, s)[1].view(np.uint16))
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (512, 272), (2048, 1024)])
+def test_pack_24_round_trip_is_bit_exact(K, N):
+    q, s = _sparse_cases(K, N, 7 * K + N)
+    q2, s2 = w4.unpack_24(*w4.pack_24(q, s), K, N)
+    assert np.array_equal(q2, q)
+    assert np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+
+
+def test_pack_24_rejects_groups_with_three_nonzero_weights_and_bad_shapes():
+    q, s = _sparse_cases(256, 64, 3)
+    bad = q.copy()
+    bad[4:8, 5] = [1, 8, 2, 3]
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.pack_24(bad, s)
+    assert e.value.status == w4.EINVAL
+    bad = q.copy()
+    bad[9, 9] = 16
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.pack_24(bad, s)
+    assert e.value.status == w4.EINVAL
+    lib = w4.library()
+    d = ctypes.c_void_p(64)
+    assert lib.w4a16_pack_24(d, d, 200, 64, d, d) == w4.ESHAPE
+    assert lib.w4a16_pack_24(d, d, 256, 40, d, d) == w4.ESHAPE
+    assert lib.w4a16_pack_24(None, d, 256, 64, d, d) == w4.EINVAL
+    # unpack refuses positions that pack never writes (two equal positions in a group)
+    packed, sp = w4.pack_24(q, s)
+    packed[2] = 0
+    with pytest.raises(w4.W4A16Error):
+        w4.unpack_24(packed, sp, 256, 64)
+
+
+def test_gemm_24_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(256)
+    assert lib.w4a16_gemm_24(None, d, d, d, 16, 1024, 1024, None) == w4.EINVAL
+    assert lib.w4a16_gemm_24(d, d, d, d, -1, 1024, 1024, None) == w4.EINVAL
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1024, 320, None) == w4.ESHAPE     # N % 256
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1000, 1024, None) == w4.ESHAPE
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 98304, 65536, None) == w4.ESHAPE  # 2.4 GB packed
+
+
+def test_sparsify_24_keeps_two_of_every_four():
+    from workloads import sparsify_24
+    _, q, _ = draw(512, 96, 1, seed=5)
+    z = sparsify_24(q, 5)
+    g = z.reshape(128, 4, 96)
+    assert ((g == 8).sum(axis=1) >= 2).all()
+    assert np.array_equal(z[z != 8], q[z != 8])
+    # every one of the six pairs occurs
+    kept = (np.arange(512) % 4)[:, None] * np.ones((1, 96), int)
+    pairs = set()
+    for a in range(0, 512, 4):
+        for n in range(96):
+            pairs.add(tuple(np.flatnonzero(z[a:a + 4, n] != 8)))
+    assert {(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)} <= pairs

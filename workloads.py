@@ -85,3 +85,27 @@ def draw_zeros(K: int, N: int, seed: int = 0, group: int = GROUP) -> np.ndarray:
 def draw_shape(shape: Shape, seed: int = 0, group: int = GROUP):
     """Inputs for every M of a shape: A has max(Ms) rows; M uses A[:M]."""
     return draw(shape.K, shape.N, max(shape.Ms), seed=seed, sigma=shape.sigma, group=group)
+
+
+# The six ways to keep 2 of 4 positions.
+_PAIRS_24 = np.array([[1, 1, 0, 0], [1, 0, 1, 0], [1, 0, 0, 1], [0, 1, 1, 0], [0, 1, 0, 1],
+                      [0, 0, 1, 1]], dtype=bool)
+
+
+def sparsify_24(q: np.ndarray, seed: int = 0) -> np.ndarray:
+    """2:4 structure along K: in every aligned group of 4 rows of each column two positions,
+    drawn uniformly from the six pairs (numpy.random.default_rng([seed, 2])), keep their code
+    and the other two become 8 (weight 0).  Returns a new uint8 [K, N]."""
+    K, N = q.shape
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    rng = np.random.default_rng([seed, 2])
+    out = np.array(q, dtype=np.uint8, copy=True)
+    step = 4096                                    # rows per chunk, to bound the mask's memory
+    for k0 in range(0, K, step):
+        rows = min(step, K - k0)
+        pick = rng.integers(0, 6, size=(rows // 4, N), dtype=np.uint8)
+        keep = _PAIRS_24[pick].transpose(0, 2, 1).reshape(rows, N)     # [rows, N]
+        blk = out[k0:k0 + rows]
+        blk[~keep] = 8
+    return out
