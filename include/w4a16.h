@@ -125,8 +125,9 @@ int w4a16_unpack_zp(const uint32_t *packed, const uint16_t *params, int K, int N
                     uint8_t *codes_out, uint16_t *scales_out, uint8_t *zeros_out);
 
 /*
- * Bytes of device workspace w4a16_gemm needs for this shape on the current device (a fixed
- * 4 KiB counter area plus room for fp32 partial output tiles), written to *bytes.
+ * Bytes of device workspace w4a16_gemm, w4a16_gemm_ex and w4a16_gemm_24 need for this shape
+ * on the current device (a fixed 4 KiB counter area plus room for fp32 partial output
+ * tiles), written to *bytes.
  * A workspace sized for one shape may be reused for any shape whose requirement is not
  * larger.  Returns W4A16_OK, W4A16_EINVAL (bytes == NULL, negative size), W4A16_ESHAPE
  * (as w4a16_gemm), W4A16_EUNSUPPORTED (current device is not gfx950) or W4A16_EHIP.
@@ -212,14 +213,18 @@ int w4a16_unpack_24(const uint32_t *packed, const uint16_t *scales_packed, int K
                     uint8_t *codes_out, uint16_t *scales_out);
 
 /*
- * C = A * Bhat with 2:4-sparse Bhat from w4a16_pack_24 (device, asynchronous on `stream`).
- * A, C, alignment and the size limits as w4a16_gemm; packed and scales as w4a16_pack_24 wrote
- * them (device copies).  No workspace.  N must be a multiple of 256, and K*N*3/8 and 128*K
- * below 2^31 bytes.  M == 0 is a no-op.  Errors: W4A16_EINVAL (null pointer, negative size),
- * W4A16_ESHAPE (shape or limit), W4A16_EUNSUPPORTED (not gfx950), W4A16_EHIP (launch failure).
+ * C = A * Bhat with 2:4-sparse Bhat from w4a16_pack_24 (device, asynchronous on `stream`),
+ * on the structured-sparse matrix instruction, computed transposed as C^T = Bhat^T A^T
+ * (Sparse-MARLIN section of the deep-dive page).  A, C, workspace (at least
+ * w4a16_workspace_size(M, K, N) bytes, first 4 KiB zero, one call at a time), alignment and
+ * the size limits as w4a16_gemm; packed and scales as w4a16_pack_24 wrote them (device
+ * copies).  N must be a multiple of 256, and K*N*3/8 and 128*K below 2^31 bytes.  Sums are
+ * formed in a fixed order: results repeat bit for bit.  M == 0 is a no-op.  Errors:
+ * W4A16_EINVAL (null pointer, negative size), W4A16_ESHAPE (shape or limit),
+ * W4A16_EUNSUPPORTED (not gfx950), W4A16_EHIP (launch failure).
  */
 int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,
-                  int M, int K, int N, void *stream);
+                  int M, int K, int N, void *workspace, void *stream);
 
 /*
  * Device-side load-time conversion of checkpoint-style packed tensors into the layouts of

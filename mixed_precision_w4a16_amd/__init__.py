@@ -64,7 +64,7 @@ _lib.w4a16_pack_24.argtypes = [_p, _p, _i, _i, _p, _p]
 _lib.w4a16_pack_24.restype = _i
 _lib.w4a16_unpack_24.argtypes = [_p, _p, _i, _i, _p, _p]
 _lib.w4a16_unpack_24.restype = _i
-_lib.w4a16_gemm_24.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p]
+_lib.w4a16_gemm_24.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _p]
 _lib.w4a16_gemm_24.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
@@ -300,8 +300,8 @@ def unpack_24(packed: np.ndarray, scales_p: np.ndarray, K: int, N: int):
     return codes, scales
 
 
-def gemm_24(A, packed, scales, N: int, out=None, stream=None):
-    """C[M, N] = A @ Bhat for 2:4-sparse Bhat from to_device(pack_24(...))."""
+def gemm_24(A, packed, scales, N: int, out=None, ws=None, stream=None):
+    """C[M, N] = A @ Bhat for 2:4-sparse Bhat from to_device(pack_24(...)); ws as for gemm."""
     import torch
     if A.dtype != torch.float16 or not A.is_cuda or A.dim() != 2 or not A.is_contiguous():
         raise ValueError("A must be a contiguous fp16 CUDA tensor of shape [M, K]")
@@ -321,9 +321,11 @@ def gemm_24(A, packed, scales, N: int, out=None, stream=None):
     if M == 0:
         return out
     with torch.cuda.device(A.device):
+        if ws is None:
+            ws = workspace(M, K, N, A.device)
         if stream is None:
             stream = torch.cuda.current_stream(A.device)
         _check("w4a16_gemm_24", _lib.w4a16_gemm_24(A.data_ptr(), packed.data_ptr(),
                                                    scales.data_ptr(), out.data_ptr(), M, K, N,
-                                                   stream.cuda_stream))
+                                                   ws.data_ptr(), stream.cuda_stream))
     return out

@@ -71,6 +71,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16 __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u3 __attribute__((ext_vector_type(3)));
 
 constexpr int kThreads = 256;                 // 4 waves of 64
 constexpr int kWaves = 4;
@@ -93,16 +94,22 @@ struct Params {
     long long T;              // total tiles = (N / Nt) * P * G
 };
 
-// Packed format: zero points (per group and column, else the fixed 8) and where the scale
-// sits (per 128-row group, or one per column applied once at the end).
-template <bool ZP_, bool COL_>
+// Packed format: zero points (per group and column, else the fixed 8), where the scale
+// sits (per 128-row group, or one per column applied once at the end), and whether the
+// weights are 2:4-sparse along K (w4a16_pack_24: group-128 scales, z = 8).
+template <bool ZP_, bool COL_, bool SP_ = false>
 struct Fmt {
+    static_assert(!SP_ || (!ZP_ && !COL_), "2:4-sparse weights have group scales and z = 8");
     static constexpr bool ZP = ZP_;
     static constexpr bool COL = COL_;
+    static constexpr bool SP = SP_;
     // the K loop needs per-tile parameters unless the scale is per column and z is fixed
     static constexpr bool kTileParams = ZP_ || !COL_;
+    // bytes of one 128 x 16 weight block and of one lane's share of it
+    static constexpr uint32_t kBlockBytes = SP_ ? 768u : 1024u;
 };
 using FmtSym = Fmt<false, false>;
+using FmtSp = Fmt<false, false, true>;
 
 // (a & m) | o in one VALU op.  gfx9 VOP3 encodings take no literal and read at most one
 // SGPR, so left to itself the compiler splits this into v_and + v_or; the "v" constraints
@@ -355,17 +362,28 @@ __device__ __forceinline__ void zero_consts(const uint32_t (&pr)[PRegs<NBW, ZP, 
 // pages' evict_first hint) and A stays in the L2.  64-row tiles can run several row
 // sub-problems that re-read a slice's weights right away, and measure faster with the weights
 // left in the cache.
+// A lane's share of one weight block: 16 bytes (8 codes of each of 4 32-k steps), or for
+// 2:4-sparse weights 12 (the kept codes of the block's two 64-k steps and their positions).
+template <class F>
+using WQuad = std::conditional_t<F::SP, u3, u4>;
+
 template <int MB, int NBW, class F>
 __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rS,
                                        int G, int lane, uint32_t wblk, uint32_t sblk,
-                                       u4 (&wq)[NBW], uint32_t (&pr)[TileRegs<NBW, F>::n])
+                                       WQuad<F> (&wq)[NBW], uint32_t (&pr)[TileRegs<NBW, F>::n])
 {
     constexpr int policy = MB <= 2 ? kNonTemporal : 0;
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
-        wq[b] = __builtin_bit_cast(
-            u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * 1024u, policy));
+        if constexpr (F::SP)
+            wq[b] = __builtin_bit_cast(
+                u3, __builtin_amdgcn_raw_buffer_load_b96(rW, lane * 12, blk * F::kBlockBytes,
+                                                         policy));
+        else
+            wq[b] = __builtin_bit_cast(
+                u4, __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16, blk * F::kBlockBytes,
+                                                          policy));
     }
     if constexpr (F::kTileParams)
         load_params<NBW, F::ZP, tile_part<F>()>(rS, lane, sblk, pr);
@@ -382,12 +400,12 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
 // rounding of s * (q - z) to fp16 is below 2^-11 relative per weight.
 template <int MB, class F>
 struct ScaleMode {
-    static constexpr bool kWeights = !F::COL && MB >= 4;
-    static constexpr bool kPartial = !F::COL && MB < 4;
+    static constexpr bool kWeights = !F::COL && (MB >= 4 || F::SP);
+    static constexpr bool kPartial = !F::COL && MB < 4 && !F::SP;
 };
 
 template <int MB, int NBW, class F>
-__device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4 (&wq)[NBW],
+__device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const WQuad<F> (&wq)[NBW],
                                              const uint32_t (&pr)[TileRegs<NBW, F>::n],
                                              f4 (&acc)[MB][NBW], uint32_t mlo, uint32_t mhi,
                                              uint32_t magic)
@@ -422,7 +440,35 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const u4
         for (int t = 0; t < 4; ++t)
             a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
 
-    if constexpr (!ScaleMode<MB, F>::kPartial) {
+    if constexpr (F::SP) {
+        // The transposed product on the sparse instruction (see the 2:4 kernel below): the
+        // lane's decoded weights are the sparse operand (row = the lane's column), A fragments
+        // 2h and 2h + 1 together are the dense operand of 64-k step h.
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const h8 x0 = dequant8_scaled(wq[b][0], s2[b], mlo, mhi, magic, zsub[b], zadd[b]);
+            const h8 x1 = dequant8_scaled(wq[b][1], s2[b], mlo, mhi, magic, zsub[b], zadd[b]);
+            const int idx0 = static_cast<int>(wq[b][2]);
+            const int idx1 = static_cast<int>(wq[b][2] >> 16);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const h16 d0 = __builtin_shufflevector(a[mb][0], a[mb][1], 0, 1, 2, 3, 4, 5, 6,
+                                                       7, 8, 9, 10, 11, 12, 13, 14, 15);
+                const h16 d1 = __builtin_shufflevector(a[mb][2], a[mb][3], 0, 1, 2, 3, 4, 5, 6,
+                                                       7, 8, 9, 10, 11, 12, 13, 14, 15);
+                acc[mb][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(x0, d0, acc[mb][b], idx0,
+                                                                      0, 0);
+                acc[mb][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(x1, d1, acc[mb][b], idx1,
+                                                                      0, 0);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                asm volatile("" : "+v"(acc[mb][b]));    // finish the update here
+        return;
+    } else if constexpr (!ScaleMode<MB, F>::kPartial) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -483,14 +529,37 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x)
 // through a buffer resource of exactly M * N * 2 bytes: stores to rows at or past M fall
 // outside it and are dropped by the hardware, so no per-row test is needed.  The lane's own
 // offset is one VGPR; the tile's position and the (mb, r) row are a running scalar offset and
-// 16b columns an immediate.
-template <int MB, int NBW, int WAVES = kWaves>
+// 16b columns an immediate.  TR: the transposed product of the 2:4-sparse weights, where
+// acc[mb][b][r] is C[row0 + 16mb + lane%16][col0 + 16b + 4(lane/16) + r], 8 bytes a lane.
+template <int MB, int NBW, int WAVES = kWaves, bool TR = false>
 __device__ __forceinline__ void write_c(const Params &p, __amdgpu_buffer_rsrc_t rC, int wave,
                                         int lane, long long sigma, const f4 (&acc)[MB][NBW])
 {
     const long long s = sigma / p.P;
     const int pm = static_cast<int>(sigma - s * p.P);
     const uint32_t rowN = opaque(static_cast<uint32_t>(p.N) * 2);
+    if constexpr (TR) {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const uint32_t voff = ((lane & 15) * static_cast<uint32_t>(p.N) + wave * NBW * 16 +
+                               4 * (lane >> 4)) * 2;
+        uint32_t srow = __builtin_amdgcn_readfirstlane(
+            (static_cast<uint32_t>(pm * 16 * MB) * static_cast<uint32_t>(p.N) +
+             static_cast<uint32_t>(s) * Tile<MB, NBW, WAVES>::Nt) * 2);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const f4 v = acc[mb][b];
+                const uint32_t lo = static_cast<uint32_t>(float_to_half_bits(v[0])) |
+                                    (static_cast<uint32_t>(float_to_half_bits(v[1])) << 16);
+                const uint32_t hi = static_cast<uint32_t>(float_to_half_bits(v[2])) |
+                                    (static_cast<uint32_t>(float_to_half_bits(v[3])) << 16);
+                __builtin_amdgcn_raw_buffer_store_b64(u2{lo, hi}, rC, voff + 32 * b, srow, 0);
+            }
+            srow += 16 * rowN;
+        }
+        return;
+    }
     const uint32_t voff = ((4 * (lane >> 4)) * static_cast<uint32_t>(p.N) + wave * NBW * 16 +
                            (lane & 15)) * 2;
     uint32_t srow = __builtin_amdgcn_readfirstlane(
@@ -584,7 +653,7 @@ __device__ __forceinline__ int slot_of(const Params &p, long long sigma, int w)
 // from its slot like the others: either way the additions are the same.  Partials are read
 // past the L2 with device-scope loads, half a tile at a time so that the loads in flight fit
 // in the registers next to the sum (spilling would serialise them).
-template <int MB, int NBW, int WAVES = kWaves>
+template <int MB, int NBW, int WAVES = kWaves, bool TR = false>
 __device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rsrc_t rP,
                                              __amdgpu_buffer_rsrc_t rC, long long sigma,
                                              int w_lo, int w_hi, int wave, int lane,
@@ -618,7 +687,7 @@ __device__ __forceinline__ void reduce_slice(const Params &p, __amdgpu_buffer_rs
                     acc[h + mb][b] += x[mb][b];
         }
     }
-    write_c<MB, NBW, WAVES>(p, rC, wave, lane, sigma, acc);
+    write_c<MB, NBW, WAVES, TR>(p, rC, wave, lane, sigma, acc);
 }
 
 // End of a slice (or of the stripe) for the running accumulators.  With one scale per
@@ -653,7 +722,7 @@ __device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_
     }
     const long long s0 = sigma * p.G;
     if (t0 <= s0 && t == s0 + p.G - 1) {
-        write_c<MB, NBW, WAVES>(p, rC, wave, lane, sigma, acc);
+        write_c<MB, NBW, WAVES, F::SP>(p, rC, wave, lane, sigma, acc);
     } else if (t0 <= s0) {
         own = sigma;
     } else {
@@ -690,7 +759,7 @@ __device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_
 constexpr int kArrived = 1 << 16;
 constexpr int kCountMask = kArrived - 1;
 
-template <int MB, int NBW, int WAVES = kWaves>
+template <int MB, int NBW, int WAVES = kWaves, bool TR = false>
 __device__ __forceinline__ void settle(const Params &p, __amdgpu_buffer_rsrc_t rP,
                                        __amdgpu_buffer_rsrc_t rC, int stripe, long long nonown,
                                        long long own, int tid, f4 (&acc)[MB][NBW], int *flag)
@@ -714,7 +783,7 @@ __device__ __forceinline__ void settle(const Params &p, __amdgpu_buffer_rsrc_t r
         const int w_hi = stripe_owner(own * p.G + p.G - 1, p.T, p.W);
         const int c = w_hi - stripe + 1;
         if ((flag[1] & kCountMask) == c - 1) {
-            reduce_slice<MB, NBW, WAVES>(p, rP, rC, own, stripe, w_hi, wave, lane, true, acc);
+            reduce_slice<MB, NBW, WAVES, TR>(p, rP, rC, own, stripe, w_hi, wave, lane, true, acc);
             if (tid == 0)
                 __hip_atomic_store(p.counters + stripe, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
@@ -726,7 +795,7 @@ __device__ __forceinline__ void settle(const Params &p, __amdgpu_buffer_rsrc_t r
                                                  __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             if (((flag[1] + 1) & kCountMask) == c) {
-                reduce_slice<MB, NBW, WAVES>(p, rP, rC, own, stripe, w_hi, wave, lane, false, acc);
+                reduce_slice<MB, NBW, WAVES, TR>(p, rP, rC, own, stripe, w_hi, wave, lane, false, acc);
                 if (tid == 0)
                     __hip_atomic_store(p.counters + stripe, 0, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -738,7 +807,7 @@ __device__ __forceinline__ void settle(const Params &p, __amdgpu_buffer_rsrc_t r
         const int w_hi = stripe_owner(nonown * p.G + p.G - 1, p.T, p.W);
         const int v = flag[0] + 1;
         if ((v & kArrived) && (v & kCountMask) == w_hi - w_lo + 1) {
-            reduce_slice<MB, NBW, WAVES>(p, rP, rC, nonown, w_lo, w_hi, wave, lane, false, acc);
+            reduce_slice<MB, NBW, WAVES, TR>(p, rP, rC, nonown, w_lo, w_hi, wave, lane, false, acc);
             if (tid == 0)
                 __hip_atomic_store(p.counters + w_lo, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -769,8 +838,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
 
     const __amdgpu_buffer_rsrc_t rA =
         make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
-    const __amdgpu_buffer_rsrc_t rW =
-        make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(
+        p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N * (F::SP ? 3 : 4) / 8));
     const __amdgpu_buffer_rsrc_t rS = make_rsrc(
         p.scales, static_cast<uint32_t>(static_cast<size_t>(p.Gs) * p.N * (F::ZP ? 4 : 2)));
     const __amdgpu_buffer_rsrc_t rP =
@@ -838,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     // weight load of the same tile, so waiting for A(i+1) never waits for a weight tile that
     // is not needed yet: each weight tile has one whole tile of compute to arrive in.
     u4 ar[MB];
-    u4 wq0[NBW], wq1[NBW];
+    WQuad<F> wq0[NBW], wq1[NBW];
     uint32_t sc0[TileRegs<NBW, F>::n], sc1[TileRegs<NBW, F>::n];
     int st_cp = 0, st_st = 1;             // ring stages being computed from / stored to
     auto next_stage = [](int x) { return x == TL::kStages - 1 ? 0 : x + 1; };
@@ -910,7 +979,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         end_of_tile();
     }
     slice_end<MB, NBW, F>(p, rP, rC, rS, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
-    settle<MB, NBW>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
+    settle<MB, NBW, kWaves, F::SP>(p, rP, rC, stripe, nonown, own, tid, acc, flag);
 }
 
 // ------------------------------------------------------------------- wide tile, M >= 128
@@ -1061,8 +1130,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
     const __amdgpu_buffer_rsrc_t rA =
         make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
-    const __amdgpu_buffer_rsrc_t rW =
-        make_rsrc(p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N / 2));
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(
+        p.packed, static_cast<uint32_t>(static_cast<size_t>(p.K) * p.N * (F::SP ? 3 : 4) / 8));
     const __amdgpu_buffer_rsrc_t rS = make_rsrc(
         p.scales, static_cast<uint32_t>(static_cast<size_t>(p.Gs) * p.N * (F::ZP ? 4 : 2)));
     const __amdgpu_buffer_rsrc_t rP =
@@ -1786,6 +1855,23 @@ Config choose_config(int M, int K, int N, int cus)
     return c;
 }
 
+// 2:4-sparse weights with more than 16 rows: the stripe kernel's 32- and 64-row tiles over
+// 256-column slices (N a multiple of 256), as for dense weights but never the 128-row tiles.
+Config choose_config_24(int M, int K, int N, int cus)
+{
+    Config c{};
+    c.MB = M <= 32 ? 2 : 4;
+    c.NBW = 4;
+    c.waves = kWaves;
+    c.G = K / kGroup;
+    c.P = (M + 16 * c.MB - 1) / (16 * c.MB);
+    c.S = N / (16 * c.waves * c.NBW);
+    c.T = static_cast<long long>(c.S) * c.P * c.G;
+    c.W = choose_stripes(c.T, cus, 2);
+    c.NS = 0;
+    return c;
+}
+
 size_t workspace_for(const Config &c)
 {
     if (c.NS > 0)
@@ -1906,7 +1992,10 @@ extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
     rc = current_device(&d);
     if (rc != W4A16_OK)
         return rc;
-    *bytes = M == 0 ? kCounterBytes : workspace_for(choose_config(M, K, N, d.cus));
+    size_t b = M == 0 ? kCounterBytes : workspace_for(choose_config(M, K, N, d.cus));
+    if (M > 16 && N % 256 == 0)
+        b = std::max(b, workspace_for(choose_config_24(M, K, N, d.cus)));
+    *bytes = b;
     return W4A16_OK;
 }
 
@@ -1966,6 +2055,7 @@ hipError_t launch_sparse(const Params &p, hipStream_t stream)
 // Most slabs per workgroup each row-block count allows without spilling (1, 2, 4 blocks of
 // 16 rows hold 4, 8, 16 A registers per 32-k step and buffer).
 constexpr int kSparseMaxNS[3] = {8, 6, 3};
+constexpr int kSparseWholeKRows = 16;   // more rows: the stripe kernel
 
 hipError_t dispatch_sparse(int mb, int ns, const Params &p, hipStream_t s)
 {
@@ -1994,14 +2084,15 @@ hipError_t dispatch_sparse(int mb, int ns, const Params &p, hipStream_t s)
 }  // namespace
 
 extern "C" int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16_t *scales,
-                             void *C, int M, int K, int N, void *stream)
+                             void *C, int M, int K, int N, void *workspace, void *stream)
 {
-    if (!A || !packed || !scales || !C || M < 0 || K < 0 || N < 0)
+    if (!A || !packed || !scales || !C || !workspace || M < 0 || K < 0 || N < 0)
         return W4A16_EINVAL;
     int rc = check_gemm_shape(M, K, N);
     if (rc != W4A16_OK)
         return rc;
-    // 256-column parameter groups; the dead loads point 2 GiB past the buffer starts
+    // 256-column parameter groups; the whole-K kernel's dead loads point 2 GiB past the
+    // buffer starts
     if (N % 256 || static_cast<uint64_t>(K) * static_cast<uint64_t>(N) * 3 / 8 >= kOutside ||
         static_cast<uint64_t>(64) * static_cast<uint64_t>(K) * 2 >= kOutside)
         return W4A16_ESHAPE;
@@ -2011,32 +2102,35 @@ extern "C" int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16
         return rc;
     if (M == 0)
         return W4A16_OK;
-    const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    const int S = N / 16;
-    const int per = 2 * d.cus;
-    int ns = (S + per - 1) / per;
-    const int nsmax = kSparseMaxNS[mb == 1 ? 0 : (mb == 2 ? 1 : 2)];
-    if (ns > nsmax)
-        ns = nsmax;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // rows in launches of 16 * mb
-    for (int r0 = 0; r0 < M; r0 += 16 * mb) {
-        Params p{};
-        p.A = static_cast<const uint16_t *>(A) + static_cast<size_t>(r0) * K;
-        p.packed = reinterpret_cast<const u4 *>(packed);
-        p.scales = scales;
-        p.C = static_cast<uint16_t *>(C) + static_cast<size_t>(r0) * N;
-        p.M = M - r0 < 16 * mb ? M - r0 : 16 * mb;
-        p.K = K;
-        p.N = N;
-        p.G = K / kGroup;
-        p.Gs = p.G;
+    Params p{};
+    p.A = static_cast<const uint16_t *>(A);
+    p.packed = reinterpret_cast<const u4 *>(packed);
+    p.scales = scales;
+    p.C = static_cast<uint16_t *>(C);
+    p.counters = static_cast<int *>(workspace);
+    p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+    p.M = M;
+    p.K = K;
+    p.N = N;
+    p.G = K / kGroup;
+    p.Gs = p.G;
+    if (M <= kSparseWholeKRows) {
+        // whole-K workgroups of NS slabs, two per CU
+        const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        const int S = N / 16;
+        const int per = 2 * d.cus;
+        const int ns = std::min((S + per - 1) / per, kSparseMaxNS[mb == 1 ? 0 : (mb == 2 ? 1 : 2)]);
         p.P = 1;
         p.W = (S + ns - 1) / ns;
-        if (dispatch_sparse(mb, ns, p, s) != hipSuccess)
-            return W4A16_EHIP;
+        return dispatch_sparse(mb, ns, p, s) == hipSuccess ? W4A16_OK : W4A16_EHIP;
     }
-    return W4A16_OK;
+    const Config c = choose_config_24(M, K, N, d.cus);
+    p.P = c.P;
+    p.W = c.W;
+    p.T = c.T;
+    const hipError_t e = c.MB == 2 ? launch<2, 4, FmtSp>(p, s) : launch<4, 4, FmtSp>(p, s);
+    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
 }
 
 extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t *scales, void *C,

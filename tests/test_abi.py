@@ -294,11 +294,12 @@ def test_pack_24_rejects_groups_with_three_nonzero_weights_and_bad_shapes():
 def test_gemm_24_rejects_bad_arguments_before_any_device_call():
     lib = w4.library()
     d = ctypes.c_void_p(256)
-    assert lib.w4a16_gemm_24(None, d, d, d, 16, 1024, 1024, None) == w4.EINVAL
-    assert lib.w4a16_gemm_24(d, d, d, d, -1, 1024, 1024, None) == w4.EINVAL
-    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1024, 320, None) == w4.ESHAPE     # N % 256
-    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1000, 1024, None) == w4.ESHAPE
-    assert lib.w4a16_gemm_24(d, d, d, d, 16, 98304, 65536, None) == w4.ESHAPE  # 2.4 GB packed
+    assert lib.w4a16_gemm_24(None, d, d, d, 16, 1024, 1024, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1024, 1024, None, None) == w4.EINVAL  # workspace
+    assert lib.w4a16_gemm_24(d, d, d, d, -1, 1024, 1024, d, None) == w4.EINVAL
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1024, 320, d, None) == w4.ESHAPE     # N % 256
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 1000, 1024, d, None) == w4.ESHAPE
+    assert lib.w4a16_gemm_24(d, d, d, d, 16, 98304, 65536, d, None) == w4.ESHAPE  # 2.4 GB
 
 
 def test_sparsify_24_keeps_two_of_every_four():

@@ -68,9 +68,10 @@ def case(K, N, M, seed):
     return A, sparsify_24(q, seed), s
 
 
-# N = 256 .. 16640: 1 to 3 slabs per workgroup (16640: the last workgroup holds two);
-# K = 128 / 384: waves without a K tile; M spans one, two and four 16-row blocks per launch
-# and several launches (M > 64).
+# M <= 16 (whole-K workgroups): N = 256 .. 16640 gives 1 to 3 slabs per workgroup (16640: the
+# last workgroup holds two); K = 128 / 384: waves without a K tile.  M > 16 (stripes of
+# 32- and 64-row tiles): one to three row sub-problems (65, 130), slices split between
+# several workgroups (K = 18432 with N = 256: up to one tile per workgroup) or whole.
 @pytest.mark.parametrize("K,N", [(128, 256), (384, 512), (1024, 1024), (2048, 16640),
                                  (4096, 9216), (18432, 256)])
 @pytest.mark.parametrize("M", [1, 3, 16, 17, 32, 33, 64, 65, 130])
@@ -118,6 +119,22 @@ def test_sparse_no_write_past_the_rows_of_c(M, N):
     torch.cuda.synchronize()
     assert int((buf[M * N:] != -7.0).sum()) == 0
     check(buf[:M * N].view(M, N).cpu().numpy(), oracle.gemm(A, q, s), f"M={M} N={N}")
+
+
+def test_sparse_leaves_the_counters_zero_and_repeats_across_workspaces():
+    # split slices count arrivals in the workspace's first 4 KiB; every call leaves them 0
+    K, N, M = 4096, 1024, 50
+    A, q, s = case(K, N, M, seed=77)
+    W = Sparse(q, s)
+    Ad = torch.from_numpy(A).cuda()
+    ws = w4.new_workspace(M, K, N, "cuda")
+    C0 = w4.gemm_24(Ad, W.packed, W.scales, N, ws=ws).cpu().numpy()
+    torch.cuda.synchronize()
+    assert int(ws[:4096].count_nonzero()) == 0
+    ws2 = w4.new_workspace(M, K, N, "cuda")
+    C1 = w4.gemm_24(Ad, W.packed, W.scales, N, ws=ws2).cpu().numpy()
+    assert np.array_equal(bits(C0), bits(C1))
+    check(C0, oracle.gemm(A, q, s), "counters")
 
 
 @pytest.mark.slow
