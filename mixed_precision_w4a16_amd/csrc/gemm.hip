@@ -58,6 +58,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <type_traits>
 
@@ -1806,16 +1807,49 @@ int check_gemm_shape(int M, int K, int N)
     return W4A16_OK;
 }
 
-// Number of stripes: a whole number of workgroups per CU, so every CU streams the same
-// amount (a fractional count leaves some CUs with one workgroup more than others).
-int choose_stripes(long long T, int cus, int per_cu)
+// Number of stripes W, from a cost model of the stripe kernel fitted to timings on gfx950
+// (K 4096 .. 28672, N 4096 .. 73728, M 24 .. 128).  A stripe's tiles stream one after the
+// other, each taking the longer of a latency floor (loads run two tiles ahead: about 1.1 us
+// with 16- and 32-row tiles, 1.3 us with more rows) and its share of HBM bandwidth with W
+// tiles in flight (6 TB/s); a slice split into n pieces
+// is summed by one workgroup at about 0.8 us a piece.  Many stripes buy bandwidth, few buy
+// short sums: a 4096 x 4096 weight at M = 24 takes 27 us with 512 one-tile stripes (32 pieces
+// a slice) and 12 us with 128.  W is two per CU or at most one per CU, so that every CU
+// streams the same amount (an uneven count leaves some CUs with twice the work of others).
+int choose_stripes(long long T, int G, int MB, double tile_bytes, int cus)
 {
-    long long w = static_cast<long long>(cus) * per_cu;
-    if (w > kMaxWGs)
-        w = kMaxWGs;
-    if (w > T)
-        w = T;
-    return static_cast<int>(w);
+    const long long wmax = std::min<long long>({2LL * cus, kMaxWGs, T});
+    const double floor_us = MB <= 2 ? 1.1 : 1.3;
+    auto cost = [&](long long W) {
+        const long long tps = (T + W - 1) / W;               // tiles of the longest stripe
+        const double per_tile =
+            std::max(floor_us, static_cast<double>(W) * tile_bytes / 6.0e6);
+        // stripes sharing a slice: one more where stripe and slice ends do not line up
+        const double per = static_cast<double>(T) / static_cast<double>(W);
+        const bool aligned = T % W == 0 && (G % tps == 0 || tps % G == 0);
+        const double pieces = std::ceil(G / per) + (aligned ? 0.0 : 1.0);
+        return static_cast<double>(tps) * per_tile + 0.8 * pieces;
+    };
+    // fewer stripes than two per CU only for a clear gain: where both are bandwidth-bound
+    // the model ties them, and two workgroups per CU hide latency better
+    long long best = wmax;
+    double tb = 0.95 * cost(wmax);
+    for (long long W = std::min<long long>(cus, wmax); W >= 1; --W) {
+        const double t = cost(W);
+        if (t < tb) {
+            tb = t;
+            best = W;
+        }
+    }
+    return static_cast<int>(best);
+}
+
+// HBM bytes of one stripe-kernel tile: Nt columns x 128 rows of codes (4 bits, or 3 per
+// weight for 2:4-sparse blocks), the Mt x 128 A tile, one fp16 parameter per column.
+double tile_bytes(int MB, int NBW, bool sparse)
+{
+    const double nt = 16.0 * kWaves * NBW;
+    return nt * kGroup * (sparse ? 0.375 : 0.5) + 16.0 * MB * kGroup * 2 + nt * 2;
 }
 
 Config choose_config(int M, int K, int N, int cus)
@@ -1848,26 +1882,26 @@ Config choose_config(int M, int K, int N, int cus)
         }
     c.S = N / (16 * c.waves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
-    c.W = choose_stripes(c.T, cus, per_cu);
+    c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, false), cus);
     c.NS = skinny_slabs(M, K, N, cus);
     if (c.NS > 0)
         c.W = (N / 16 + c.NS - 1) / c.NS;
     return c;
 }
 
-// 2:4-sparse weights with more than 16 rows: the stripe kernel's 32- and 64-row tiles over
-// 256-column slices (N a multiple of 256), as for dense weights but never the 128-row tiles.
+// 2:4-sparse weights on the stripe kernel: 16-, 32- and 64-row tiles over 256-column slices
+// (N a multiple of 256), as for dense weights but never the 128-row tiles.
 Config choose_config_24(int M, int K, int N, int cus)
 {
     Config c{};
-    c.MB = M <= 32 ? 2 : 4;
+    c.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     c.NBW = 4;
     c.waves = kWaves;
     c.G = K / kGroup;
     c.P = (M + 16 * c.MB - 1) / (16 * c.MB);
     c.S = N / (16 * c.waves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
-    c.W = choose_stripes(c.T, cus, 2);
+    c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, true), cus);
     c.NS = 0;
     return c;
 }
@@ -1993,7 +2027,7 @@ extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
     if (rc != W4A16_OK)
         return rc;
     size_t b = M == 0 ? kCounterBytes : workspace_for(choose_config(M, K, N, d.cus));
-    if (M > 16 && N % 256 == 0)
+    if (M > 0 && N % 256 == 0)
         b = std::max(b, workspace_for(choose_config_24(M, K, N, d.cus)));
     *bytes = b;
     return W4A16_OK;
@@ -2129,7 +2163,9 @@ extern "C" int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16
     p.P = c.P;
     p.W = c.W;
     p.T = c.T;
-    const hipError_t e = c.MB == 2 ? launch<2, 4, FmtSp>(p, s) : launch<4, 4, FmtSp>(p, s);
+    const hipError_t e = c.MB == 1   ? launch<1, 4, FmtSp>(p, s)
+                         : c.MB == 2 ? launch<2, 4, FmtSp>(p, s)
+                                     : launch<4, 4, FmtSp>(p, s);
     return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
 }
 
