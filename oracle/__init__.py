@@ -19,6 +19,11 @@ weights along K two are zero; Sparse-MARLIN section of the deep-dive page) need 
 their own: the product is the same definition with the pruned weights zero, i.e. code 8 in the
 symmetric format, and ``gemm`` computes it from those dense codes.
 
+A mixture-of-experts layer (deep-dive page, the section on where the format pays off, items 1
+and 4: the layer regroups tokens by expert, so each expert's product has its own M) is
+``moe_align`` (the regrouping) and ``moe_gemm`` (each assignment's row times its expert's
+dequantised weights), in fp64 with one rounding to fp16 or bfloat16 (``bf16_round``).
+
 The operation (MARLIN paper, arXiv 2408.11743, sec. 3.4 "Kernel Design"; deep-dive page,
 section "Marlin 要解决的精确问题"):  C = A * Bhat,  Bhat[k, n] = s[k // group, n] * (q[k, n] - z),
 z = 8 (symmetric) or a zero-point code z[k // group, n] in 0..15 (the page's general affine
@@ -272,3 +277,78 @@ def decode_along_n(qweight, rows: int, N: int, order=None) -> np.ndarray:
     for i in range(8):
         codes[:, order[i]::8] = (w >> np.uint32(4 * i)) & np.uint32(15)
     return codes
+
+
+# --------------------------------------------------------------------------------------------
+# Mixture-of-experts layer: token t's j-th expert is topk_ids[t, j]; assignment a = t*topk + j
+# is row a of the output, computed from row t of A with that expert's weights.  Deep-dive
+# page, section on where the format pays off: item 1 (MoE regroups tokens by expert, so each
+# expert's GEMM sees its own M) and item 4 (grouped GEMM).
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bfloat16 value (8 significant bits, ties to even) of float64 x, as float64.
+    bfloat16 is binary32 cut to 16 bits: same exponent range, 7 stored mantissa bits.  Values
+    here stay far inside the normal range, where this is the whole definition."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                     # x = m * 2^e with 0.5 <= |m| < 1, or m = 0
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of bf16_round(x): the upper half of the binary32 word."""
+    r = bf16_round(x).astype(np.float32)   # exact: 8 significant bits
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_value(bits) -> np.ndarray:
+    """float64 values of bfloat16 bit patterns."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def moe_align(topk_ids, E: int):
+    """The assignments grouped by expert: (sorted_ids int32, offsets int32 [E+1]) with expert
+    e's assignments, in increasing order, at sorted_ids[offsets[e]:offsets[e+1]].  Entries
+    outside 0..E-1 are left out."""
+    flat = np.asarray(topk_ids).reshape(-1)
+    lists = [np.flatnonzero(flat == e) for e in range(E)]
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum([len(x) for x in lists])
+    ids = np.concatenate(lists) if lists else np.zeros(0, dtype=np.int64)
+    return ids.astype(np.int32), offsets.astype(np.int32)
+
+
+def moe_gemm(A, topk_ids, q, s, zeros=None, row_scale=None, act: str = "f16",
+             group: int = 128):
+    """Grouped product of an MoE layer.  A: float [T, K] (values of the activation type),
+    topk_ids int [T, topk], q uint8 [E, K, N], s float [E, K/group, N] (values), zeros
+    optional uint8 [E, K/group, N] (default 8), row_scale optional [T*topk].
+    Returns (C float64 [T*topk, N], each listed row rounded once to fp16 or bfloat16, and a
+    bool mask [T*topk] of the rows computed).  Per expert: Bhat = s (q - z) and
+    C[a] = row_scale[a] * A[a // topk] @ Bhat in fp64."""
+    A = np.asarray(A, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    T, topk = ids.shape
+    E, K, N = q.shape
+    R = T * topk
+    C = np.zeros((R, N), dtype=np.float64)
+    done = np.zeros(R, dtype=bool)
+    order, offsets = moe_align(ids, E)
+    for e in range(E):
+        rows = order[offsets[e]:offsets[e + 1]].astype(np.int64)
+        if rows.size == 0:
+            continue
+        z = 8.0 if zeros is None else np.repeat(np.asarray(zeros[e], np.float64), group, axis=0)
+        W = np.repeat(np.asarray(s[e], np.float64), group, axis=0) * (q[e].astype(np.float64) - z)
+        Y = A[rows // topk] @ W
+        if row_scale is not None:
+            Y = Y * np.asarray(row_scale, dtype=np.float64)[rows][:, None]
+        C[rows] = Y
+        done[rows] = True
+    if act == "f16":
+        C = C.astype(np.float16).astype(np.float64)
+    elif act == "bf16":
+        C = bf16_round(C)
+    else:
+        raise ValueError(act)
+    return C, done

@@ -64,6 +64,29 @@ COMPUTE_SWEEP = Workload("compute_8192x28672_m256_1024", (
 ALL = (SMALL, LARGE, LLAMA2_7B, LLAMA2_70B, COMPUTE_SWEEP)
 
 
+@dataclass(frozen=True)
+class MoeShape:
+    name: str
+    E: int          # experts
+    topk: int       # experts per token
+    K: int
+    N: int
+    Ts: tuple       # tokens per call
+
+
+# Mixture-of-experts layers (the pages name the case, not a model): experts shaped like a
+# Mixtral-8x7B block (8 experts, top-2, hidden 4096, expert width 14336; gate and up fused)
+# and like a 64-expert, top-6 block with hidden 2048 and expert width 1408.
+MOE_8E = Workload("moe_8e_top2_4096", (
+    MoeShape("8e_gate_up", 8, 2, 4096, 28672, (1, 4, 16, 64)),
+    MoeShape("8e_down", 8, 2, 14336, 4096, (1, 4, 16, 64)),
+))
+MOE_64E = Workload("moe_64e_top6_2048", (
+    MoeShape("64e_gate_up", 64, 6, 2048, 2816, (1, 4, 16, 64)),
+    MoeShape("64e_down", 64, 6, 1408, 2048, (1, 4, 16, 64)),
+))
+
+
 def draw(K: int, N: int, M: int, seed: int = 0, sigma: float = 1.0, group: int = GROUP):
     """Return (A fp16 [M,K], q uint8 [K,N], s fp16 [K/group,N]) from one seeded stream."""
     if K % group:
@@ -109,3 +132,40 @@ def sparsify_24(q: np.ndarray, seed: int = 0) -> np.ndarray:
         blk = out[k0:k0 + rows]
         blk[~keep] = 8
     return out
+
+
+def to_act(x: np.ndarray, act: str):
+    """Round float32 draws to the activation type: (16-bit patterns uint16, values float64).
+    fp16 by numpy's cast, bf16 by torch's (both round to nearest even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if act == "f16":
+        h = x.astype(np.float16)
+        return h.view(np.uint16), h.astype(np.float64)
+    if act == "bf16":
+        import torch
+        b = torch.from_numpy(x).to(torch.bfloat16)
+        bits = b.view(torch.int16).numpy().view(np.uint16).copy()
+        return bits, b.to(torch.float64).numpy()
+    raise ValueError(act)
+
+
+def draw_moe(E: int, topk: int, K: int, N: int, T: int, seed: int = 0, act: str = "f16",
+             zero_points: bool = False, group: int = GROUP) -> dict:
+    """Inputs of one MoE layer call, from numpy.random.default_rng([seed, 3]):
+      q [E, K, N] ~ U{0..15}; scales [E, K/group, N] ~ U[0.005, 0.02]; A [T, K] ~ N(0, 1);
+      router: logits [T, E] ~ N(0, 1) plus a per-expert N(0, 1/4) offset (some experts are
+      picked more often than others, as with a trained router); each token takes its topk
+      largest; row_scale [T*topk] ~ U[0.1, 1] (router weights); zero points ~ U{0..15}.
+    A and the scales are rounded to the activation type ("f16" or "bf16")."""
+    rng = np.random.default_rng([seed, 3])
+    q = rng.integers(0, 16, size=(E, K, N), dtype=np.uint8)
+    s32 = rng.uniform(0.005, 0.02, size=(E, K // group, N)).astype(np.float32)
+    A32 = rng.standard_normal((T, K), dtype=np.float32)
+    logits = rng.standard_normal((T, E)) + 0.5 * rng.standard_normal(E)
+    topk_ids = np.argsort(-logits, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    row_scale = rng.uniform(0.1, 1.0, size=T * topk).astype(np.float32)
+    z = rng.integers(0, 16, size=(E, K // group, N), dtype=np.uint8) if zero_points else None
+    A_bits, A = to_act(A32, act)
+    s_bits, s = to_act(s32, act)
+    return {"A": A, "A_bits": A_bits, "q": q, "s": s, "s_bits": s_bits, "zeros": z,
+            "topk_ids": topk_ids, "row_scale": row_scale, "act": act}
