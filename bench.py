@@ -252,6 +252,66 @@ def time_repack(w4, torch, dev, K, N, steps, stream):
     return rows
 
 
+def time_moe(w4, torch, dev, steps, stream):
+    """Mixture-of-experts layers (w4a16_moe_align + w4a16_moe_gemm) on the Mixtral-shaped and
+    64-expert shapes, fp16 and bf16 activations, every token count of the workload.  Bytes
+    per call: the weights and scales of the experts the call's tokens use, A, and C
+    (T * topk rows).  Enough weight copies rotate between calls that a copy's experts are
+    not still in the memory-side cache when they come round again."""
+    from workloads import MOE_64E, MOE_8E, draw_moe
+    rows = []
+    for wl in (MOE_8E, MOE_64E):
+        for sh in wl.shapes:
+            G = sh.K // GROUP
+            per_expert = sh.K * sh.N // 2 + G * sh.N * 2
+            for act in ("f16", "bf16"):
+                t = time.perf_counter()
+                d = draw_moe(sh.E, sh.topk, sh.K, sh.N, max(sh.Ts), seed=0, act=act)
+                scales = d["s_bits"] if act == "bf16" else d["s"].astype(np.float16)
+                pk, pr = w4.to_device(*w4.pack_experts(d["q"], scales), dev)
+                log(f"moe {sh.name} {act}: drawn and packed in {time.perf_counter() - t:.1f} s")
+                dt = torch.bfloat16 if act == "bf16" else torch.float16
+                A_all = torch.from_numpy(d["A_bits"].view(np.int16)).to(dev).view(dt)
+                used = {T: len(np.unique(d["topk_ids"][:T])) for T in sh.Ts}
+                touched = min(used.values()) * per_expert
+                ncp = int(min(max(2, -(-600e6 // touched)), max(2, 8e9 // (sh.E * per_expert))))
+                cps = [(pk, pr)] + [(pk.clone(), pr.clone()) for _ in range(ncp - 1)]
+                for T in sh.Ts:
+                    A = A_all[:T].contiguous()
+                    ids = torch.from_numpy(np.ascontiguousarray(d["topk_ids"][:T])).to(dev)
+                    rs = torch.from_numpy(d["row_scale"][:T * sh.topk]).to(dev)
+                    out = torch.empty((T * sh.topk, sh.N), dtype=dt, device=dev)
+                    ev = []
+                    for i in range(4 + steps):
+                        p_, r_ = cps[i % len(cps)]
+                        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                        e0.record(stream)
+                        sid, off = w4.moe_align(ids, sh.E, stream=stream)
+                        e1.record(stream)
+                        w4.moe_gemm(A, p_, r_, sid, off, sh.topk, sh.E, sh.N, row_scale=rs,
+                                    out=out, stream=stream)
+                        e2.record(stream)
+                        if i >= 4:
+                            ev.append((e0, e1, e2))
+                    torch.cuda.synchronize()
+                    ua = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
+                    ug = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+                    D = used[T] * per_expert + T * sh.K * 2 + T * sh.topk * sh.N * 2
+                    rows.append({"workload": wl.name, "shape": sh.name, "act": act, "T": T,
+                                 "E": sh.E, "topk": sh.topk, "K": sh.K, "N": sh.N,
+                                 "experts_used": used[T], "align_us": round(ua, 2),
+                                 "gemm_us": round(ug, 2), "us": round(ua + ug, 2),
+                                 "gemm_GBps": round(D / ug / 1e3, 1),
+                                 "gemm_hbm_frac": round(D / ug / 1e3 / HBM_PEAK_GBPS, 4),
+                                 "weight_copies_rotated": ncp})
+                    log(f"moe {sh.name:12s} {act:4s} T={T:3d} experts={used[T]:2d}  align "
+                        f"{ua:6.1f} us  gemm {ug:7.1f} us  {D / ug / 1e3:6.0f} GB/s "
+                        f"({D / ug / 1e3 / HBM_PEAK_GBPS:5.1%} HBM)")
+                del cps, pk, pr, d
+                torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +323,8 @@ def main():
                     help="weight copies rotated between calls so no call hits the MALL")
     ap.add_argument("--format-steps", type=int, default=20,
                     help="timed calls per M for each other packed format (0 skips them)")
+    ap.add_argument("--moe-steps", type=int, default=20,
+                    help="timed calls per token count of each MoE layer shape (0 skips them)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
@@ -381,6 +443,7 @@ def main():
     if args.format_steps > 0:
         sparse = time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, args.format_steps,
                              max(2, args.warmup // 4), args.copies, stream, copies)
+    moe = time_moe(w4, torch, dev, args.moe_steps, stream) if args.moe_steps > 0 else None
     formats = None
     if args.format_steps > 0:
         formats = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
@@ -399,6 +462,7 @@ def main():
         "formats": formats,
         "repack": repack,
         "sparse_24": sparse,
+        "moe": moe,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }

@@ -41,6 +41,10 @@ extern "C" {
 #define W4A16_GROUP 128           /* rows per scale group; group = K (one per column) also works */
 #define W4A16_N_ALIGN 64          /* N must be a multiple of this */
 
+/* Activation types of w4a16_moe_gemm (A, C and the scales share it). */
+#define W4A16_ACT_F16 0           /* IEEE binary16 */
+#define W4A16_ACT_BF16 1          /* bfloat16: the upper 16 bits of an IEEE binary32 */
+
 /* Source arrangements for w4a16_repack (8 codes per 32-bit word). */
 #define W4A16_PACKED_ALONG_K 0    /* word (r, n) of [K/8][N]: rows 8r..8r+7 of column n */
 #define W4A16_PACKED_ALONG_N 1    /* word (k, c) of [K][N/8]: columns 8c..8c+7 of row k */
@@ -264,6 +268,62 @@ int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16_t *scales,
 int w4a16_repack(const uint32_t *qweight, int src_layout, const uint8_t *order,
                  const uint16_t *scales, const uint32_t *qzeros, int K, int N, int group,
                  uint32_t *packed_out, uint16_t *params_out, void *stream);
+
+/*
+ * Regrouping of a mixture-of-experts layer's token assignments by expert (device,
+ * asynchronous on `stream`).  The pages' observation that an MoE layer regroups tokens by
+ * expert, so that each expert's product sees its own M (deep-dive page, section on where the
+ * format pays off, item 1; item 4 on grouped GEMM).
+ *
+ *   topk_ids       [in]  device int32 [T*topk]: entry a = t*topk + j is the j-th expert of
+ *                        token t.  Entries outside 0..E-1 are left out (their rows of C are
+ *                        then not written by w4a16_moe_gemm).
+ *   sorted_ids     [out] device int32 [T*topk]: the assignments a with a valid expert,
+ *                        grouped by expert (expert 0 first), increasing a within an expert;
+ *                        entries past expert_offsets[E] are not written.
+ *   expert_offsets [out] device int32 [E+1]: expert e's assignments are
+ *                        sorted_ids[expert_offsets[e] .. expert_offsets[e+1]).
+ * Deterministic (a stable counting sort in one workgroup).  E at most 1024.  Errors:
+ * W4A16_EINVAL (null pointer, T < 0, topk < 1, E < 1), W4A16_ESHAPE (E > 1024 or
+ * T*topk >= 2^31), W4A16_EUNSUPPORTED, W4A16_EHIP.
+ */
+int w4a16_moe_align(const int32_t *topk_ids, int T, int topk, int E, int32_t *sorted_ids,
+                    int32_t *expert_offsets, void *stream);
+
+/*
+ * Grouped W4A16 product of an MoE layer (device, asynchronous on `stream`), one launch for
+ * all experts:
+ *   C[a][n] = row_scale[a] * sum_k A[a / topk][k] * Bhat_e[k][n],  e = expert of assignment a,
+ * for every assignment a listed in sorted_ids, with Bhat_e = s_e (q_e - z_e) as in
+ * w4a16_gemm_ex (group 128; z = 8, or per group and column with zero_points = 1).  Each
+ * token row is read where it lies in A and each result written to its own row of C: no
+ * permuted copy is made.  Experts without rows cost nothing but an early exit.
+ *
+ *   A              [in]  device [T*K] row-major, fp16 or bf16 (act_dtype)
+ *   packed         [in]  device uint32 [E][K*N/8]: expert e's w4a16_pack / w4a16_pack_zp
+ *                        output (group 128) at word e*K*N/8
+ *   params         [in]  device 16-bit [E][(K/128)*N] (scales_out of w4a16_pack), or
+ *                        [E][2*(K/128)*N] with zero_points = 1 (params_out of w4a16_pack_zp);
+ *                        the scales are of type act_dtype (w4a16_pack moves their bits only)
+ *   sorted_ids, expert_offsets  [in] device, as w4a16_moe_align writes them
+ *   row_scale      [in]  device float [T*topk] indexed by assignment, or NULL for 1 (the
+ *                        router weight of a down projection)
+ *   C              [out] device [T*topk][N] of act_dtype; rows not listed are not written
+ *   zero_points    0 or 1;  act_dtype  W4A16_ACT_F16 or W4A16_ACT_BF16
+ * fp32 sums, one rounding of C to nearest-even.  fp16: the dense path's exact decode, so a
+ * row equals w4a16_gemm's result for that token and expert bit for bit when w4a16_gemm
+ * takes its whole-K kernel (M <= 16).  bf16: codes enter the matrix unit as 128 + q and
+ * (128 + z) * sum_k A is subtracted per row and group before the scale.
+ * Results do not depend on how the rows are grouped.  Limits: K a multiple of 128, N a
+ * multiple of 256, and K*N/2, T*K*2, T*topk*N*2 and (K/128)*N*4 below 2^31 bytes.  T == 0
+ * is a no-op.  Errors: W4A16_EINVAL (null pointer other than row_scale, negative size,
+ * topk or E below 1, zero_points or act_dtype out of range), W4A16_ESHAPE (shape or
+ * limit), W4A16_EUNSUPPORTED (not gfx950), W4A16_EHIP (launch failure).
+ */
+int w4a16_moe_gemm(const void *A, const uint32_t *packed, const uint16_t *params,
+                   const int32_t *sorted_ids, const int32_t *expert_offsets,
+                   const float *row_scale, void *C, int T, int topk, int E, int K, int N,
+                   int zero_points, int act_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -66,12 +66,18 @@ _lib.w4a16_unpack_24.argtypes = [_p, _p, _i, _i, _p, _p]
 _lib.w4a16_unpack_24.restype = _i
 _lib.w4a16_gemm_24.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _p]
 _lib.w4a16_gemm_24.restype = _i
+_lib.w4a16_moe_align.argtypes = [_p, _i, _i, _i, _p, _p, _p]
+_lib.w4a16_moe_align.restype = _i
+_lib.w4a16_moe_gemm.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]
+_lib.w4a16_moe_gemm.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
+ACT_F16, ACT_BF16 = 0, 1
 EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
             "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
-            "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24")
+            "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24",
+            "w4a16_moe_align", "w4a16_moe_gemm")
 
 
 class W4A16Error(RuntimeError):
@@ -97,23 +103,25 @@ def pack(codes: np.ndarray, scales: np.ndarray, group: int = GROUP, zeros=None):
     """Offline reorder.  codes uint8 [K, N] (0..15), scales fp16 [K/group, N] (group 128, or
     K for one scale per column), zeros optional uint8 [K/group, N] (0..15) ->
     (packed uint32 [K*N/8], params fp16: the scales [(K/group)*N], or scales and zero terms
-    [2*(K/group)*N] when zeros are given)."""
+    [2*(K/group)*N] when zeros are given).  Scales given as uint16 are taken as raw 16-bit
+    patterns (bf16 scales for w4a16_moe_gemm) and params come back as uint16."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
-    scales = np.ascontiguousarray(scales, dtype=np.float16)
+    raw = np.asarray(scales).dtype == np.uint16
+    scales = np.ascontiguousarray(scales, dtype=np.uint16 if raw else np.float16)
     K, N = codes.shape
     if not group or K % group or scales.shape != (K // group, N):
         raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape} "
                          f"with group {group}")
     packed = np.empty(K * N // 8, dtype=np.uint32)
     if zeros is None:
-        params = np.empty(scales.size, dtype=np.float16)
+        params = np.empty(scales.size, dtype=scales.dtype)
         _check("w4a16_pack", _lib.w4a16_pack(codes.ctypes.data, scales.ctypes.data, K, N, group,
                                              packed.ctypes.data, params.ctypes.data))
     else:
         zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
         if zeros.shape != scales.shape:
             raise ValueError(f"zeros shape {zeros.shape} != scales shape {scales.shape}")
-        params = np.empty(2 * scales.size, dtype=np.float16)
+        params = np.empty(2 * scales.size, dtype=scales.dtype)
         _check("w4a16_pack_zp", _lib.w4a16_pack_zp(codes.ctypes.data, scales.ctypes.data,
                                                    zeros.ctypes.data, K, N, group,
                                                    packed.ctypes.data, params.ctypes.data))
@@ -142,13 +150,26 @@ def unpack(packed: np.ndarray, params: np.ndarray, K: int, N: int, group: int = 
     return codes, scales, zeros
 
 
+def pack_experts(codes: np.ndarray, scales: np.ndarray, zeros=None):
+    """pack() for every expert of an MoE layer (group 128): codes uint8 [E, K, N], scales
+    [E, K/128, N] (fp16 values, or uint16 bit patterns for bf16 scales), zeros optional uint8
+    [E, K/128, N] -> (packed uint32 [E, K*N/8], params [E, P]) for moe_gemm."""
+    E = codes.shape[0]
+    outs = [pack(codes[e], scales[e], GROUP, None if zeros is None else zeros[e])
+            for e in range(E)]
+    return np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs])
+
+
 # ------------------------------------------------------------------------------ device side
 
 def to_device(packed: np.ndarray, scales_p: np.ndarray, device="cuda"):
     """Upload pack() output: (int32 tensor holding the uint32 words, fp16 tensor)."""
     import torch
+    sp = np.ascontiguousarray(scales_p)
+    if sp.dtype == np.uint16:
+        sp = sp.view(np.int16)
     return (torch.from_numpy(np.ascontiguousarray(packed).view(np.int32)).to(device),
-            torch.from_numpy(np.ascontiguousarray(scales_p)).to(device))
+            torch.from_numpy(sp).to(device))
 
 
 def workspace_bytes(M: int, K: int, N: int) -> int:
@@ -328,4 +349,64 @@ def gemm_24(A, packed, scales, N: int, out=None, ws=None, stream=None):
         _check("w4a16_gemm_24", _lib.w4a16_gemm_24(A.data_ptr(), packed.data_ptr(),
                                                    scales.data_ptr(), out.data_ptr(), M, K, N,
                                                    ws.data_ptr(), stream.cuda_stream))
+    return out
+
+
+def moe_align(topk_ids, E: int, stream=None):
+    """Regroup the assignments of topk_ids (int32 [T, topk] on the GPU) by expert
+    (w4a16_moe_align) -> (sorted_ids int32 [T*topk], expert_offsets int32 [E+1])."""
+    import torch
+    if (topk_ids.dtype != torch.int32 or not topk_ids.is_cuda or topk_ids.dim() != 2
+            or not topk_ids.is_contiguous()):
+        raise ValueError("topk_ids must be a contiguous int32 CUDA tensor [T, topk]")
+    T, topk = topk_ids.shape
+    sorted_ids = torch.empty(T * topk, dtype=torch.int32, device=topk_ids.device)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=topk_ids.device)
+    with torch.cuda.device(topk_ids.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(topk_ids.device)
+        _check("w4a16_moe_align", _lib.w4a16_moe_align(topk_ids.data_ptr(), T, topk, E,
+                                                       sorted_ids.data_ptr(), offsets.data_ptr(),
+                                                       stream.cuda_stream))
+    return sorted_ids, offsets
+
+
+def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, row_scale=None,
+             zero_points: bool = False, out=None, stream=None):
+    """Grouped MoE product (w4a16_moe_gemm): out[a] = row_scale[a] * A[a // topk] @ Bhat_e for
+    each assignment a listed in sorted_ids.  A: fp16 or bf16 [T, K]; packed int32 [E, K*N/8]
+    and params [E, P] from to_device(pack_experts(...)); out: optional [T*topk, N] of A's
+    dtype (rows not listed keep their contents)."""
+    import torch
+    if A.dtype not in (torch.float16, torch.bfloat16) or not A.is_cuda or A.dim() != 2 \
+            or not A.is_contiguous():
+        raise ValueError("A must be a contiguous fp16 or bf16 CUDA tensor [T, K]")
+    T, K = A.shape
+    dev = A.device
+    per = 2 if zero_points else 1
+    if (packed.dtype != torch.int32 or packed.numel() * 8 != E * K * N or not packed.is_contiguous()
+            or packed.device != dev):
+        raise ValueError("packed must be a contiguous int32 tensor of E*K*N/8 words on A's device")
+    if (K % GROUP or params.element_size() != 2 or params.numel() != E * per * (K // GROUP) * N
+            or not params.is_contiguous() or params.device != dev):
+        raise ValueError("params must be the 16-bit tensor pack_experts() returned, on A's device")
+    for t, n in ((sorted_ids, T * topk), (offsets, E + 1)):
+        if t.dtype != torch.int32 or t.numel() < n or not t.is_contiguous() or t.device != dev:
+            raise ValueError("sorted_ids / offsets must be moe_align()'s int32 tensors")
+    if row_scale is not None and (row_scale.dtype != torch.float32 or row_scale.numel() != T * topk
+                                  or not row_scale.is_contiguous() or row_scale.device != dev):
+        raise ValueError("row_scale must be a contiguous float32 tensor [T*topk]")
+    if out is None:
+        out = torch.empty((T * topk, N), dtype=A.dtype, device=dev)
+    elif (out.dtype != A.dtype or tuple(out.shape) != (T * topk, N) or not out.is_contiguous()
+          or out.device != dev):
+        raise ValueError("out must be a contiguous [T*topk, N] tensor of A's dtype on A's device")
+    act = ACT_BF16 if A.dtype == torch.bfloat16 else ACT_F16
+    with torch.cuda.device(dev):
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        _check("w4a16_moe_gemm", _lib.w4a16_moe_gemm(
+            A.data_ptr(), packed.data_ptr(), params.data_ptr(), sorted_ids.data_ptr(),
+            offsets.data_ptr(), None if row_scale is None else row_scale.data_ptr(),
+            out.data_ptr(), T, topk, E, K, N, int(bool(zero_points)), act, stream.cuda_stream))
     return out

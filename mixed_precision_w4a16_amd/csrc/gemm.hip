@@ -64,19 +64,10 @@
 
 #include "w4a16.h"
 #include "device.h"
+#include "kernel_common.h"
 
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h16 __attribute__((ext_vector_type(16)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u3 __attribute__((ext_vector_type(3)));
-
-constexpr int kThreads = 256;                 // 4 waves of 64
-constexpr int kWaves = 4;
-constexpr int kGroup = 128;                   // K rows per tile = one scale group
 constexpr size_t kCounterBytes = 4096;        // fixed counter area at the workspace start
 constexpr int kMaxWGs = static_cast<int>(kCounterBytes / sizeof(int));
 
@@ -112,80 +103,6 @@ struct Fmt {
 using FmtSym = Fmt<false, false>;
 using FmtSp = Fmt<false, false, true>;
 
-// (a & m) | o in one VALU op.  gfx9 VOP3 encodings take no literal and read at most one
-// SGPR, so left to itself the compiler splits this into v_and + v_or; the "v" constraints
-// keep both constants in (loop-invariant) VGPRs instead.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-    return r;
-}
-
-// 8 codes -> 8 fp16 values q - z, in MFMA B-operand order (see pack.cpp for the nibbles).
-// 9 VALU ops per 8 weights: 4 mask-and-OR, 1 shift, 2 packed adds, 2 packed FMAs.  `zsub`
-// is 1024 + z and `zadd` is 960 - (1024 + z) = -(64 + z), both exact in fp16: the low nibbles
-// give 1024 + q, the high ones 1024 + 16q, so (1024 + q) - zsub and (1024 + 16q) / 16 + zadd
-// are q - z exactly.  The symmetric format passes z = 8: 1032 and -72.
-__device__ __forceinline__ h8 dequant8(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic,
-                                       h2 zsub, h2 zadd)
-{
-    const uint32_t w8 = w >> 8;
-    const uint32_t x0 = and_or(w, mlo, magic);     // k0, k1: fp16 1024 + q
-    const uint32_t x1 = and_or(w, mhi, magic);     // k2, k3: fp16 1024 + 16 q
-    const uint32_t x2 = and_or(w8, mlo, magic);    // k4, k5
-    const uint32_t x3 = and_or(w8, mhi, magic);    // k6, k7
-    const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-    const h2 y0 = __builtin_bit_cast(h2, x0) - zsub;                                // q - z
-    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, zadd); // q - z
-    const h2 y2 = __builtin_bit_cast(h2, x2) - zsub;
-    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, zadd);
-    h8 r;
-    r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
-    r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
-    return r;
-}
-
-// 8 weights, decoded and scaled: fp16(s * (q - z)), one rounding.
-__device__ __forceinline__ h8 dequant8_scaled(uint32_t w, h2 s, uint32_t mlo, uint32_t mhi,
-                                              uint32_t magic, h2 zsub, h2 zadd)
-{
-    const uint32_t w8 = w >> 8;
-    const uint32_t x0 = and_or(w, mlo, magic);
-    const uint32_t x1 = and_or(w, mhi, magic);
-    const uint32_t x2 = and_or(w8, mlo, magic);
-    const uint32_t x3 = and_or(w8, mhi, magic);
-    const h2 mul = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-    const h2 y0 = (__builtin_bit_cast(h2, x0) - zsub) * s;
-    const h2 y1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x1), mul, zadd) * s;
-    const h2 y2 = (__builtin_bit_cast(h2, x2) - zsub) * s;
-    const h2 y3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, x3), mul, zadd) * s;
-    h8 r;
-    r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
-    r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
-    return r;
-}
-
-// Decode constants (zsub, zadd) of the symmetric format, z = 8.
-__device__ __forceinline__ h2 sym_zsub()
-{
-    return h2{static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-}
-__device__ __forceinline__ h2 sym_zadd()
-{
-    return h2{static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint16_t b)
-{
-    return static_cast<float>(__builtin_bit_cast(_Float16, b));
-}
-
-__device__ __forceinline__ uint16_t float_to_half_bits(float x)
-{
-    // v_cvt_f16_f32: one rounding, nearest-even in the default mode
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-}
 
 // First tile of stripe r, and the stripe that owns tile t (stripes are [r*T/W, (r+1)*T/W)).
 __device__ __forceinline__ long long stripe_begin(long long r, long long T, int W)
@@ -206,15 +123,6 @@ struct Tile {
     static constexpr int kSlotFloats = Mt * Nt;
 };
 
-// Raw buffer resources: base, size in bytes, gfx9 dword-access flags.  Loads past `bytes`
-// return zero, which masks the rows of A beyond M for free.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
-
-constexpr int kNonTemporal = 2;    // cache policy: streaming, evict first (weights, read once)
-constexpr int kDeviceScope = 16;   // cache policy sc1: write through / read past the XCD's L2
 
 // Where the next tile's loads come from.  Tiles run in (slice, M sub-problem, K) order;
 // inside a slice only the K step changes and every offset moves by a constant.
@@ -517,14 +425,6 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const WQ
     }
 }
 
-// Opaque copy of a uniform value: offsets derived from it are computed where they are used.
-// Without it the compiler hoists every loop-invariant store offset of the epilogue out of the
-// main loop and keeps them all live there.
-__device__ __forceinline__ uint32_t opaque(uint32_t x)
-{
-    asm volatile("" : "+s"(x));
-    return x;
-}
 
 // acc[mb][b][r] is C[row0 + 16mb + 4(lane/16) + r][col0 + 16b + lane%16].  C is written
 // through a buffer resource of exactly M * N * 2 bytes: stores to rows at or past M fall
@@ -1288,9 +1188,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // uniform selects per dword (j0 % 4 is the same for the whole workgroup).
 //
 // The tiles after a wave's run are still "loaded" (every iteration issues the same loads),
-// from an offset outside every buffer: no memory traffic, and the compiler never meets a join
+// from an offset outside every buffer (kOutside): no memory traffic, and the compiler never meets a join
 // where it would have to wait for everything.
-constexpr uint32_t kOutside = 0x80000000u;   // above every buffer the skinny kernel reads
 
 template <int NS>
 struct SkinnyGroups {

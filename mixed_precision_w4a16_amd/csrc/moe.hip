@@ -1,0 +1,574 @@
+// Grouped W4A16 product of a mixture-of-experts layer on gfx950: every token row meets the
+// weights of the experts its router picked, each expert with its own number of rows.
+//
+// The pages (deep-dive page, section on where the format stops paying off, items 1 and 4):
+// an MoE layer regroups the tokens by expert, so each expert's GEMM sees its own M, not the
+// batch's, and the grouped product is scheduled differently from a dense layer.  Here:
+//
+// * w4a16_moe_align: the regrouping.  The assignments a = t * topk + j (token t, its j-th
+//   expert) are sorted by expert with a stable counting sort, so expert e's rows are
+//   sorted_ids[offsets[e] .. offsets[e + 1]) in increasing a.  One workgroup; ranks inside
+//   a wave come from ballots, so the order is deterministic.
+// * w4a16_moe_gemm: one launch for all experts.  Workgroup (e, s) owns NS 16-column slabs
+//   of expert e over the whole K range (the whole-K scheme of the dense kernel for few
+//   rows: four waves split K, partial sums meet in LDS, no output shared between
+//   workgroups); workgroups of experts without rows return at once, so an expert's weights
+//   are read only if a token uses it.  Each lane gathers its own A row (row a / topk of A)
+//   and scatters its outputs to rows a of C, so no permuted copy of A or C is made.
+//   Experts with more rows than one block (16 MB) loop over blocks, re-reading the slab
+//   weights from cache.
+// * fp16 activations: the dense kernels' exact decode (q - z in fp16 by mask-and-OR into
+//   the exponent 0x6400 and one packed add or FMA per pair), fp32 sums over each 128-row
+//   group, one scale FMA per output and group.
+// * bf16 activations (and bf16 scales): gfx950 has bf16 matrix instructions but no packed
+//   bf16 add or multiply, so the codes are fed as they come: mask-and-OR into the bf16
+//   exponent 0x4300 gives 128 + q exactly (7 VALU ops per 8 weights), the MFMA sums
+//   A * (128 + q) over the group, and (128 + z) * sum_k A is subtracted per row and group
+//   before the scale: sum_k A (q - z) = sum_k A (128 + q) - (128 + z) sum_k A.  The row sums
+//   come from the same MFMA against a ones operand (4 extra instructions per 16 rows and
+//   group, shared by every slab).  The fp32 error this adds is near 2^-24 * 136 relative to
+//   the group's sum of |A|, far below bf16's 2^-9.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "w4a16.h"
+#include "device.h"
+#include "kernel_common.h"
+
+namespace {
+
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+// ----------------------------------------------------------------------------- regrouping
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kMaxExperts = 1024;
+
+__device__ __forceinline__ uint64_t ballot(bool p)
+{
+    return __builtin_amdgcn_ballot_w64(p);
+}
+
+// Lanes below this one.
+__device__ __forceinline__ uint64_t lanes_below(int lane)
+{
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(const int32_t *__restrict__ ids,
+                                                                  int R, int E,
+                                                                  int32_t *__restrict__ sorted,
+                                                                  int32_t *__restrict__ offsets)
+{
+    __shared__ int cnt[kAlignWaves][kMaxExperts];   // per round: wave w's rows of expert e
+    __shared__ int base[kMaxExperts];               // next free position of expert e
+    __shared__ int scan[kAlignThreads];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+    for (int e = tid; e < E; e += kAlignThreads) {
+        base[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kAlignWaves; ++w)
+            cnt[w][e] = 0;
+    }
+    __syncthreads();
+    // totals (order-free: LDS atomics)
+    for (int a = tid; a < R; a += kAlignThreads) {
+        const int e = ids[a];
+        if (e >= 0 && e < E)
+            atomicAdd(&base[e], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the totals, kAlignThreads experts per pass
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kAlignThreads) {
+        const int e = e0 + tid;
+        const int v = e < E ? base[e] : 0;
+        scan[tid] = v;
+        __syncthreads();
+        for (int d = 1; d < kAlignThreads; d <<= 1) {
+            const int add = tid >= d ? scan[tid - d] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        if (e < E) {
+            const int excl = carry + scan[tid] - v;
+            base[e] = excl;
+            offsets[e] = excl;
+        }
+        carry += scan[kAlignThreads - 1];
+        __syncthreads();
+    }
+    if (tid == 0)
+        offsets[E] = carry;
+    __syncthreads();
+
+    // Stable scatter, kAlignThreads assignments per round.  In each wave, lanes holding the
+    // same expert find each other with ballots (one pass per distinct expert in the wave);
+    // a lane's position is its expert's base, plus that expert's rows in lower waves of the
+    // round, plus its rank among the lower lanes of its own wave.
+    for (int a0 = 0; a0 < R; a0 += kAlignThreads) {
+        const int a = a0 + tid;
+        const int e = a < R ? ids[a] : -1;
+        const bool valid = e >= 0 && e < E;
+        int rank = 0;
+        uint64_t todo = ballot(valid);
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const int v = __builtin_amdgcn_readlane(e, leader);
+            const uint64_t same = ballot(valid && e == v);
+            if (valid && e == v)
+                rank = __builtin_popcountll(same & lanes_below(lane));
+            if (lane == leader)
+                cnt[wave][v] = __builtin_popcountll(same);
+            todo &= ~same;
+        }
+        __syncthreads();
+        if (valid) {
+            int pos = base[e] + rank;
+            for (int w = 0; w < wave; ++w)
+                pos += cnt[w][e];
+            sorted[pos] = a;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kAlignThreads) {
+            int t = 0;
+#pragma unroll
+            for (int w = 0; w < kAlignWaves; ++w) {
+                t += cnt[w][x];
+                cnt[w][x] = 0;
+            }
+            base[x] += t;
+        }
+        __syncthreads();
+    }
+}
+
+// --------------------------------------------------------------------------- grouped GEMM
+
+struct MoeParams {
+    const uint16_t *A;          // [T][K], fp16 or bf16
+    const u4 *packed;           // E experts, K * N / 8 words each (w4a16_pack layout)
+    const uint16_t *params;     // E experts, G * N halves each (2 G N with zero points)
+    const int32_t *sorted;      // assignments grouped by expert
+    const int32_t *offsets;     // [E + 1]
+    const float *row_scale;     // [T * topk] or null
+    uint16_t *C;                // [T * topk][N]
+    int T, topk, E, K, N, G;
+    int WE;                     // workgroups per expert
+};
+
+// Parameter groups a workgroup's NS slabs can touch, and dwords holding NS halves.
+template <int NS>
+struct MoeGroups {
+    static constexpr int n = (NS + 6) / 4;
+    static constexpr int nh = (NS + 1) / 2;
+};
+
+template <int MB, int NS, bool ZP, bool BF>
+struct MoeBuf {
+    u4 w[NS];                                 // weight quads, one per slab
+    u4 a[MB][4];                              // A fragments, 4 32-k steps per 16-row block
+    uint32_t p[MoeGroups<NS>::n][ZP ? 4 : 2]; // per-group parameters of the lane's column
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b)
+{
+    return __builtin_bit_cast(float, b << 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float x)
+{
+    // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+template <int MB, int NS, bool ZP, bool BF>
+__global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
+{
+    using MG = MoeGroups<NS>;
+    constexpr int NG = MG::n, NH = MG::nh;
+    constexpr uint32_t PB = ZP ? 16 : 8;                 // parameter bytes per column and group
+    __shared__ f4 red[kWaves * MB * NS * 64];
+
+    const int e = blockIdx.x / p.WE;
+    const int j0 = (blockIdx.x % p.WE) * NS;             // first slab of the workgroup
+    const int row0 = p.offsets[e];
+    const int rows = p.offsets[e + 1] - row0;
+    if (rows <= 0)
+        return;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15, quad = lane >> 4;
+    const int S = p.N >> 4;
+    const int U = S >> 2;
+    const int u0 = j0 >> 2, r = j0 & 3;
+    const int g0 = p.G * wave / kWaves;
+    const int g1 = p.G * (wave + 1) / kWaves;
+
+    const size_t ew = static_cast<size_t>(p.K) * p.N / 2;               // weight bytes / expert
+    const size_t ep = static_cast<size_t>(p.G) * p.N * (ZP ? 2 : 1);    // params / expert
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A, static_cast<uint32_t>(p.T) * static_cast<uint32_t>(p.K) * 2u);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(
+        reinterpret_cast<const char *>(p.packed) + static_cast<size_t>(e) * ew,
+        static_cast<uint32_t>(ew));
+    const __amdgpu_buffer_rsrc_t rS =
+        make_rsrc(p.params + static_cast<size_t>(e) * ep, static_cast<uint32_t>(ep * 2));
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(
+        p.C, static_cast<uint32_t>(p.T) * static_cast<uint32_t>(p.topk) *
+                 static_cast<uint32_t>(p.N) * 2u);
+
+    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u;
+    const uint32_t magic = BF ? 0x43004300u : 0x64006400u;
+    const uint32_t v_par = static_cast<uint32_t>(c) * PB;
+    auto slab = [&](int i) __attribute__((always_inline)) {
+        const int j = j0 + i;
+        return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
+    };
+    const bool sel_dw = (r & 2) != 0, sel_half = (r & 1) != 0;     // uniform
+    // halves r .. r + NS - 1 of the concatenated groups (part 0: scales, 1: zero terms)
+    auto pick = [&](const uint32_t (&pg)[NG][ZP ? 4 : 2], int part, uint32_t (&out)[NH])
+        __attribute__((always_inline)) {
+        auto D = [&](int m) __attribute__((always_inline)) {
+            m = m < 2 * NG ? m : 2 * NG - 1;
+            return pg[m >> 1][2 * part + (m & 1)];
+        };
+        uint32_t x[NH + 1];
+#pragma unroll
+        for (int m = 0; m <= NH; ++m)
+            x[m] = sel_dw ? D(m + 1) : D(m);
+#pragma unroll
+        for (int m = 0; m < NH; ++m)
+            out[m] = sel_half ? __builtin_amdgcn_alignbit(x[m + 1], x[m], 16) : x[m];
+    };
+
+    for (int rb = 0; rb < rows; rb += 16 * MB) {
+        // the lane's A row in each 16-row block: token a / topk of assignment a
+        uint32_t v_a[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int i = rb + 16 * mb + c;
+            v_a[mb] = kOutside;
+            if (i < rows) {
+                const int a = p.sorted[row0 + i];
+                v_a[mb] = (static_cast<uint32_t>(a / p.topk) * p.K + 8 * quad) * 2;
+            }
+        }
+
+        auto load = [&](MoeBuf<MB, NS, ZP, BF> &b, int g) __attribute__((always_inline)) {
+            const bool live = g < g1;
+            const uint32_t vw = live ? static_cast<uint32_t>(lane) * 16 : kOutside;
+            const uint32_t vp = live ? v_par : kOutside;
+            const int gg = live ? g : g1 - 1;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    b.a[mb][t] = __builtin_bit_cast(
+                        u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                rA, live ? v_a[mb] : kOutside,
+                                static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                b.w[i] = __builtin_bit_cast(
+                    u4, __builtin_amdgcn_raw_buffer_load_b128(
+                            rW, vw, (static_cast<uint32_t>(slab(i)) * p.G + gg) * 1024u,
+                            kNonTemporal));
+#pragma unroll
+            for (int k = 0; k < NG; ++k) {
+                const int u = u0 + k < U ? u0 + k : U - 1;
+                const uint32_t so = (static_cast<uint32_t>(u) * p.G + gg) * (16u * PB);
+                if constexpr (ZP) {
+                    const u4 v = __builtin_bit_cast(
+                        u4, __builtin_amdgcn_raw_buffer_load_b128(rS, vp, so, 0));
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        b.p[k][d] = v[d];
+                } else {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, vp, so, 0);
+                    b.p[k][0] = v[0];
+                    b.p[k][1] = v[1];
+                }
+            }
+        };
+
+        f4 acc[MB][NS];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
+
+        auto compute = [&](const MoeBuf<MB, NS, ZP, BF> &b) __attribute__((always_inline)) {
+            uint32_t sh[NH], zh[NH];
+            pick(b.p, 0, sh);
+            if constexpr (ZP)
+                pick(b.p, 1, zh);
+            float sf[NS];
+            uint32_t zb[NS];
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const uint32_t sb = (sh[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                sf[i] = BF ? bf16_bits_to_float(sb) : half_bits_to_float(static_cast<uint16_t>(sb));
+                asm volatile("" : "+v"(sf[i]));
+                zb[i] = ZP ? (zh[i >> 1] >> (16 * (i & 1))) & 0xffffu : 0x6408u;
+            }
+            if constexpr (BF) {
+                // A * (128 + q) per group, minus (128 + z) times the group's row sums of A
+                const u4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+                f4 rs[MB];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    rs[mb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        rs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(b8, b.a[mb][t]), __builtin_bit_cast(b8, ones),
+                            rs[mb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    f4 part[MB];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t w = b.w[i][t];
+                        const u4 x = {and_or(w, mlo, magic), and_or(w >> 4, mlo, magic),
+                                      and_or(w >> 8, mlo, magic), and_or(w >> 12, mlo, magic)};
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const f4 cin = t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : part[mb];
+                            part[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(b8, b.a[mb][t]), __builtin_bit_cast(b8, x),
+                                cin, 0, 0, 0);
+                        }
+                    }
+                    const float nz = -static_cast<float>(128 + (zb[i] & 15u));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[mb][i][q] = __builtin_fmaf(
+                                sf[i], __builtin_fmaf(nz, rs[mb][q], part[mb][q]), acc[mb][i][q]);
+                        asm volatile("" : "+v"(acc[mb][i]));
+                    }
+                }
+            } else {
+                // exact q - z per group in fp16, one scale FMA per output
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    const _Float16 zt = __builtin_bit_cast(_Float16, static_cast<uint16_t>(zb[i]));
+                    const h2 zsub = {zt, zt};
+                    const h2 k960 = {static_cast<_Float16>(960.0f), static_cast<_Float16>(960.0f)};
+                    const h2 zadd = k960 - zsub;
+                    f4 part[MB];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const h8 x = dequant8(b.w[i][t], mlo, mhi, magic, zsub, zadd);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const f4 cin = t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : part[mb];
+                            part[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(h8, b.a[mb][t]), x, cin, 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[mb][i][q] = __builtin_fmaf(sf[i], part[mb][q], acc[mb][i][q]);
+                        asm volatile("" : "+v"(acc[mb][i]));
+                    }
+                }
+            }
+        };
+
+        if (g0 < g1) {
+            // two buffers, one loop exit, memory fences: as the dense whole-K kernel
+            MoeBuf<MB, NS, ZP, BF> b[2];
+            load(b[0], g0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            load(b[1], g0 + 1);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const int rounds = (g1 - g0) >> 1;
+            int g = g0;
+            for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    compute(b[d]);
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                    load(b[d], g + d + 2);
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                g += 2;
+            }
+            if (g < g1)
+                compute(b[0]);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+
+        // Partial sums meet in LDS; wave w finishes slabs w, w + 4, ...  Result lane l holds
+        // rows 16 mb + 4(l/16) + 0..3 of the block, column 16j + l % 16.
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                red[((wave * MB + mb) * NS + i) * 64 + lane] = acc[mb][i];
+        __syncthreads();
+        int orow[MB][4];                    // output row (assignment) of each result, or -1
+        float osc[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = rb + 16 * mb + 4 * quad + q;
+                orow[mb][q] = i < rows ? p.sorted[row0 + i] : -1;
+                osc[mb][q] = (p.row_scale && orow[mb][q] >= 0) ? p.row_scale[orow[mb][q]] : 1.0f;
+            }
+#pragma unroll
+        for (int i0 = 0; i0 < NS; i0 += kWaves) {
+            const int i = i0 + wave;
+            if (i < NS && j0 + i < S) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    f4 v = red[((0 * MB + mb) * NS + i) * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < kWaves; ++w)
+                        v += red[((w * MB + mb) * NS + i) * 64 + lane];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float y = v[q] * osc[mb][q];
+                        const uint16_t h = BF ? float_to_bf16_bits(y) : float_to_half_bits(y);
+                        const uint32_t off =
+                            orow[mb][q] >= 0
+                                ? (static_cast<uint32_t>(orow[mb][q]) * p.N + 16 * (j0 + i) + c) * 2
+                                : kOutside;
+                        __builtin_amdgcn_raw_buffer_store_b16(h, rC, off, 0, 0);
+                    }
+                }
+            }
+        }
+        __syncthreads();                    // red is reused by the next row block
+    }
+}
+
+template <int MB, int NS, bool ZP, bool BF>
+hipError_t launch_moe(const MoeParams &p, int blocks, hipStream_t s)
+{
+    hipLaunchKernelGGL((w4a16_moe_kernel<MB, NS, ZP, BF>), dim3(blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <bool ZP, bool BF>
+hipError_t dispatch_moe(int mb, int ns, const MoeParams &p, int blocks, hipStream_t s)
+{
+    switch (mb * 16 + ns) {
+    case 17: return launch_moe<1, 1, ZP, BF>(p, blocks, s);
+    case 18: return launch_moe<1, 2, ZP, BF>(p, blocks, s);
+    case 20: return launch_moe<1, 4, ZP, BF>(p, blocks, s);
+    case 24: return launch_moe<1, 8, ZP, BF>(p, blocks, s);
+    case 33: return launch_moe<2, 1, ZP, BF>(p, blocks, s);
+    case 34: return launch_moe<2, 2, ZP, BF>(p, blocks, s);
+    case 36: return launch_moe<2, 4, ZP, BF>(p, blocks, s);
+    case 65: return launch_moe<4, 1, ZP, BF>(p, blocks, s);
+    case 66: return launch_moe<4, 2, ZP, BF>(p, blocks, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+extern "C" int w4a16_moe_align(const int32_t *topk_ids, int T, int topk, int E,
+                               int32_t *sorted_ids, int32_t *expert_offsets, void *stream)
+{
+    if (!topk_ids || !sorted_ids || !expert_offsets || T < 0 || topk < 1 || E < 1)
+        return W4A16_EINVAL;
+    if (E > kMaxExperts || static_cast<long long>(T) * topk > INT_MAX)
+        return W4A16_ESHAPE;
+    w4a16_detail::DeviceInfo d;
+    const int rc = w4a16_detail::current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), 0,
+                       static_cast<hipStream_t>(stream), topk_ids, T * topk, E, sorted_ids,
+                       expert_offsets);
+    return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}
+
+extern "C" int w4a16_moe_gemm(const void *A, const uint32_t *packed, const uint16_t *params,
+                              const int32_t *sorted_ids, const int32_t *expert_offsets,
+                              const float *row_scale, void *C, int T, int topk, int E, int K,
+                              int N, int zero_points, int act_dtype, void *stream)
+{
+    if (!A || !packed || !params || !sorted_ids || !expert_offsets || !C || T < 0 || topk < 1 ||
+        E < 1 || K < 0 || N < 0 || (zero_points != 0 && zero_points != 1) ||
+        (act_dtype != W4A16_ACT_F16 && act_dtype != W4A16_ACT_BF16))
+        return W4A16_EINVAL;
+    if (K == 0 || K % kGroup || N == 0 || N % 256)
+        return W4A16_ESHAPE;
+    // 32-bit buffer offsets, and the dead loads' offset above every buffer
+    const uint64_t R = static_cast<uint64_t>(T) * static_cast<uint64_t>(topk);
+    if (static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
+        static_cast<uint64_t>(T) * static_cast<uint64_t>(K) * 2 >= kOutside ||
+        R * static_cast<uint64_t>(N) * 2 >= kOutside ||
+        static_cast<uint64_t>(K / kGroup) * static_cast<uint64_t>(N) * 4 >= kOutside)
+        return W4A16_ESHAPE;
+    w4a16_detail::DeviceInfo d;
+    const int rc = w4a16_detail::current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    if (T == 0)
+        return W4A16_OK;
+
+    // Rows per block from the mean rows per expert; slabs per workgroup so that the experts
+    // in use (at most min(E, T * topk)) give about two workgroups per CU.
+    const long long mean_rows = (static_cast<long long>(R) + E - 1) / E;
+    const int mb = mean_rows <= 16 ? 1 : (mean_rows <= 32 ? 2 : 4);
+    const int nsmax = mb == 1 ? 8 : (mb == 2 ? 4 : 2);
+    const long long S = N / 16;
+    const long long active = std::min<long long>(E, static_cast<long long>(R));
+    long long want = (active * S + 2LL * d.cus - 1) / (2LL * d.cus);
+    int ns = 1;
+    while (ns < nsmax && ns < want)
+        ns *= 2;
+    MoeParams p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.packed = reinterpret_cast<const u4 *>(packed);
+    p.params = params;
+    p.sorted = sorted_ids;
+    p.offsets = expert_offsets;
+    p.row_scale = row_scale;
+    p.C = static_cast<uint16_t *>(C);
+    p.T = T;
+    p.topk = topk;
+    p.E = E;
+    p.K = K;
+    p.N = N;
+    p.G = K / kGroup;
+    p.WE = static_cast<int>((S + ns - 1) / ns);
+    const long long blocks = static_cast<long long>(p.WE) * E;
+    if (blocks > INT_MAX)
+        return W4A16_ESHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = act_dtype == W4A16_ACT_BF16;
+    hipError_t e;
+    if (zero_points)
+        e = bf ? dispatch_moe<true, true>(mb, ns, p, static_cast<int>(blocks), s)
+               : dispatch_moe<true, false>(mb, ns, p, static_cast<int>(blocks), s);
+    else
+        e = bf ? dispatch_moe<false, true>(mb, ns, p, static_cast<int>(blocks), s)
+               : dispatch_moe<false, false>(mb, ns, p, static_cast<int>(blocks), s);
+    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}

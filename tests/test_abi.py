@@ -316,3 +316,38 @@ def test_sparsify_24_keeps_two_of_every_four():
         for n in range(96):
             pairs.add(tuple(np.flatnonzero(z[a:a + 4, n] != 8)))
     assert {(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)} <= pairs
+
+
+def test_moe_entry_points_reject_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(256)
+    # w4a16_moe_align(topk_ids, T, topk, E, sorted_ids, expert_offsets, stream)
+    assert lib.w4a16_moe_align(None, 4, 2, 8, d, d, None) == w4.EINVAL
+    assert lib.w4a16_moe_align(d, -1, 2, 8, d, d, None) == w4.EINVAL
+    assert lib.w4a16_moe_align(d, 4, 0, 8, d, d, None) == w4.EINVAL
+    assert lib.w4a16_moe_align(d, 4, 2, 0, d, d, None) == w4.EINVAL
+    assert lib.w4a16_moe_align(d, 4, 2, 1025, d, d, None) == w4.ESHAPE
+    assert lib.w4a16_moe_align(d, 1 << 30, 4, 8, d, d, None) == w4.ESHAPE
+    # w4a16_moe_gemm(A, packed, params, sorted, offsets, row_scale, C, T, topk, E, K, N,
+    #                zero_points, act_dtype, stream)
+    ok = [d, d, d, d, d, None, d, 4, 2, 8, 1024, 1024, 0, w4.ACT_F16, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["A", "packed", "params", "sorted", "offsets", "row_scale", "C", "T", "topk",
+                 "E", "K", "N", "zp", "act", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.w4a16_moe_gemm(*a)
+    assert call(A=None) == w4.EINVAL
+    assert call(sorted=None) == w4.EINVAL
+    assert call(C=None) == w4.EINVAL
+    assert call(T=-1) == w4.EINVAL
+    assert call(topk=0) == w4.EINVAL
+    assert call(E=0) == w4.EINVAL
+    assert call(zp=2) == w4.EINVAL
+    assert call(act=2) == w4.EINVAL
+    assert call(K=1000) == w4.ESHAPE
+    assert call(N=320) == w4.ESHAPE                    # N a multiple of 256
+    assert call(K=65536, N=65536) == w4.ESHAPE         # 2 GiB of codes per expert
+    assert call(T=600000, K=4096) == w4.ESHAPE         # A past 2^31 bytes
