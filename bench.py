@@ -253,11 +253,12 @@ def time_repack(w4, torch, dev, K, N, steps, stream):
 
 
 def time_moe(w4, torch, dev, steps, stream):
-    """Mixture-of-experts layers (w4a16_moe_align + w4a16_moe_gemm) on the Mixtral-shaped and
-    64-expert shapes, fp16 and bf16 activations, every token count of the workload.  Bytes
-    per call: the weights and scales of the experts the call's tokens use, A, and C
-    (T * topk rows).  Enough weight copies rotate between calls that a copy's experts are
-    not still in the memory-side cache when they come round again."""
+    """Mixture-of-experts layers on the Mixtral-shaped and 64-expert shapes, fp16 and bf16
+    activations, every token count of the workload: w4a16_moe_align + w4a16_moe_gemm (two
+    launches) and w4a16_moe_gemm_topk (routing inside the product, one launch), alternated
+    call by call.  Bytes per call: the weights and scales of the experts the call's tokens
+    use, A, and C (T * topk rows).  Enough weight copies rotate between calls that a copy's
+    experts are not still in the memory-side cache when they come round again."""
     from workloads import MOE_64E, MOE_8E, draw_moe
     rows = []
     for wl in (MOE_8E, MOE_64E):
@@ -281,21 +282,27 @@ def time_moe(w4, torch, dev, steps, stream):
                     ids = torch.from_numpy(np.ascontiguousarray(d["topk_ids"][:T])).to(dev)
                     rs = torch.from_numpy(d["row_scale"][:T * sh.topk]).to(dev)
                     out = torch.empty((T * sh.topk, sh.N), dtype=dt, device=dev)
-                    ev = []
+                    ev, evt = [], []
                     for i in range(4 + steps):
                         p_, r_ = cps[i % len(cps)]
-                        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                        e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
                         e0.record(stream)
                         sid, off = w4.moe_align(ids, sh.E, stream=stream)
                         e1.record(stream)
                         w4.moe_gemm(A, p_, r_, sid, off, sh.topk, sh.E, sh.N, row_scale=rs,
                                     out=out, stream=stream)
                         e2.record(stream)
+                        p_, r_ = cps[(i + len(cps) // 2) % len(cps)]
+                        w4.moe_gemm_topk(A, p_, r_, ids, sh.E, sh.N, row_scale=rs, out=out,
+                                         stream=stream)
+                        e3.record(stream)
                         if i >= 4:
                             ev.append((e0, e1, e2))
+                            evt.append((e2, e3))
                     torch.cuda.synchronize()
                     ua = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
                     ug = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+                    ut = float(np.mean([a.elapsed_time(b) for a, b in evt])) * 1e3
                     D = used[T] * per_expert + T * sh.K * 2 + T * sh.topk * sh.N * 2
                     rows.append({"workload": wl.name, "shape": sh.name, "act": act, "T": T,
                                  "E": sh.E, "topk": sh.topk, "K": sh.K, "N": sh.N,
@@ -303,10 +310,13 @@ def time_moe(w4, torch, dev, steps, stream):
                                  "gemm_us": round(ug, 2), "us": round(ua + ug, 2),
                                  "gemm_GBps": round(D / ug / 1e3, 1),
                                  "gemm_hbm_frac": round(D / ug / 1e3 / HBM_PEAK_GBPS, 4),
+                                 "routed_us": round(ut, 2),
+                                 "routed_GBps": round(D / ut / 1e3, 1),
                                  "weight_copies_rotated": ncp})
                     log(f"moe {sh.name:12s} {act:4s} T={T:3d} experts={used[T]:2d}  align "
                         f"{ua:6.1f} us  gemm {ug:7.1f} us  {D / ug / 1e3:6.0f} GB/s "
-                        f"({D / ug / 1e3 / HBM_PEAK_GBPS:5.1%} HBM)")
+                        f"({D / ug / 1e3 / HBM_PEAK_GBPS:5.1%} HBM)  routed {ut:7.1f} us "
+                        f"{D / ut / 1e3:6.0f} GB/s")
                 del cps, pk, pr, d
                 torch.cuda.empty_cache()
     return rows

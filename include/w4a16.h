@@ -325,6 +325,20 @@ int w4a16_moe_gemm(const void *A, const uint32_t *packed, const uint16_t *params
                    const float *row_scale, void *C, int T, int topk, int E, int K, int N,
                    int zero_points, int act_dtype, void *stream);
 
+/*
+ * w4a16_moe_gemm with the regrouping done inside the product (device, asynchronous on
+ * `stream`): for decode-sized batches, where a separate w4a16_moe_align launch would cost as
+ * much as the product of a few experts.  Every workgroup lists its expert's assignments from
+ * topk_ids itself (same order as w4a16_moe_align, so the results equal w4a16_moe_gemm's bit
+ * for bit).  topk_ids as for w4a16_moe_align ([T*topk] int32, entries outside 0..E-1 left
+ * out, their rows of C not written); everything else as w4a16_moe_gemm.  T*topk at most
+ * 2048, else W4A16_ESHAPE (use w4a16_moe_align + w4a16_moe_gemm).
+ */
+int w4a16_moe_gemm_topk(const void *A, const uint32_t *packed, const uint16_t *params,
+                        const int32_t *topk_ids, const float *row_scale, void *C, int T,
+                        int topk, int E, int K, int N, int zero_points, int act_dtype,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

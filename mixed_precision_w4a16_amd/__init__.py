@@ -70,6 +70,8 @@ _lib.w4a16_moe_align.argtypes = [_p, _i, _i, _i, _p, _p, _p]
 _lib.w4a16_moe_align.restype = _i
 _lib.w4a16_moe_gemm.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]
 _lib.w4a16_moe_gemm.restype = _i
+_lib.w4a16_moe_gemm_topk.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]
+_lib.w4a16_moe_gemm_topk.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
@@ -77,7 +79,7 @@ ACT_F16, ACT_BF16 = 0, 1
 EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
             "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
             "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24",
-            "w4a16_moe_align", "w4a16_moe_gemm")
+            "w4a16_moe_align", "w4a16_moe_gemm", "w4a16_moe_gemm_topk")
 
 
 class W4A16Error(RuntimeError):
@@ -371,12 +373,10 @@ def moe_align(topk_ids, E: int, stream=None):
     return sorted_ids, offsets
 
 
-def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, row_scale=None,
-             zero_points: bool = False, out=None, stream=None):
-    """Grouped MoE product (w4a16_moe_gemm): out[a] = row_scale[a] * A[a // topk] @ Bhat_e for
-    each assignment a listed in sorted_ids.  A: fp16 or bf16 [T, K]; packed int32 [E, K*N/8]
-    and params [E, P] from to_device(pack_experts(...)); out: optional [T*topk, N] of A's
-    dtype (rows not listed keep their contents)."""
+MOE_ROUTE_MAX = 2048
+
+
+def _moe_args(A, packed, params, topk, E, N, row_scale, zero_points, out):
     import torch
     if A.dtype not in (torch.float16, torch.bfloat16) or not A.is_cuda or A.dim() != 2 \
             or not A.is_contiguous():
@@ -390,9 +390,6 @@ def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, 
     if (K % GROUP or params.element_size() != 2 or params.numel() != E * per * (K // GROUP) * N
             or not params.is_contiguous() or params.device != dev):
         raise ValueError("params must be the 16-bit tensor pack_experts() returned, on A's device")
-    for t, n in ((sorted_ids, T * topk), (offsets, E + 1)):
-        if t.dtype != torch.int32 or t.numel() < n or not t.is_contiguous() or t.device != dev:
-            raise ValueError("sorted_ids / offsets must be moe_align()'s int32 tensors")
     if row_scale is not None and (row_scale.dtype != torch.float32 or row_scale.numel() != T * topk
                                   or not row_scale.is_contiguous() or row_scale.device != dev):
         raise ValueError("row_scale must be a contiguous float32 tensor [T*topk]")
@@ -402,6 +399,42 @@ def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, 
           or out.device != dev):
         raise ValueError("out must be a contiguous [T*topk, N] tensor of A's dtype on A's device")
     act = ACT_BF16 if A.dtype == torch.bfloat16 else ACT_F16
+    return T, K, out, act
+
+
+def moe_gemm_topk(A, packed, params, topk_ids, E: int, N: int, row_scale=None,
+                  zero_points: bool = False, out=None, stream=None):
+    """moe_gemm with the regrouping inside the product (w4a16_moe_gemm_topk): topk_ids int32
+    [T, topk] on the GPU, T*topk <= MOE_ROUTE_MAX.  Same result as moe_align + moe_gemm."""
+    import torch
+    if (topk_ids.dtype != torch.int32 or not topk_ids.is_cuda or topk_ids.dim() != 2
+            or not topk_ids.is_contiguous() or topk_ids.device != A.device
+            or topk_ids.shape[0] != A.shape[0]):
+        raise ValueError("topk_ids must be a contiguous int32 [T, topk] tensor on A's device")
+    topk = topk_ids.shape[1]
+    T, K, out, act = _moe_args(A, packed, params, topk, E, N, row_scale, zero_points, out)
+    with torch.cuda.device(A.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        _check("w4a16_moe_gemm_topk", _lib.w4a16_moe_gemm_topk(
+            A.data_ptr(), packed.data_ptr(), params.data_ptr(), topk_ids.data_ptr(),
+            None if row_scale is None else row_scale.data_ptr(), out.data_ptr(), T, topk, E, K,
+            N, int(bool(zero_points)), act, stream.cuda_stream))
+    return out
+
+
+def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, row_scale=None,
+             zero_points: bool = False, out=None, stream=None):
+    """Grouped MoE product (w4a16_moe_gemm): out[a] = row_scale[a] * A[a // topk] @ Bhat_e for
+    each assignment a listed in sorted_ids.  A: fp16 or bf16 [T, K]; packed int32 [E, K*N/8]
+    and params [E, P] from to_device(pack_experts(...)); out: optional [T*topk, N] of A's
+    dtype (rows not listed keep their contents)."""
+    import torch
+    T, K, out, act = _moe_args(A, packed, params, topk, E, N, row_scale, zero_points, out)
+    dev = A.device
+    for t, n in ((sorted_ids, T * topk), (offsets, E + 1)):
+        if t.dtype != torch.int32 or t.numel() < n or not t.is_contiguous() or t.device != dev:
+            raise ValueError("sorted_ids / offsets must be moe_align()'s int32 tensors")
     with torch.cuda.device(dev):
         if stream is None:
             stream = torch.cuda.current_stream(dev)

@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(const int32_t 
 {
     __shared__ int cnt[kAlignWaves][kMaxExperts];   // per round: wave w's rows of expert e
     __shared__ int base[kMaxExperts];               // next free position of expert e
-    __shared__ int scan[kAlignThreads];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
     for (int e = tid; e < E; e += kAlignThreads) {
@@ -84,29 +83,32 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(const int32_t 
             atomicAdd(&base[e], 1);
     }
     __syncthreads();
-    // exclusive scan of the totals, kAlignThreads experts per pass
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kAlignThreads) {
-        const int e = e0 + tid;
-        const int v = e < E ? base[e] : 0;
-        scan[tid] = v;
-        __syncthreads();
-        for (int d = 1; d < kAlignThreads; d <<= 1) {
-            const int add = tid >= d ? scan[tid - d] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
+    // Exclusive scan of the totals, by one wave: lane j adds up experts [jc, (j+1)c) with
+    // c = ceil(E / 64), the 64 lane sums are scanned across the wave, and each lane hands out
+    // its experts' bases.
+    if (wave == 0) {
+        const int c = (E + 63) / 64;
+        const int e0 = lane * c, e1 = e0 + c < E ? e0 + c : E;
+        int sum = 0;
+        for (int x = e0; x < e1; ++x)
+            sum += base[x];
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d, 64);
+            if (lane >= d)
+                incl += y;
         }
-        if (e < E) {
-            const int excl = carry + scan[tid] - v;
-            base[e] = excl;
-            offsets[e] = excl;
+        int run = incl - sum;
+        for (int x = e0; x < e1; ++x) {
+            const int v = base[x];
+            base[x] = run;
+            offsets[x] = run;
+            run += v;
         }
-        carry += scan[kAlignThreads - 1];
-        __syncthreads();
+        if (lane == 63)
+            offsets[E] = incl;
     }
-    if (tid == 0)
-        offsets[E] = carry;
     __syncthreads();
 
     // Stable scatter, kAlignThreads assignments per round.  In each wave, lanes holding the
@@ -156,8 +158,9 @@ struct MoeParams {
     const uint16_t *A;          // [T][K], fp16 or bf16
     const u4 *packed;           // E experts, K * N / 8 words each (w4a16_pack layout)
     const uint16_t *params;     // E experts, G * N halves each (2 G N with zero points)
-    const int32_t *sorted;      // assignments grouped by expert
-    const int32_t *offsets;     // [E + 1]
+    const int32_t *sorted;      // assignments grouped by expert (presorted entry)
+    const int32_t *offsets;     // [E + 1] (presorted entry)
+    const int32_t *topk_ids;    // [T * topk] (routing entry)
     const float *row_scale;     // [T * topk] or null
     uint16_t *C;                // [T * topk][N]
     int T, topk, E, K, N, G;
@@ -189,24 +192,83 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float x)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-template <int MB, int NS, bool ZP, bool BF>
+// Routing inside the product (w4a16_moe_gemm_topk): the workgroup lists expert e's
+// assignments itself.  Wave w scans a contiguous quarter of topk_ids, 64 ids per ballot, all
+// its loads issued before the first ballot; the waves' counts meet in LDS, and each wave
+// writes its matches at its offset.  The list comes out in increasing order, as
+// w4a16_moe_align's, so both entries put the same rows in the same blocks.
+constexpr int kRouteMax = 2048;                          // assignments the routing entry takes
+
+__device__ __forceinline__ int route_rows(const int32_t *__restrict__ ids, int R, int e, int wave,
+                                          int lane, int *rlist, int *wcnt)
+{
+    constexpr int kChunks = kRouteMax / (64 * kWaves);
+    const int per = (R + 64 * kWaves - 1) / (64 * kWaves) * 64;    // ids per wave
+    const int a0 = wave * per;
+    int ev[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int a = a0 + 64 * i + lane;
+        ev[i] = (64 * i < per && a < R) ? ids[a] : -1;
+    }
+    uint64_t m[kChunks];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        m[i] = ballot(ev[i] == e);
+        cnt += __builtin_popcountll(m[i]);
+    }
+    if (lane == 0)
+        wcnt[wave] = cnt;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = wcnt[w];
+        base += w < wave ? c : 0;
+        total += c;
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        if (ev[i] == e)
+            rlist[base + __builtin_popcountll(m[i] & lanes_below(lane))] = a0 + 64 * i + lane;
+        base += __builtin_popcountll(m[i]);
+    }
+    __syncthreads();
+    return total;
+}
+
+template <int MB, int NS, bool ZP, bool BF, bool RT>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
 {
     using MG = MoeGroups<NS>;
     constexpr int NG = MG::n, NH = MG::nh;
     constexpr uint32_t PB = ZP ? 16 : 8;                 // parameter bytes per column and group
     __shared__ f4 red[kWaves * MB * NS * 64];
+    __shared__ int rlist[RT ? kRouteMax : 1];            // expert e's assignments (RT)
+    __shared__ int wcnt[kWaves];
 
     const int e = blockIdx.x / p.WE;
     const int j0 = (blockIdx.x % p.WE) * NS;             // first slab of the workgroup
-    const int row0 = p.offsets[e];
-    const int rows = p.offsets[e + 1] - row0;
-    if (rows <= 0)
-        return;
-
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
+    int row0 = 0, rows;
+    if constexpr (RT) {
+        rows = route_rows(p.topk_ids, p.T * p.topk, e, wave, lane, rlist, wcnt);
+    } else {
+        row0 = p.offsets[e];
+        rows = p.offsets[e + 1] - row0;
+    }
+    if (rows <= 0)
+        return;
+    // assignment of the expert's i-th row
+    auto row_of = [&](int i) __attribute__((always_inline)) {
+        if constexpr (RT)
+            return rlist[i];
+        else
+            return p.sorted[row0 + i];
+    };
     const int c = lane & 15, quad = lane >> 4;
     const int S = p.N >> 4;
     const int U = S >> 2;
@@ -259,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
             const int i = rb + 16 * mb + c;
             v_a[mb] = kOutside;
             if (i < rows) {
-                const int a = p.sorted[row0 + i];
+                const int a = row_of(i);
                 v_a[mb] = (static_cast<uint32_t>(a / p.topk) * p.K + 8 * quad) * 2;
             }
         }
@@ -434,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = rb + 16 * mb + 4 * quad + q;
-                orow[mb][q] = i < rows ? p.sorted[row0 + i] : -1;
+                orow[mb][q] = i < rows ? row_of(i) : -1;
                 osc[mb][q] = (p.row_scale && orow[mb][q] >= 0) ? p.row_scale[orow[mb][q]] : 1.0f;
             }
 #pragma unroll
@@ -464,28 +526,90 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
     }
 }
 
-template <int MB, int NS, bool ZP, bool BF>
+template <int MB, int NS, bool ZP, bool BF, bool RT>
 hipError_t launch_moe(const MoeParams &p, int blocks, hipStream_t s)
 {
-    hipLaunchKernelGGL((w4a16_moe_kernel<MB, NS, ZP, BF>), dim3(blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((w4a16_moe_kernel<MB, NS, ZP, BF, RT>), dim3(blocks), dim3(kThreads), 0, s,
+                       p);
     return hipGetLastError();
 }
 
-template <bool ZP, bool BF>
+template <bool ZP, bool BF, bool RT>
 hipError_t dispatch_moe(int mb, int ns, const MoeParams &p, int blocks, hipStream_t s)
 {
     switch (mb * 16 + ns) {
-    case 17: return launch_moe<1, 1, ZP, BF>(p, blocks, s);
-    case 18: return launch_moe<1, 2, ZP, BF>(p, blocks, s);
-    case 20: return launch_moe<1, 4, ZP, BF>(p, blocks, s);
-    case 24: return launch_moe<1, 8, ZP, BF>(p, blocks, s);
-    case 33: return launch_moe<2, 1, ZP, BF>(p, blocks, s);
-    case 34: return launch_moe<2, 2, ZP, BF>(p, blocks, s);
-    case 36: return launch_moe<2, 4, ZP, BF>(p, blocks, s);
-    case 65: return launch_moe<4, 1, ZP, BF>(p, blocks, s);
-    case 66: return launch_moe<4, 2, ZP, BF>(p, blocks, s);
+    case 17: return launch_moe<1, 1, ZP, BF, RT>(p, blocks, s);
+    case 18: return launch_moe<1, 2, ZP, BF, RT>(p, blocks, s);
+    case 20: return launch_moe<1, 4, ZP, BF, RT>(p, blocks, s);
+    case 33: return launch_moe<2, 1, ZP, BF, RT>(p, blocks, s);
+    case 34: return launch_moe<2, 2, ZP, BF, RT>(p, blocks, s);
+    case 36: return launch_moe<2, 4, ZP, BF, RT>(p, blocks, s);
+    case 65: return launch_moe<4, 1, ZP, BF, RT>(p, blocks, s);
+    case 66: return launch_moe<4, 2, ZP, BF, RT>(p, blocks, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <bool RT>
+hipError_t dispatch_moe_fmt(bool zp, bool bf, int mb, int ns, const MoeParams &p, int blocks,
+                            hipStream_t s)
+{
+    if (zp)
+        return bf ? dispatch_moe<true, true, RT>(mb, ns, p, blocks, s)
+                  : dispatch_moe<true, false, RT>(mb, ns, p, blocks, s);
+    return bf ? dispatch_moe<false, true, RT>(mb, ns, p, blocks, s)
+              : dispatch_moe<false, false, RT>(mb, ns, p, blocks, s);
+}
+
+// Checks shared by both entries, the launch shape, and the launch.  `routed`: the product
+// lists each expert's rows itself from p.topk_ids.
+int moe_run(MoeParams &p, int zero_points, int act_dtype, bool routed, void *stream)
+{
+    const int T = p.T, topk = p.topk, E = p.E, K = p.K, N = p.N;
+    if (!p.A || !p.packed || !p.params || !p.C || T < 0 || topk < 1 || E < 1 || K < 0 ||
+        N < 0 || (zero_points != 0 && zero_points != 1) ||
+        (act_dtype != W4A16_ACT_F16 && act_dtype != W4A16_ACT_BF16))
+        return W4A16_EINVAL;
+    if (K == 0 || K % kGroup || N == 0 || N % 256)
+        return W4A16_ESHAPE;
+    // 32-bit buffer offsets, and the dead loads' offset above every buffer
+    const uint64_t R = static_cast<uint64_t>(T) * static_cast<uint64_t>(topk);
+    if (static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
+        static_cast<uint64_t>(T) * static_cast<uint64_t>(K) * 2 >= kOutside ||
+        R * static_cast<uint64_t>(N) * 2 >= kOutside ||
+        static_cast<uint64_t>(K / kGroup) * static_cast<uint64_t>(N) * 4 >= kOutside ||
+        (routed && R > static_cast<uint64_t>(kRouteMax)))
+        return W4A16_ESHAPE;
+    w4a16_detail::DeviceInfo d;
+    const int rc = w4a16_detail::current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    if (T == 0)
+        return W4A16_OK;
+
+    // Rows per block from the mean rows per expert (blocks sized for the busiest expert
+    // measure up to 2x slower: every block pays 4 A loads per 16 rows and 32-k step).  Four
+    // slabs per workgroup (as many weight loads per K step as A loads with 16-row blocks),
+    // fewer only while the experts in use -- at most min(E, T * topk) -- would not give
+    // every CU a workgroup.
+    const long long mean_rows = (static_cast<long long>(R) + E - 1) / E;
+    const int mb = mean_rows <= 16 ? 1 : (mean_rows <= 32 ? 2 : 4);
+    const long long S = N / 16;
+    const long long active = std::min<long long>(E, static_cast<long long>(R));
+    int ns = mb == 4 ? 2 : 4;
+    while (ns > 1 && active * ((S + ns - 1) / ns) < d.cus)
+        ns /= 2;
+    p.G = K / kGroup;
+    p.WE = static_cast<int>((S + ns - 1) / ns);
+    const long long blocks = static_cast<long long>(p.WE) * E;
+    if (blocks > INT_MAX)
+        return W4A16_ESHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = act_dtype == W4A16_ACT_BF16;
+    const hipError_t e =
+        routed ? dispatch_moe_fmt<true>(zero_points != 0, bf, mb, ns, p, static_cast<int>(blocks), s)
+               : dispatch_moe_fmt<false>(zero_points != 0, bf, mb, ns, p, static_cast<int>(blocks), s);
+    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
 }
 
 }  // namespace
@@ -512,38 +636,9 @@ extern "C" int w4a16_moe_gemm(const void *A, const uint32_t *packed, const uint1
                               const float *row_scale, void *C, int T, int topk, int E, int K,
                               int N, int zero_points, int act_dtype, void *stream)
 {
-    if (!A || !packed || !params || !sorted_ids || !expert_offsets || !C || T < 0 || topk < 1 ||
-        E < 1 || K < 0 || N < 0 || (zero_points != 0 && zero_points != 1) ||
-        (act_dtype != W4A16_ACT_F16 && act_dtype != W4A16_ACT_BF16))
+    if (!sorted_ids || !expert_offsets)
         return W4A16_EINVAL;
-    if (K == 0 || K % kGroup || N == 0 || N % 256)
-        return W4A16_ESHAPE;
-    // 32-bit buffer offsets, and the dead loads' offset above every buffer
-    const uint64_t R = static_cast<uint64_t>(T) * static_cast<uint64_t>(topk);
-    if (static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
-        static_cast<uint64_t>(T) * static_cast<uint64_t>(K) * 2 >= kOutside ||
-        R * static_cast<uint64_t>(N) * 2 >= kOutside ||
-        static_cast<uint64_t>(K / kGroup) * static_cast<uint64_t>(N) * 4 >= kOutside)
-        return W4A16_ESHAPE;
-    w4a16_detail::DeviceInfo d;
-    const int rc = w4a16_detail::current_device(&d);
-    if (rc != W4A16_OK)
-        return rc;
-    if (T == 0)
-        return W4A16_OK;
-
-    // Rows per block from the mean rows per expert; slabs per workgroup so that the experts
-    // in use (at most min(E, T * topk)) give about two workgroups per CU.
-    const long long mean_rows = (static_cast<long long>(R) + E - 1) / E;
-    const int mb = mean_rows <= 16 ? 1 : (mean_rows <= 32 ? 2 : 4);
-    const int nsmax = mb == 1 ? 8 : (mb == 2 ? 4 : 2);
-    const long long S = N / 16;
-    const long long active = std::min<long long>(E, static_cast<long long>(R));
-    long long want = (active * S + 2LL * d.cus - 1) / (2LL * d.cus);
-    int ns = 1;
-    while (ns < nsmax && ns < want)
-        ns *= 2;
-    MoeParams p;
+    MoeParams p{};
     p.A = static_cast<const uint16_t *>(A);
     p.packed = reinterpret_cast<const u4 *>(packed);
     p.params = params;
@@ -556,19 +651,27 @@ extern "C" int w4a16_moe_gemm(const void *A, const uint32_t *packed, const uint1
     p.E = E;
     p.K = K;
     p.N = N;
-    p.G = K / kGroup;
-    p.WE = static_cast<int>((S + ns - 1) / ns);
-    const long long blocks = static_cast<long long>(p.WE) * E;
-    if (blocks > INT_MAX)
-        return W4A16_ESHAPE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool bf = act_dtype == W4A16_ACT_BF16;
-    hipError_t e;
-    if (zero_points)
-        e = bf ? dispatch_moe<true, true>(mb, ns, p, static_cast<int>(blocks), s)
-               : dispatch_moe<true, false>(mb, ns, p, static_cast<int>(blocks), s);
-    else
-        e = bf ? dispatch_moe<false, true>(mb, ns, p, static_cast<int>(blocks), s)
-               : dispatch_moe<false, false>(mb, ns, p, static_cast<int>(blocks), s);
-    return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
+    return moe_run(p, zero_points, act_dtype, false, stream);
+}
+
+extern "C" int w4a16_moe_gemm_topk(const void *A, const uint32_t *packed, const uint16_t *params,
+                                   const int32_t *topk_ids, const float *row_scale, void *C,
+                                   int T, int topk, int E, int K, int N, int zero_points,
+                                   int act_dtype, void *stream)
+{
+    if (!topk_ids)
+        return W4A16_EINVAL;
+    MoeParams p{};
+    p.A = static_cast<const uint16_t *>(A);
+    p.packed = reinterpret_cast<const u4 *>(packed);
+    p.params = params;
+    p.topk_ids = topk_ids;
+    p.row_scale = row_scale;
+    p.C = static_cast<uint16_t *>(C);
+    p.T = T;
+    p.topk = topk;
+    p.E = E;
+    p.K = K;
+    p.N = N;
+    return moe_run(p, zero_points, act_dtype, true, stream);
 }

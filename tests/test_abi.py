@@ -351,3 +351,19 @@ def test_moe_entry_points_reject_bad_arguments_before_any_device_call():
     assert call(N=320) == w4.ESHAPE                    # N a multiple of 256
     assert call(K=65536, N=65536) == w4.ESHAPE         # 2 GiB of codes per expert
     assert call(T=600000, K=4096) == w4.ESHAPE         # A past 2^31 bytes
+
+
+def test_moe_routing_entry_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(256)
+    # w4a16_moe_gemm_topk(A, packed, params, topk_ids, row_scale, C, T, topk, E, K, N,
+    #                     zero_points, act_dtype, stream)
+    assert lib.w4a16_moe_gemm_topk(d, d, d, None, None, d, 4, 2, 8, 1024, 1024, 0, 0,
+                                   None) == w4.EINVAL
+    assert lib.w4a16_moe_gemm_topk(None, d, d, d, None, d, 4, 2, 8, 1024, 1024, 0, 0,
+                                   None) == w4.EINVAL
+    assert lib.w4a16_moe_gemm_topk(d, d, d, d, None, d, 1025, 2, 8, 1024, 1024, 0, 0,
+                                   None) == w4.ESHAPE        # more than 2048 assignments
+    assert lib.w4a16_moe_gemm_topk(d, d, d, d, None, d, 4, 2, 8, 1024, 1000, 0, 0,
+                                   None) == w4.ESHAPE
+    assert w4.MOE_ROUTE_MAX == 2048

@@ -8,7 +8,8 @@ bf16 ulp (2^-8 relative) where the two sums straddle a rounding boundary: relati
 <= 4e-3 (below 2^-8 even if every element differed) and max abs <= 1e-2 * max|C_ref|.
 With fp16 activations a row is also bit-identical to the dense w4a16_gemm of the same token
 and expert when the dense call takes its whole-K kernel (same decode, same K split, same
-summation order).
+summation order).  The routing entry (w4a16_moe_gemm_topk) lists the same rows in the same
+order as w4a16_moe_align, so its results equal the presorted entry's bit for bit.
 """
 import gc
 
@@ -66,14 +67,18 @@ class Moe:
         scales = d["s_bits"] if self.act == "bf16" else d["s"].astype(np.float16)
         self.packed, self.params = w4.to_device(*w4.pack_experts(d["q"], scales, d["zeros"]))
 
-    def run(self, d, row_scale=True, out=None, topk_ids=None):
+    def run(self, d, row_scale=True, out=None, topk_ids=None, routed=False):
         ids = d["topk_ids"] if topk_ids is None else topk_ids
         A = to_torch(d["A_bits"], self.act)
-        sorted_ids, offsets = w4.moe_align(torch.from_numpy(np.ascontiguousarray(ids)).cuda(),
-                                           self.E)
+        ids_d = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
         rs = torch.from_numpy(d["row_scale"]).cuda() if row_scale else None
-        C = w4.moe_gemm(A, self.packed, self.params, sorted_ids, offsets, ids.shape[1], self.E,
-                        self.N, row_scale=rs, zero_points=self.zp, out=out)
+        if routed:
+            C = w4.moe_gemm_topk(A, self.packed, self.params, ids_d, self.E, self.N,
+                                 row_scale=rs, zero_points=self.zp, out=out)
+        else:
+            sorted_ids, offsets = w4.moe_align(ids_d, self.E)
+            C = w4.moe_gemm(A, self.packed, self.params, sorted_ids, offsets, ids.shape[1],
+                            self.E, self.N, row_scale=rs, zero_points=self.zp, out=out)
         torch.cuda.synchronize()
         return C
 
@@ -134,10 +139,12 @@ def test_moe_against_oracle(E, topk, K, N, T, zp, act):
     assert done.all()
     check(values(C), want, act, f"{act} zp={zp} E={E} topk={topk} K={K} N={N} T={T}")
     assert torch.equal(W.run(d), C)                      # fixed summation order
+    assert torch.equal(W.run(d, routed=True), C)         # the routing entry: same bits
 
 
+@pytest.mark.parametrize("routed", [False, True])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
-def test_rows_of_no_expert_are_not_written(act):
+def test_rows_of_no_expert_are_not_written(act, routed):
     E, topk, K, N, T = 6, 3, 512, 512, 20
     d = draw_moe(E, topk, K, N, T, seed=5, act=act)
     ids = d["topk_ids"].copy()
@@ -146,7 +153,7 @@ def test_rows_of_no_expert_are_not_written(act):
     W = Moe(d)
     dt = torch.bfloat16 if act == "bf16" else torch.float16
     out = torch.full((T * topk, N), -7.0, dtype=dt, device="cuda")
-    W.run(d, out=out, topk_ids=ids)
+    W.run(d, out=out, topk_ids=ids, routed=routed)
     want, done = ref(d, topk_ids=ids)
     got = values(out)
     assert (got[~done] == -7.0).all()
@@ -170,6 +177,21 @@ def test_f16_rows_equal_the_dense_product_of_their_token_and_expert():
         De = w4.gemm(Ae, W.packed[e].reshape(per), W.params[e].view(torch.float16).reshape(-1), N)
         torch.cuda.synchronize()
         assert torch.equal(De.cpu(), C[torch.from_numpy(rows)]), e
+
+
+def test_routing_entry_at_its_limit():
+    # T * topk = 2048, the most the routing entry takes
+    E, topk, K, N, T = 16, 8, 256, 512, 256
+    d = draw_moe(E, topk, K, N, T, seed=12, act="f16")
+    ids = d["topk_ids"].copy()
+    W = Moe(d)
+    with pytest.raises(ValueError):
+        w4.moe_gemm_topk(to_torch(d["A_bits"][:T - 1], "f16"), W.packed, W.params,
+                         torch.from_numpy(ids).cuda(), E, N)
+    C = W.run(d, routed=True)
+    assert torch.equal(C, W.run(d))
+    want, _ = ref(d)
+    check(values(C), want, "f16", "routing at 2048 assignments")
 
 
 def test_row_scale_none_is_one():
@@ -212,10 +234,13 @@ def test_moe_full_size_sampled(sh, act):
     for T in sh.Ts:
         dT = dict(d, A=d["A"][:T], A_bits=d["A_bits"][:T], topk_ids=d["topk_ids"][:T],
                   row_scale=d["row_scale"][:T * sh.topk])
-        C = values(W.run(dT))
+        Ct = W.run(dT)
+        C = values(Ct)
         want, done = ref(dT, cols=cols)
         assert done.all()
         check(C[:, cols], want, act, f"{sh.name} {act} T={T} ({len(cols)} sampled columns)")
+        if T * sh.topk <= w4.MOE_ROUTE_MAX:
+            assert torch.equal(W.run(dT, routed=True), Ct)
     del W, d
     gc.collect()
     torch.cuda.empty_cache()
