@@ -329,8 +329,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-cols", type=int, default=65536,
                     help="columns of the CPU-baseline sample (0 skips it)")
-    ap.add_argument("--copies", type=int, default=2,
-                    help="weight copies rotated between calls so no call hits the MALL")
+    ap.add_argument("--copies", type=int, default=9,
+                    help="weight copies rotated between calls: more copies than calls per step, "
+                         "so no call finds its weights still in the 256 MB memory-side cache")
     ap.add_argument("--format-steps", type=int, default=20,
                     help="timed calls per M for each other packed format (0 skips them)")
     ap.add_argument("--moe-steps", type=int, default=20,
