@@ -7,18 +7,20 @@ bytes per call: D = 2MK (A) + KN/2 (codes) + KN/64 (scales) + 2MN (C); flops F =
 Roofline per call: T_bound = max(D / 8 TB/s, F / 2.5 PFLOP/s); fp16-weight byte bound
 D16 = 2MK + 2KN + 2MN (the MARLIN paper's uncompressed reference point).
 
-`roofline` covers the dominant kernel: the whole-K-workgroup kernel that serves M = 1..16
-(nine 16-column slabs per workgroup on this weight), five of the eight calls and about half
-the sweep's time; HBM-bound, so achieved = its algorithmic bytes per launch / its mean
-launch time.  `roofline_by_kernel` gives the same for every kernel
-of the sweep, the 128-row (M = 128) kernel against the fp16 MFMA peak.
+`roofline` covers the dominant kernel: the whole-K-workgroup kernel as it serves M = 1..8
+(six 16-column slabs per workgroup on this weight, three workgroups per CU), four of the eight
+calls and about 40% of the sweep's time; HBM-bound, so achieved = its algorithmic bytes per
+launch / its mean launch time.  `roofline_by_kernel` gives the same for every kernel of the
+sweep (M = 16 runs the same kernel with nine slabs, two workgroups per CU), the 128-row
+(M = 128) kernel against the fp16 MFMA peak.
 
 Also reported, outside `value`: `formats`, the per-call time of the other packed formats
 (one scale per column, zero points, both) on the same weight at M = 1, 16, 64, 128, timed
 call by call alternately with the group-128 symmetric format; `repack`, the load-time
 conversion of a checkpoint-style packed weight of the same size into the multiply's layout;
 `sparse_24`, the 2:4-sparse path on the same weight with two of every four codes pruned, at
-every M, alternated call by call with the dense path.
+every M, alternated call by call with the dense path; `moe`, the mixture-of-experts grouped
+product on two layer shapes, fp16 and bf16 activations.
 
 Prints one JSON line on stdout.  Single GPU only.
 """
@@ -46,7 +48,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
 # 16-column slabs over all of K up to M = 16, 32-row tiles up to 32, 64-row up to 64, then
 # 128-row tiles on this shape), and the roof that bounds it.
 KERNELS = [
-    ("w4a16_gemm_skinny_kernel<9> (whole-K workgroups, 9 slabs)", (1, 2, 4, 8, 16), "hbm"),
+    ("w4a16_gemm_skinny_kernel<6> (whole-K workgroups, 6 slabs, 3 per CU)", (1, 2, 4, 8), "hbm"),
+    ("w4a16_gemm_skinny_kernel<9> (whole-K workgroups, 9 slabs, 2 per CU)", (16,), "hbm"),
     ("w4a16_gemm_kernel<2,4> (32-row tiles)", (32,), "hbm"),
     ("w4a16_gemm_kernel<4,4> (64-row tiles)", (64,), "hbm"),
     ("w4a16_gemm_wide_kernel<4,2> (128-row tiles)", (128,), "mfma"),

@@ -1672,7 +1672,10 @@ constexpr int kSkinnyMaxNS = 10;
 
 // Skinny kernel (M <= 16, N a multiple of 256): NS = the fewest slabs per workgroup that keep
 // the workgroups within two per CU, so every workgroup streams as many bytes as possible at
-// once.  With one slab per workgroup four of a wave's six loads per tile are A fragments;
+// once.  At M <= 8 (A mostly rows past M, read as zero without memory traffic) three per CU
+// measure faster where that leaves 2 to 7 slabs (7 still fits three workgroups' registers):
+// 72k x 18k 110.5 vs 113.2 us at M = 1; at M = 16 the extra A re-reads make it slower (128.9
+// vs 124.4 us).  With one slab per workgroup four of a wave's six loads per tile are A fragments;
 // there the stripe kernel measures faster once K runs long (28672 x 8192: 31 vs 33 us at
 // M = 1), while on every shorter or wider weight measured the skinny kernel is faster
 // (1.1x to 4x).  Its dead loads point 2 GiB past the buffer starts, so the weights and A
@@ -1682,8 +1685,12 @@ int skinny_slabs(int M, int K, int N, int cus)
     if (M > 16 || N % 256)
         return 0;
     const long long S = N / 16;
-    const long long per = 2LL * cus;
-    const long long ns = (S + per - 1) / per;
+    long long ns = (S + 2LL * cus - 1) / (2LL * cus);
+    if (M <= 8) {
+        const long long ns3 = (S + 3LL * cus - 1) / (3LL * cus);
+        if (ns3 >= 2 && ns3 <= 7)
+            ns = ns3;
+    }
     if (ns > kSkinnyMaxNS || (ns == 1 && K / kGroup > 128) ||
         static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
         static_cast<uint64_t>(16) * static_cast<uint64_t>(K) * 2 >= kOutside)
