@@ -28,14 +28,18 @@
 // * Contraction: v_mfma_f32_16x16x32_f16, tokens as the 16 rows, output columns as the 16
 //   columns; k-step loop outermost so independent accumulators separate dependent MFMAs
 //   (MARLIN paper sec. 3.2 "Tensor Core Level").
-// * Scheduling.  Tiles are 128 (K) x Nt (N) x Mt (M rows).  Tile order: column slice, then
-//   64-row M sub-problem, then K (weights of a slice are re-read from cache for the next M
+// * Scheduling.  Tiles are 128 (K) x Nt (N) x Mt (M rows).  Tile order: M sub-problem, then
+//   column slice, then K (with several M sub-problems the weight grid is walked once per
 //   sub-problem: the pages' "virtual replication" of the weight grid for large M).  Each
 //   workgroup takes one contiguous run of floor/ceil(T/W) tiles (a stripe), so every CU gets
 //   the same work and only stripe ends split a slice.  Pages: deep-dive page sections
 //   "为什么规则二维网格会浪费最后一波 SM" and "大 M 时虚拟复制权重网格"; MARLIN README
 //   page, striped partitioning.  Workgroup ids are remapped so consecutive stripes sit on
-//   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs).
+//   the same XCD (the hardware deals workgroups round-robin over the 8 XCDs), so each XCD
+//   works on few M sub-problems at a time and their rows of A stay in its L2, while the
+//   weights, read once per sub-problem, come from HBM or the memory-side cache (sub-problem
+//   outermost measured 5-7% faster than slice outermost at M = 256..1024, which re-read all
+//   of A per slice).
 // * Cross-workgroup reduction.  Only the first and last slice of a stripe can be shared
 //   with a neighbouring stripe.  A stripe that entered a slice part-way writes its fp32 piece
 //   to its own workspace slot with device-scope stores and streams on without waiting; the
@@ -82,6 +86,7 @@ struct Params {
     int G;                    // K / 128: tiles per slice
     int Gs;                   // scale groups per column: G, or 1 for one scale per column
     int P;                    // M sub-problems of Mt rows
+    int S;                    // column slices of Nt columns
     int W;                    // workgroups = stripes
     long long T;              // total tiles = (N / Nt) * P * G
 };
@@ -124,7 +129,7 @@ struct Tile {
 };
 
 
-// Where the next tile's loads come from.  Tiles run in (slice, M sub-problem, K) order;
+// Where the next tile's loads come from.  Tiles run in (M sub-problem, slice, K) order;
 // inside a slice only the K step changes and every offset moves by a constant.
 struct LoadCursor {
     int g, pm, s;
@@ -436,8 +441,8 @@ template <int MB, int NBW, int WAVES = kWaves, bool TR = false>
 __device__ __forceinline__ void write_c(const Params &p, __amdgpu_buffer_rsrc_t rC, int wave,
                                         int lane, long long sigma, const f4 (&acc)[MB][NBW])
 {
-    const long long s = sigma / p.P;
-    const int pm = static_cast<int>(sigma - s * p.P);
+    const int pm = static_cast<int>(sigma / p.S);
+    const long long s = sigma - static_cast<long long>(pm) * p.S;
     const uint32_t rowN = opaque(static_cast<uint32_t>(p.N) * 2);
     if constexpr (TR) {
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -608,7 +613,7 @@ __device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_
                                           long long &nonown, long long &own)
 {
     if constexpr (F::COL) {
-        const long long sl = sigma / p.P;
+        const long long sl = sigma % p.S;
         uint32_t pr[PRegs<NBW, F::ZP, Part::Scales>::n];
         load_params<NBW, F::ZP, Part::Scales>(rS, lane, static_cast<uint32_t>(sl) * WAVES + wave,
                                               pr);
@@ -770,8 +775,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     // each A load is issued before the weight load of the same tile (see the schedule below).
     LoadCursor lc;
     lc.g = g;
-    lc.s = static_cast<int>(sigma / p.P);
-    lc.pm = static_cast<int>(sigma - static_cast<long long>(lc.s) * p.P);
+    lc.pm = static_cast<int>(sigma / p.S);
+    lc.s = static_cast<int>(sigma - static_cast<long long>(lc.pm) * p.S);
     load_cursor_set<MB, NBW>(p, wave, lc);
     uint32_t a_voff[MB];
     a_thread_offsets<MB>(p, tid, lc.pm * 16 * MB, a_voff);
@@ -787,9 +792,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
             lc.a_soff += kGroup * 2;
             if (lc.g == p.G) {         // next slice (uniform, rare)
                 lc.g = 0;
-                if (++lc.pm == p.P) {
-                    lc.pm = 0;
-                    ++lc.s;
+                if (++lc.s == p.S) {
+                    lc.s = 0;
+                    ++lc.pm;
                 }
                 load_cursor_set<MB, NBW>(p, wave, lc);
                 a_thread_offsets<MB>(p, tid, lc.pm * 16 * MB, a_voff);
@@ -1059,8 +1064,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
     // i.e. waiting for everything.
     LoadCursor lc;
     lc.g = g;
-    lc.s = static_cast<int>(sigma / p.P);
-    lc.pm = static_cast<int>(sigma - static_cast<long long>(lc.s) * p.P);
+    lc.pm = static_cast<int>(sigma / p.S);
+    lc.s = static_cast<int>(sigma - static_cast<long long>(lc.pm) * p.S);
     load_cursor_set<MB, NBW, WAVES>(p, wave, lc);
     // byte offset of the wave's first A row at the load position's K step (uniform)
     auto a_rowoff = [&]() __attribute__((always_inline)) {
@@ -1078,9 +1083,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
             lc.a_soff += kGroup * 2;
             if (lc.g == p.G) {
                 lc.g = 0;
-                if (++lc.pm == p.P) {
-                    lc.pm = 0;
-                    ++lc.s;
+                if (++lc.s == p.S) {
+                    lc.s = 0;
+                    ++lc.pm;
                 }
                 load_cursor_set<MB, NBW, WAVES>(p, wave, lc);
             }
@@ -1988,6 +1993,7 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     p.G = c.G;
     p.Gs = col ? 1 : c.G;
     p.P = c.P;
+    p.S = c.S;
     p.W = c.W;
     p.T = c.T;
 
@@ -2082,6 +2088,7 @@ extern "C" int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16
     }
     const Config c = choose_config_24(M, K, N, d.cus);
     p.P = c.P;
+    p.S = c.S;
     p.W = c.W;
     p.T = c.T;
     const hipError_t e = c.MB == 1   ? launch<1, 4, FmtSp>(p, s)
