@@ -20,7 +20,10 @@ call by call alternately with the group-128 symmetric format; `repack`, the load
 conversion of a checkpoint-style packed weight of the same size into the multiply's layout;
 `sparse_24`, the 2:4-sparse path on the same weight with two of every four codes pruned, at
 every M, alternated call by call with the dense path; `moe`, the mixture-of-experts grouped
-product on two layer shapes, fp16 and bf16 activations.
+product on two layer shapes, fp16 and bf16 activations; `compute_sweep`, the compute-bound
+8192 x 28672 weight at M = 256, 512, 1024 with its fraction of the fp16 matrix peak;
+`tp8_rank_shapes`, one 8-way tensor-parallel rank's share of the Llama-2-70B block;
+`stream_read_reference`, the HBM read rate of a plain streaming read, for context.
 
 Prints one JSON line on stdout.  Single GPU only.
 """
@@ -325,6 +328,127 @@ def time_moe(w4, torch, dev, steps, stream):
     return rows
 
 
+def time_compute_sweep(w4, torch, dev, steps, stream):
+    """The compute-bound transition sweep (K = 8192, N = 28672, M = 256, 512, 1024, A ~ N(0,
+    0.5^2)): us per call, TFLOP/s and its fraction of the 2.5 PFLOP/s dense fp16 matrix peak
+    (MFMA utilisation), GB/s of the algorithmic bytes and the speed-up over the fp16-weight
+    byte bound.  Five weight copies (585 MB) rotate, more than the memory-side cache holds."""
+    from workloads import COMPUTE_SWEEP, draw_shape
+    sh = COMPUTE_SWEEP.shapes[0]
+    K, N = sh.K, sh.N
+    A, q, s = draw_shape(sh, seed=0)
+    pd, sd = w4.to_device(*w4.pack(q, s), dev)
+    cps = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(4)]
+    Ad = torch.from_numpy(A).to(dev)
+    rows = []
+    for M in sh.Ms:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = w4.new_workspace(M, K, N, dev)
+        evs = []
+        for i in range(5 + steps):
+            p_, s_ = cps[i % len(cps)]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            w4.gemm(Ad[:M], p_, s_, N, out=out, ws=ws, stream=stream)
+            e1.record(stream)
+            if i >= 5:
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        F, D, D16 = flops(M, K, N), algorithmic_bytes(M, K, N), fp16_weight_bytes(M, K, N)
+        rows.append({"M": M, "K": K, "N": N, "us": round(us, 2),
+                     "TFLOPs": round(F / us / 1e6, 1),
+                     "mfma_frac": round(F / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
+                     "GBps": round(D / us / 1e3, 1),
+                     "speedup_vs_fp16_bound": round(max(D16 / (HBM_PEAK_GBPS * 1e3),
+                                                        F / (MFMA_F16_PEAK_TFLOPS * 1e6)) / us, 3)})
+        log(f"compute sweep M={M:5d} {us:8.1f} us  {F / us / 1e6:7.1f} TFLOP/s "
+            f"({F / us / 1e6 / MFMA_F16_PEAK_TFLOPS:5.1%} of fp16 MFMA peak)")
+    del cps, pd, sd
+    torch.cuda.empty_cache()
+    return rows
+
+
+def time_tp8_rank(w4, torch, dev, steps, stream):
+    """One 8-way tensor-parallel rank's share of the Llama-2-70B block (the kernel at the
+    local shapes a sharded layer runs), M = 16, 32, 128: back-to-back calls between one event
+    pair (these kernels run for a few us, which a pair of events per call would inflate);
+    enough weight copies rotate that each call's weights come from HBM."""
+    from workloads import LLAMA2_70B_TP8, draw_shape
+    rows = []
+    for sh in LLAMA2_70B_TP8.shapes:
+        A, q, s = draw_shape(sh, seed=0)
+        pd, sd = w4.to_device(*w4.pack(q, s), dev)
+        wbytes = sh.K * sh.N // 2 + sh.K // GROUP * sh.N * 2
+        ncp = max(2, -(-600_000_000 // wbytes))
+        cps = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(ncp - 1)]
+        Ad = torch.from_numpy(A).to(dev)
+        for M in sh.Ms:
+            out = torch.empty((M, sh.N), dtype=torch.float16, device=dev)
+            ws = w4.new_workspace(M, sh.K, sh.N, dev)
+            for i in range(5):
+                p_, s_ = cps[i % len(cps)]
+                w4.gemm(Ad[:M], p_, s_, sh.N, out=out, ws=ws, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                p_, s_ = cps[i % len(cps)]
+                w4.gemm(Ad[:M], p_, s_, sh.N, out=out, ws=ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            D = algorithmic_bytes(M, sh.K, sh.N)
+            rows.append({"shape": sh.name, "M": M, "K": sh.K, "N": sh.N, "us": round(us, 2),
+                         "GBps": round(D / us / 1e3, 1),
+                         "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4),
+                         "weight_copies_rotated": ncp})
+            log(f"tp8 {sh.name:16s} M={M:4d} {us:7.1f} us  {D / us / 1e3:6.0f} GB/s")
+        del cps, pd, sd
+        torch.cuda.empty_cache()
+    return rows
+
+
+def stream_read_rate(w4, torch, dev, stream):
+    """Context for the HBM fraction: the read rate of a plain streaming read (w4a16_read_probe:
+    each workgroup one contiguous chunk, the fastest pattern measured) over 4 GiB, best of 5
+    calls."""
+    x = torch.empty(1 << 31, dtype=torch.float16, device=dev)
+    x.fill_(1.0)
+    out = torch.zeros(2048, dtype=torch.int32, device=dev)
+    best = 0.0
+    for _ in range(6):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        w4.read_probe(x, out=out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return {"kernel": "w4a16_read_probe over 4 GiB (contiguous chunk per workgroup, 128-bit "
+                      "non-temporal loads)",
+            "GBps": round(best, 1), "frac_of_spec": round(best / HBM_PEAK_GBPS, 4)}
+
+
+def device_state(torch, props):
+    """Software and clock state of the run (clocks and power through rocm-smi when present)."""
+    import subprocess
+    st = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__,
+          "name": props.name, "arch": getattr(props, "gcnArchName", ""),
+          "cus": props.multi_processor_count}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
+                            "--showmemuse"], capture_output=True, text=True, timeout=20)
+        st["rocm_smi"] = [ln.strip() for ln in r.stdout.splitlines()
+                          if ":" in ln and ("clk" in ln.lower() or "power" in ln.lower())][:16]
+    except Exception as exc:            # tool missing or not permitted: note it and go on
+        st["rocm_smi"] = f"unavailable ({type(exc).__name__})"
+    return st
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +463,9 @@ def main():
                     help="timed calls per M for each other packed format (0 skips them)")
     ap.add_argument("--moe-steps", type=int, default=20,
                     help="timed calls per token count of each MoE layer shape (0 skips them)")
+    ap.add_argument("--extra-steps", type=int, default=20,
+                    help="timed calls per M of the compute sweep and the tensor-parallel rank "
+                         "shapes, plus the stream-read reference (0 skips them)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
@@ -458,6 +585,12 @@ def main():
         sparse = time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, args.format_steps,
                              max(2, args.warmup // 4), args.copies, stream, copies)
     moe = time_moe(w4, torch, dev, args.moe_steps, stream) if args.moe_steps > 0 else None
+    compute_sweep = tp8 = stream_ref = None
+    if args.extra_steps > 0:
+        compute_sweep = time_compute_sweep(w4, torch, dev, args.extra_steps, stream)
+        tp8 = time_tp8_rank(w4, torch, dev, args.extra_steps, stream)
+        stream_ref = stream_read_rate(w4, torch, dev, stream)
+        log(f"stream read reference: {stream_ref}")
     formats = None
     if args.format_steps > 0:
         formats = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
@@ -477,8 +610,10 @@ def main():
         "repack": repack,
         "sparse_24": sparse,
         "moe": moe,
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count},
+        "compute_sweep": compute_sweep,
+        "tp8_rank_shapes": tp8,
+        "stream_read_reference": stream_ref,
+        "device": device_state(torch, props),
     }
     if args.cpu_cols > 0:
         nthreads = min(16, os.cpu_count() or 1)

@@ -339,6 +339,17 @@ int w4a16_moe_gemm_topk(const void *A, const uint32_t *packed, const uint16_t *p
                         int topk, int E, int K, int N, int zero_points, int act_dtype,
                         void *stream);
 
+/*
+ * Measurement support, not part of the multiply: streams `bytes` from device buffer `src`
+ * (each workgroup one contiguous chunk, 128-bit non-temporal loads, the fastest read pattern
+ * measured) and discards the data, for a measured HBM read rate to compare the multiply against
+ * (MARLIN paper sec. 3.4: the layer is bound by weight loading).  `out`: device uint32[2048],
+ * written only in the rare case a checksum equals a fixed value (the writes keep the loads
+ * alive).  Device, asynchronous on `stream`.  Errors: W4A16_EINVAL (null pointer, bytes 0
+ * or not a multiple of 16, src not 16-byte aligned), W4A16_EUNSUPPORTED, W4A16_EHIP.
+ */
+int w4a16_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

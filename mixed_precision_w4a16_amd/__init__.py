@@ -72,6 +72,8 @@ _lib.w4a16_moe_gemm.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, 
 _lib.w4a16_moe_gemm.restype = _i
 _lib.w4a16_moe_gemm_topk.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]
 _lib.w4a16_moe_gemm_topk.restype = _i
+_lib.w4a16_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _p]
+_lib.w4a16_read_probe.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
@@ -79,7 +81,7 @@ ACT_F16, ACT_BF16 = 0, 1
 EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
             "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
             "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24",
-            "w4a16_moe_align", "w4a16_moe_gemm", "w4a16_moe_gemm_topk")
+            "w4a16_moe_align", "w4a16_moe_gemm", "w4a16_moe_gemm_topk", "w4a16_read_probe")
 
 
 class W4A16Error(RuntimeError):
@@ -442,4 +444,20 @@ def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, 
             A.data_ptr(), packed.data_ptr(), params.data_ptr(), sorted_ids.data_ptr(),
             offsets.data_ptr(), None if row_scale is None else row_scale.data_ptr(),
             out.data_ptr(), T, topk, E, K, N, int(bool(zero_points)), act, stream.cuda_stream))
+    return out
+
+
+def read_probe(x, out=None, stream=None):
+    """Measurement support (w4a16_read_probe): stream the bytes of CUDA tensor x (each
+    workgroup one contiguous chunk) and discard them.  out: optional int32 [2048] tensor."""
+    import torch
+    if not x.is_cuda or not x.is_contiguous() or (x.numel() * x.element_size()) % 16:
+        raise ValueError("x must be a contiguous CUDA tensor of a multiple of 16 bytes")
+    if out is None:
+        out = torch.zeros(2048, dtype=torch.int32, device=x.device)
+    with torch.cuda.device(x.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        _check("w4a16_read_probe", _lib.w4a16_read_probe(x.data_ptr(), x.numel() * x.element_size(),
+                                                         out.data_ptr(), stream.cuda_stream))
     return out

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "gemm.hip"), os.path.join(CSRC, "repack.hip"),
-           os.path.join(CSRC, "moe.hip"),
+           os.path.join(CSRC, "moe.hip"), os.path.join(CSRC, "probe.hip"),
            os.path.join(CSRC, "pack.cpp")]
 LIB = os.path.join(PKG, "libw4a16.so")
 ARCH = "gfx950"

@@ -367,3 +367,13 @@ def test_moe_routing_entry_rejects_bad_arguments_before_any_device_call():
     assert lib.w4a16_moe_gemm_topk(d, d, d, d, None, d, 4, 2, 8, 1024, 1000, 0, 0,
                                    None) == w4.ESHAPE
     assert w4.MOE_ROUTE_MAX == 2048
+
+
+def test_read_probe_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(256)
+    assert lib.w4a16_read_probe(None, 4096, d, None) == w4.EINVAL
+    assert lib.w4a16_read_probe(d, 0, d, None) == w4.EINVAL
+    assert lib.w4a16_read_probe(d, 4100, d, None) == w4.EINVAL
+    assert lib.w4a16_read_probe(ctypes.c_void_p(264), 4096, d, None) == w4.EINVAL
+    assert lib.w4a16_read_probe(d, 4096, None, None) == w4.EINVAL

@@ -15,7 +15,8 @@ torch = pytest.importorskip("torch")
 
 import mixed_precision_w4a16_amd as w4
 import oracle
-from workloads import ALL, COMPUTE_SWEEP, LARGE, LLAMA2_70B, LLAMA2_7B, SMALL, draw
+from workloads import (ALL, COMPUTE_SWEEP, LARGE, LLAMA2_70B, LLAMA2_70B_TP8, LLAMA2_7B, SMALL,
+                       draw)
 
 pytestmark = pytest.mark.gpu
 
@@ -282,6 +283,16 @@ def test_full_size_workloads_sampled(shape):
     _sampled_check(shape)
 
 
+# One tensor-parallel rank's shapes of the 70B block, every column against the oracle.
+@pytest.mark.parametrize("shape", LLAMA2_70B_TP8.shapes, ids=lambda sh: sh.name)
+def test_tensor_parallel_rank_shapes(shape):
+    A, q, s = draw(shape.K, shape.N, max(shape.Ms), seed=3)
+    W = Weights(q, s)
+    ref = oracle.gemm(A, q, s)
+    for M in shape.Ms:
+        check(W.run(A[:M]), ref[:M], f"{shape.name} M={M}")
+
+
 # ------------------------------------------------------------------ other packed formats
 # One scale per column (group = K) and zero points per group and column (w4a16_pack_zp,
 # w4a16_gemm_ex), against the oracle with the same group and zero points.
@@ -453,3 +464,49 @@ def test_whole_k_workgroups_one_hot_rows_are_bit_exact(fmt):
         zz = 8 if z is None else z[k // g].astype(np.float64)
         w = s[k // g].astype(np.float64) * (q[k].astype(np.float64) - zz)
         assert same(C[m], w.astype(np.float16)), (fmt, m, k)
+
+
+# Seeded random shapes across every kernel choice (whole-K at M <= 16 with two or three
+# workgroups per CU, 16/32/64-row stripes, 128-row tiles, several row sub-problems), the
+# stripe-count model's range of split pieces and N from one to many slices, for all four
+# formats.  The oracle runs them in seconds.
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([1, 2, 3, 5, 8, 11, 16, 17, 24, 31, 32, 40, 64, 65, 100, 128, 129, 200]))
+        K = 128 * int(rng.integers(1, 17))
+        N = 64 * int(rng.integers(1, 49))
+        if rng.random() < 0.4:
+            N = 256 * int(rng.integers(1, 13))
+        out.append((M, K, N))
+    return out
+
+
+@pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("col", [False, True])
+@pytest.mark.parametrize("M,K,N", _random_shapes(12, 2026))
+def test_random_shapes_every_format(M, K, N, col, zp):
+    A, q, s = draw(K, N, M, seed=M * 7 + K + N)
+    group = K if col else 128
+    if col:
+        s = s[:1].copy()
+    z = None
+    if zp:
+        from workloads import draw_zeros
+        z = draw_zeros(K, N, seed=M + K, group=group)
+    packed, params = w4.pack(q, s, group=group, zeros=z)
+    pd, prm = w4.to_device(packed, params)
+    Ad = torch.from_numpy(A).cuda()
+    C = w4.gemm(Ad, pd, prm, N, group=group, zero_points=zp)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, q, s, group=group, zeros=z)
+    check(C.cpu().numpy(), ref, f"M={M} K={K} N={N} col={col} zp={zp}")
+
+
+def test_read_probe_streams_without_writing():
+    # all-ones fp16 words XOR to zero, never the checksum that would store
+    x = torch.ones(1 << 22, dtype=torch.float16, device="cuda")
+    out = w4.read_probe(x)
+    torch.cuda.synchronize()
+    assert int(out.count_nonzero()) == 0

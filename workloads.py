@@ -58,6 +58,15 @@ LLAMA2_70B = Workload("llama2_70b_block_m16_32_128", (
     Shape("70b_down", 28672, 8192, (16, 32, 128)),
 ))
 
+# One rank's share of the Llama-2-70B block under 8-way tensor parallelism (column-parallel
+# qkv and gate+up split N, row-parallel o and down split K): the kernel at the local shapes.
+LLAMA2_70B_TP8 = Workload("llama2_70b_tp8_rank_m16_32_128", (
+    Shape("70b_tp8_qkv", 8192, 1280, (16, 32, 128)),
+    Shape("70b_tp8_o", 1024, 8192, (16, 32, 128)),
+    Shape("70b_tp8_gate_up", 8192, 7168, (16, 32, 128)),
+    Shape("70b_tp8_down", 3584, 8192, (16, 32, 128)),
+))
+
 COMPUTE_SWEEP = Workload("compute_8192x28672_m256_1024", (
     Shape("8192x28672", 8192, 28672, (256, 512, 1024), sigma=0.5),))
 
