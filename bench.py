@@ -97,6 +97,51 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_SPIN_CYCLES_PER_US = None
+
+
+def hold_gpu(torch, stream, us):
+    """Keep `stream` busy for about `us` microseconds with torch's spin kernel, so that calls
+    enqueued right after are all queued before the GPU reaches them: back-to-back timing of
+    kernels shorter than the host's per-call cost (the Python binding takes ~15-25 us a call)
+    then sees kernel time, not the host's launch rate.  The spin's clock is calibrated once."""
+    global _SPIN_CYCLES_PER_US
+    if _SPIN_CYCLES_PER_US is None:
+        torch.cuda._sleep(1000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(2_000_000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_US = 2_000_000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
+
+
+def queued_batch(torch, stream, calls, warmup=5):
+    """GPU time per call of `calls(i)` for i in range(n) run back to back: `warmup` untimed
+    calls (which also measure the host's cost per call), a spin that outlasts enqueuing the
+    batch, then the batch between one event pair.  Returns (us per call, queued) where
+    queued says the first event was still waiting behind the spin when the last call had
+    been enqueued, i.e. the GPU never waited for the host."""
+    n = calls.n
+    t0 = time.perf_counter()
+    for i in range(warmup):
+        calls(i)
+    host_us = (time.perf_counter() - t0) * 1e6 / max(warmup, 1)
+    torch.cuda.synchronize()
+    hold_gpu(torch, stream, 1.5 * host_us * n + 500.0)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        calls(warmup + i)
+    e1.record(stream)
+    queued = not e0.query()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n, queued
+
+
 def cpu_baseline(A, q, s, Ms, ncols, nthreads):
     """The oracle as it stands, on a column sample of the same workload and every M."""
     import oracle
@@ -289,7 +334,8 @@ def time_moe(w4, torch, dev, steps, stream):
                     rs = torch.from_numpy(d["row_scale"][:T * sh.topk]).to(dev)
                     out = torch.empty((T * sh.topk, sh.N), dtype=dt, device=dev)
                     ev, evt = [], []
-                    for i in range(4 + steps):
+
+                    def iteration(i):
                         p_, r_ = cps[i % len(cps)]
                         e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
                         e0.record(stream)
@@ -302,9 +348,21 @@ def time_moe(w4, torch, dev, steps, stream):
                         w4.moe_gemm_topk(A, p_, r_, ids, sh.E, sh.N, row_scale=rs, out=out,
                                          stream=stream)
                         e3.record(stream)
-                        if i >= 4:
-                            ev.append((e0, e1, e2))
-                            evt.append((e2, e3))
+                        return e0, e1, e2, e3
+                    # warm-up iterations measure the host's cost of one; the timed ones are
+                    # queued behind a spin that outlasts enqueuing them all, so the decode-size
+                    # calls (a few us each) are timed on the GPU, not at the host's launch rate
+                    t0 = time.perf_counter()
+                    for i in range(4):
+                        iteration(i)
+                    host_us = (time.perf_counter() - t0) * 1e6 / 4
+                    torch.cuda.synchronize()
+                    hold_gpu(torch, stream, 1.5 * host_us * steps + 500.0)
+                    for i in range(4, 4 + steps):
+                        e0, e1, e2, e3 = iteration(i)
+                        ev.append((e0, e1, e2))
+                        evt.append((e2, e3))
+                    queued = not ev[0][0].query()
                     torch.cuda.synchronize()
                     ua = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
                     ug = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
@@ -318,7 +376,8 @@ def time_moe(w4, torch, dev, steps, stream):
                                  "gemm_hbm_frac": round(D / ug / 1e3 / HBM_PEAK_GBPS, 4),
                                  "routed_us": round(ut, 2),
                                  "routed_GBps": round(D / ut / 1e3, 1),
-                                 "weight_copies_rotated": ncp})
+                                 "weight_copies_rotated": ncp,
+                                 "queued_ahead_of_gpu": queued})
                     log(f"moe {sh.name:12s} {act:4s} T={T:3d} experts={used[T]:2d}  align "
                         f"{ua:6.1f} us  gemm {ug:7.1f} us  {D / ug / 1e3:6.0f} GB/s "
                         f"({D / ug / 1e3 / HBM_PEAK_GBPS:5.1%} HBM)  routed {ut:7.1f} us "
@@ -373,8 +432,8 @@ def time_compute_sweep(w4, torch, dev, steps, stream):
 def time_tp8_rank(w4, torch, dev, steps, stream):
     """One 8-way tensor-parallel rank's share of the Llama-2-70B block (the kernel at the
     local shapes a sharded layer runs), M = 16, 32, 128: back-to-back calls between one event
-    pair (these kernels run for a few us, which a pair of events per call would inflate);
-    enough weight copies rotate that each call's weights come from HBM."""
+    pair, queued behind a spin so the host's launch rate does not set the time (these kernels
+    run for a few us); enough weight copies rotate that each call's weights come from HBM."""
     from workloads import LLAMA2_70B_TP8, draw_shape
     rows = []
     for sh in LLAMA2_70B_TP8.shapes:
@@ -387,23 +446,18 @@ def time_tp8_rank(w4, torch, dev, steps, stream):
         for M in sh.Ms:
             out = torch.empty((M, sh.N), dtype=torch.float16, device=dev)
             ws = w4.new_workspace(M, sh.K, sh.N, dev)
-            for i in range(5):
+            Am = Ad[:M]
+
+            def calls(i, Am=Am, out=out, ws=ws):
                 p_, s_ = cps[i % len(cps)]
-                w4.gemm(Ad[:M], p_, s_, sh.N, out=out, ws=ws, stream=stream)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(steps):
-                p_, s_ = cps[i % len(cps)]
-                w4.gemm(Ad[:M], p_, s_, sh.N, out=out, ws=ws, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / steps
+                w4.gemm(Am, p_, s_, sh.N, out=out, ws=ws, stream=stream)
+            calls.n = steps
+            us, queued = queued_batch(torch, stream, calls)
             D = algorithmic_bytes(M, sh.K, sh.N)
             rows.append({"shape": sh.name, "M": M, "K": sh.K, "N": sh.N, "us": round(us, 2),
                          "GBps": round(D / us / 1e3, 1),
                          "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4),
-                         "weight_copies_rotated": ncp})
+                         "weight_copies_rotated": ncp, "queued_ahead_of_gpu": queued})
             log(f"tp8 {sh.name:16s} M={M:4d} {us:7.1f} us  {D / us / 1e3:6.0f} GB/s")
         del cps, pd, sd
         torch.cuda.empty_cache()

@@ -88,6 +88,8 @@ struct Params {
     int P;                    // M sub-problems of Mt rows
     int S;                    // column slices of Nt columns
     int gens;                 // workgroups resident per CU (1..3), for wave priorities
+    int KS;                   // whole-K kernel: workgroups sharing one slab group's K range
+    int Kq, Kr;               // ... and G = KS * Kq + Kr: split k gets Kq (+1 if k < Kr) tiles
     int W;                    // workgroups = stripes
     long long T;              // total tiles = (N / Nt) * P * G
 };
@@ -1204,6 +1206,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // step) straight into the MFMA operand registers, rows at or past M falling outside the buffer
 // (zero, no memory access).  No per-tile barrier.
 //
+// Split K (p.KS > 1), for weights with too few slab groups to give every CU work: the grid's
+// second dimension is the split, and the KS workgroups (x, 0 .. KS - 1) share slab group x,
+// each taking a contiguous 1/KS of the K tiles.  Each
+// stores its fp32 sums as one piece (device-scope stores, a 1 KiB slot per slab), counts in on
+// the group's counter, and the last to arrive sums the KS pieces in split order -- a fixed
+// order, so results repeat bit for bit -- scales, writes C and resets the counter, the
+// protocol of the stripe kernel's split slices (see settle()).  Nobody waits for another
+// workgroup.
+//
 // Parameters: with N a multiple of 256 the parameter stream groups four slabs, so per K step a
 // column holds 4 scales (and 4 zero terms) of a group in 8 (16) contiguous bytes.  A
 // workgroup's NS slabs start at j0 and touch at most (NS + 6) / 4 groups; one load per group
@@ -1213,6 +1224,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // The tiles after a wave's run are still "loaded" (every iteration issues the same loads),
 // from an offset outside every buffer (kOutside): no memory traffic, and the compiler never meets a join
 // where it would have to wait for everything.
+
+constexpr int kSkinnyMaxKS = 8;            // split-K pieces summed in one load round
 
 template <int NS>
 struct SkinnyGroups {
@@ -1245,10 +1258,15 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
     const int c = lane & 15;
     const int S = p.N >> 4;                              // slabs
     const int U = S >> 2;                                // parameter groups
-    const int j0 = blockIdx.x * NS;                      // the workgroup's first slab
+    const int KS = p.KS;
+    const int jg = blockIdx.x;                           // slab group
+    const int ks = blockIdx.y;                           // its K split
+    const int j0 = jg * NS;                              // the workgroup's first slab
     const int u0 = j0 >> 2, r = j0 & 3;
-    const int g0 = p.G * wave / kWaves;                  // this wave's run of K tiles
-    const int g1 = p.G * (wave + 1) / kWaves;
+    const int gk0 = ks * p.Kq + (ks < p.Kr ? ks : p.Kr);            // the split's K tiles
+    const int gk1 = gk0 + p.Kq + (ks < p.Kr ? 1 : 0);
+    const int g0 = gk0 + (gk1 - gk0) * wave / kWaves;    // this wave's run of them
+    const int g1 = gk0 + (gk1 - gk0) * (wave + 1) / kWaves;
 
     const __amdgpu_buffer_rsrc_t rA =
         make_rsrc(p.A, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.K) * 2u);
@@ -1455,6 +1473,34 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
     __syncthreads();
     const uint32_t v_c = (static_cast<uint32_t>(4 * (lane >> 4)) * p.N + c) * 2;
     const uint32_t rowN = opaque(static_cast<uint32_t>(p.N) * 2);
+    auto write_slab = [&](int i, f4 v) __attribute__((always_inline)) {
+        if constexpr (F::COL)
+            v *= half_bits_to_float(col_param(j0 + i, 0));
+        uint32_t srow = static_cast<uint32_t>(j0 + i) * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(v[q]), rC, v_c, srow, 0);
+            srow += rowN;
+        }
+    };
+    if (KS == 1) {
+#pragma unroll
+        for (int i0 = 0; i0 < NS; i0 += kWaves) {
+            const int i = i0 + wave;
+            if (i < NS && j0 + i < S) {
+                f4 v = red[(0 * NS + i) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w)
+                    v += red[(w * NS + i) * 64 + lane];
+                write_slab(i, v);
+            }
+        }
+        return;
+    }
+
+    // Split K: the piece of slab j0 + i from split k goes to slot (jg * KS + k) * NS + i.
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(p.partials, static_cast<uint32_t>(gridDim.x) * KS * NS * 1024u);
 #pragma unroll
     for (int i0 = 0; i0 < NS; i0 += kWaves) {
         const int i = i0 + wave;
@@ -1463,16 +1509,43 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
 #pragma unroll
             for (int w = 1; w < kWaves; ++w)
                 v += red[(w * NS + i) * 64 + lane];
-            if constexpr (F::COL)
-                v *= half_bits_to_float(col_param(j0 + i, 0));
-            uint32_t srow = static_cast<uint32_t>(j0 + i) * 32;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(v[q]), rC, v_c, srow, 0);
-                srow += rowN;
-            }
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u4, v), rP, lane * 16,
+                ((static_cast<uint32_t>(jg) * KS + ks) * NS + i) * 1024u, kDeviceScope);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's pieces are stored
+    __shared__ int arrived;
+    __syncthreads();
+    if (tid == 0)
+        arrived = __hip_atomic_fetch_add(p.counters + jg, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != KS - 1)
+        return;
+    // the last to arrive: every piece is stored; sum them in split order
+#pragma unroll
+    for (int i0 = 0; i0 < NS; i0 += kWaves) {
+        const int i = i0 + wave;
+        if (i < NS && j0 + i < S) {
+            f4 x[kSkinnyMaxKS];
+#pragma unroll
+            for (int k = 0; k < kSkinnyMaxKS; ++k) {
+                const uint32_t off = k < KS ? ((static_cast<uint32_t>(jg) * KS + k) * NS + i) * 1024u
+                                            : kOutside;
+                x[k] = __builtin_bit_cast(
+                    f4, __builtin_amdgcn_raw_buffer_load_b128(rP, lane * 16, off, kDeviceScope));
+            }
+            f4 v = x[0];
+#pragma unroll
+            for (int k = 1; k < kSkinnyMaxKS; ++k)
+                if (k < KS)
+                    v += x[k];
+            write_slab(i, v);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(p.counters + jg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ 2:4-sparse weights
@@ -1690,6 +1763,7 @@ struct Config {
     int P, S, G, W;
     long long T;
     int NS;          // > 0: the skinny kernel, NS slabs per workgroup (W workgroups)
+    int KS;          // the skinny kernel's K splits per slab group (1: none)
 };
 
 constexpr int kSkinnyMaxNS = 10;
@@ -1701,9 +1775,9 @@ constexpr int kSkinnyMaxNS = 10;
 // 72k x 18k 110.5 vs 113.2 us at M = 1; at M = 16 the extra A re-reads make it slower (128.9
 // vs 124.4 us).  With one slab per workgroup four of a wave's six loads per tile are A fragments;
 // there the stripe kernel measures faster once K runs long (28672 x 8192: 31 vs 33 us at
-// M = 1), while on every shorter or wider weight measured the skinny kernel is faster
-// (1.1x to 4x).  Its dead loads point 2 GiB past the buffer starts, so the weights and A
-// must lie below that.
+// M = 1) unless K is split (choose_config), while on every shorter or wider weight measured
+// the skinny kernel is faster (1.1x to 4x).  Its dead loads point 2 GiB past the buffer
+// starts, so the weights and A must lie below that.
 int skinny_slabs(int M, int K, int N, int cus)
 {
     if (M > 16 || N % 256)
@@ -1715,11 +1789,33 @@ int skinny_slabs(int M, int K, int N, int cus)
         if (ns3 >= 2 && ns3 <= 7)
             ns = ns3;
     }
-    if (ns > kSkinnyMaxNS || (ns == 1 && K / kGroup > 128) ||
+    if (ns > kSkinnyMaxNS ||
         static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
         static_cast<uint64_t>(16) * static_cast<uint64_t>(K) * 2 >= kOutside)
         return 0;
     return static_cast<int>(ns);
+}
+
+// K splits for the skinny kernel.  On weights with few slab groups (wn well below the CU
+// count) the kernel's time is a fixed ~2.5 us plus the K tiles each wave walks one after the
+// other, ~0.31 us a tile at M <= 8 and ~0.48 us at M = 16 (fitted to timings of K 4096..14336,
+// N 1280..3072); a split divides the walk by KS and adds ~2.1 us for its store, count and
+// reload.  Splits are taken only while the grid stays within one workgroup per CU (past that,
+// timings got worse: 8192 x 2560 at M = 16, 10.4 -> 12.7 us with two), as many as fit, at most
+// kSkinnyMaxKS (summed in one load round) and never below two tiles per wave, and only where
+// the model's saving exceeds 2.4 us.  Measured: 8192 x 1280 at M = 16, 10.2 -> 7.3 us with
+// three splits; 14336 x 2048, 16.5 -> 11.5 us with two.  The counters bound the slab groups.
+int skinny_splits(int wn, int G, int M, int cus)
+{
+    if (wn > kMaxWGs)
+        return 1;
+    const int ks = std::min({kSkinnyMaxKS, cus / wn, G / (2 * kWaves)});
+    if (ks < 2)
+        return 1;
+    const double tile_us = M <= 8 ? 0.31 : 0.48;
+    const double walk = static_cast<double>(G) / kWaves;
+    const double saved = walk * (1.0 - 1.0 / ks) * tile_us;
+    return saved > 2.4 ? ks : 1;
 }
 
 int check_gemm_shape(int M, int K, int N)
@@ -1814,8 +1910,15 @@ Config choose_config(int M, int K, int N, int cus)
     c.T = static_cast<long long>(c.S) * c.P * c.G;
     c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, false), cus);
     c.NS = skinny_slabs(M, K, N, cus);
-    if (c.NS > 0)
-        c.W = (N / 16 + c.NS - 1) / c.NS;
+    c.KS = 1;
+    if (c.NS > 0) {
+        const int wn = (N / 16 + c.NS - 1) / c.NS;
+        c.KS = skinny_splits(wn, c.G, M, cus);
+        if (c.NS == 1 && c.KS == 1 && c.G > 128)
+            c.NS = 0;                  // one slab a workgroup over a long K: the stripe kernel
+        else
+            c.W = wn * c.KS;
+    }
     return c;
 }
 
@@ -1833,13 +1936,14 @@ Config choose_config_24(int M, int K, int N, int cus)
     c.T = static_cast<long long>(c.S) * c.P * c.G;
     c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, true), cus);
     c.NS = 0;
+    c.KS = 1;
     return c;
 }
 
 size_t workspace_for(const Config &c)
 {
-    if (c.NS > 0)
-        return kCounterBytes;          // the skinny kernel shares nothing between workgroups
+    if (c.NS > 0)                      // the skinny kernel: one 1 KiB piece per slab when split
+        return kCounterBytes + (c.KS > 1 ? static_cast<size_t>(c.W) * c.NS * 1024 : 0);
     const size_t slot = static_cast<size_t>(16 * c.MB) * (16 * c.waves * c.NBW) * sizeof(float);
     return kCounterBytes + 2 * static_cast<size_t>(c.W) * slot;
 }
@@ -1877,8 +1981,8 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
 template <int NS, class F>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<NS, F>), dim3(p.W), dim3(kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<NS, F>), dim3(p.W / p.KS, p.KS), dim3(kThreads),
+                       0, stream, p);
     return hipGetLastError();
 }
 
@@ -1999,7 +2103,7 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     const Config c = choose_config(M, K, N, d.cus);
     // K = 128 makes the two scale granularities the same thing; take the grouped path
     const bool col = group != kGroup;
-    Params p;
+    Params p{};
     p.A = static_cast<const uint16_t *>(A);
     p.packed = reinterpret_cast<const u4 *>(packed);
     p.scales = params;
@@ -2016,6 +2120,9 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     p.W = c.W;
     p.T = c.T;
     p.gens = std::min(3, (c.W + d.cus - 1) / d.cus);
+    p.KS = c.KS;
+    p.Kq = c.G / c.KS;
+    p.Kr = c.G % c.KS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (zero_points)

@@ -466,6 +466,52 @@ def test_whole_k_workgroups_one_hot_rows_are_bit_exact(fmt):
         assert same(C[m], w.astype(np.float16)), (fmt, m, k)
 
 
+# Whole-K workgroups with K split between several workgroups (few slab groups over a long K):
+# 8192 x 1280 (80 slab groups, three splits), 14336 x 2048 (128 groups, two), 28672 x 1024
+# (64 groups, four: one slab per workgroup over a long K), 6144 x 256 (16 groups, six).  The
+# last workgroup to finish a slab group sums the pieces: two calls on one workspace check
+# that the counters come back to zero and that results repeat bit for bit.
+SPLIT_K_SHAPES = [(8192, 1280), (14336, 2048), (28672, 1024), (6144, 256)]
+
+
+@pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
+@pytest.mark.parametrize("K,N", SPLIT_K_SHAPES)
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_whole_k_split_k_against_oracle(M, K, N, fmt):
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=M + K + N + 1)
+        W, g, z = FmtWeights(q, s, 128), 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=M + K + N + 1)
+        W = FmtWeights(q, s, g, z)
+    ws = w4.workspace(M, K, N, torch.device("cuda"))
+    C = W.run(A, ws=ws)
+    check(C, oracle.gemm(A, q, s, group=g, zeros=z), f"split-K {fmt} M={M} K={K} N={N}")
+    assert np.array_equal(bits(W.run(A, ws=ws)), bits(C))
+    assert int(ws[:4096].count_nonzero()) == 0        # the counters are back at zero
+
+
+@pytest.mark.parametrize("fmt", ["group128", "column_zeros"])
+def test_whole_k_split_k_one_hot_rows_are_bit_exact(fmt):
+    # the other splits' pieces of a one-hot row are zeros: the sum is the one product
+    K, N, M = 14336, 2048, 16
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=91)
+        g, z = 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=91)
+    A[:] = 0
+    ks = [0, 127, 128, 3583, 3584, 7167, 7168, 7200, 10751, 10752, 14335, 5000, 9000, 12000,
+          1, 14000]
+    for m, k in enumerate(ks):
+        A[m, k] = 1.0
+    C = FmtWeights(q, s, g, z).run(A)
+    for m, k in enumerate(ks):
+        zz = 8 if z is None else z[k // g].astype(np.float64)
+        w = s[k // g].astype(np.float64) * (q[k].astype(np.float64) - zz)
+        assert same(C[m], w.astype(np.float16)), (fmt, m, k)
+
+
 # Seeded random shapes across every kernel choice (whole-K at M <= 16 with two or three
 # workgroups per CU, 16/32/64-row stripes, 128-row tiles, several row sub-problems), the
 # stripe-count model's range of split pieces and N from one to many slices, for all four
