@@ -1531,10 +1531,12 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
             f4 x[kSkinnyMaxKS];
 #pragma unroll
             for (int k = 0; k < kSkinnyMaxKS; ++k) {
-                const uint32_t off = k < KS ? ((static_cast<uint32_t>(jg) * KS + k) * NS + i) * 1024u
-                                            : kOutside;
+                // splits past KS: a lane offset outside the buffer (reads zero, no access)
+                const uint32_t vo =
+                    k < KS ? ((static_cast<uint32_t>(jg) * KS + k) * NS + i) * 1024u + lane * 16
+                           : kOutside;
                 x[k] = __builtin_bit_cast(
-                    f4, __builtin_amdgcn_raw_buffer_load_b128(rP, lane * 16, off, kDeviceScope));
+                    f4, __builtin_amdgcn_raw_buffer_load_b128(rP, vo, 0, kDeviceScope));
             }
             f4 v = x[0];
 #pragma unroll
