@@ -1769,8 +1769,14 @@ struct Config {
 };
 
 constexpr int kSkinnyMaxNS = 10;
+constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this many slabs
 
-// Skinny kernel (M <= 16, N a multiple of 256): NS = the fewest slabs per workgroup that keep
+// Skinny kernel (M <= 16, N a multiple of 256).  Weights of up to 7 slabs per CU (N up to
+// 28672 on 256 CUs) take the fewest slabs that leave at most one workgroup per CU: measured
+// on K 4096..8192, N 7168..28672 this beats two or three per CU by 1.1-1.5x (8192 x 10240 at
+// M = 16: 13.6 us with 3 slabs, 20.7 with 2; 8192 x 28672: 23.8 us with 7, 29.5 with 4); a
+// CU running two workgroups of a short weight takes twice as long, it does not overlap them.
+// Larger weights: NS = the fewest slabs per workgroup that keep
 // the workgroups within two per CU, so every workgroup streams as many bytes as possible at
 // once.  At M <= 8 (A mostly rows past M, read as zero without memory traffic) three per CU
 // measure faster where that leaves 2 to 7 slabs (7 still fits three workgroups' registers):
@@ -1786,7 +1792,10 @@ int skinny_slabs(int M, int K, int N, int cus)
         return 0;
     const long long S = N / 16;
     long long ns = (S + 2LL * cus - 1) / (2LL * cus);
-    if (M <= 8) {
+    const long long ns1 = (S + cus - 1) / cus;
+    if (ns1 <= kSkinnyOneMaxNS) {
+        ns = ns1;
+    } else if (M <= 8) {
         const long long ns3 = (S + 3LL * cus - 1) / (3LL * cus);
         if (ns3 >= 2 && ns3 <= 7)
             ns = ns3;
@@ -1798,26 +1807,44 @@ int skinny_slabs(int M, int K, int N, int cus)
     return static_cast<int>(ns);
 }
 
-// K splits for the skinny kernel.  On weights with few slab groups (wn well below the CU
-// count) the kernel's time is a fixed ~2.5 us plus the K tiles each wave walks one after the
-// other, ~0.31 us a tile at M <= 8 and ~0.48 us at M = 16 (fitted to timings of K 4096..14336,
-// N 1280..3072); a split divides the walk by KS and adds ~2.1 us for its store, count and
-// reload.  Splits are taken only while the grid stays within one workgroup per CU (past that,
-// timings got worse: 8192 x 2560 at M = 16, 10.4 -> 12.7 us with two), as many as fit, at most
-// kSkinnyMaxKS (summed in one load round) and never below two tiles per wave, and only where
-// the model's saving exceeds 2.4 us.  Measured: 8192 x 1280 at M = 16, 10.2 -> 7.3 us with
-// three splits; 14336 x 2048, 16.5 -> 11.5 us with two.  The counters bound the slab groups.
-int skinny_splits(int wn, int G, int M, int cus)
+// Slabs and K splits for the skinny kernel once it runs at most one workgroup per CU.  There
+// its time follows the K tiles each wave walks one after the other: about 2.5 us, plus per tile
+// a + b * NS (a = 0.27, b = 0.075 us at M <= 8; a = 0.45, b = 0.06 at M = 16), plus ~2.1 us for
+// the split's store, count and reload when K is split (fitted to timings of K 6144..28672,
+// N 256..7168, NS 1..4, KS 1..8 on MI355X; past four slabs the model is too optimistic).  The
+// search keeps at most one workgroup per CU, up to 4 slabs and kSkinnyMaxKS splits (summed in
+// one load round), never below two tiles per wave, and leaves the one-per-CU choice only for a
+// predicted gain of 15%.  Measured: 8192 x 1280 at M = 16 10.3 -> 6.5-6.8 us, 11008 x 4096
+// 13.4 -> 9.6 us, 14336 x 2048 16.5 -> 8.4 us, 28672 x 1024 22 -> 10 us.  The counters bound
+// the slab groups.
+double skinny_model_us(int G, int NS, int KS, int M)
 {
-    if (wn > kMaxWGs)
-        return 1;
-    const int ks = std::min({kSkinnyMaxKS, cus / wn, G / (2 * kWaves)});
-    if (ks < 2)
-        return 1;
-    const double tile_us = M <= 8 ? 0.31 : 0.48;
-    const double walk = static_cast<double>(G) / kWaves;
-    const double saved = walk * (1.0 - 1.0 / ks) * tile_us;
-    return saved > 2.4 ? ks : 1;
+    const double a = M <= 8 ? 0.27 : 0.45, b = M <= 8 ? 0.075 : 0.06;
+    return 2.5 + static_cast<double>(G) / (kWaves * KS) * (a + b * NS) + (KS > 1 ? 2.1 : 0.0);
+}
+
+void skinny_split(int S, int G, int M, int cus, int &ns, int &ks)
+{
+    ks = 1;
+    if ((S + ns - 1) / ns > cus)
+        return;                                   // more than one workgroup per CU
+    const double base = skinny_model_us(G, ns, 1, M);
+    double best = 0.85 * base;
+    const int ns0 = ns;
+    for (int n = ns0; n <= 4; n = n < 2 ? 2 : n + 2) {
+        const int wn = (S + n - 1) / n;
+        if (wn > kMaxWGs)
+            continue;
+        const int kmax = std::min({kSkinnyMaxKS, cus / wn, G / (2 * kWaves)});
+        for (int k = 2; k <= kmax; ++k) {
+            const double t = skinny_model_us(G, n, k, M);
+            if (t < best) {
+                best = t;
+                ns = n;
+                ks = k;
+            }
+        }
+    }
 }
 
 int check_gemm_shape(int M, int K, int N)
@@ -1914,8 +1941,8 @@ Config choose_config(int M, int K, int N, int cus)
     c.NS = skinny_slabs(M, K, N, cus);
     c.KS = 1;
     if (c.NS > 0) {
+        skinny_split(N / 16, c.G, M, cus, c.NS, c.KS);
         const int wn = (N / 16 + c.NS - 1) / c.NS;
-        c.KS = skinny_splits(wn, c.G, M, cus);
         if (c.NS == 1 && c.KS == 1 && c.G > 128)
             c.NS = 0;                  // one slab a workgroup over a long K: the stripe kernel
         else

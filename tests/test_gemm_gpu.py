@@ -424,11 +424,14 @@ def test_no_write_past_the_rows_of_c(M, K, N, fmt):
 
 # ------------------------------------------------------------------ M <= 16: whole-K workgroups
 
-# N chosen for 2, 3, 4 and 9 slabs per workgroup (16640: 1040 slabs in 347 workgroups of
-# three, the last holding two; first slabs at every offset mod 4), K = 128..384 so that some
-# waves of a workgroup get no K tile at all.
+# N chosen for 2 to 9 slabs per workgroup: one workgroup per CU up to 7 slabs (8192 -> 2,
+# 9216 -> 3, 12544 -> 4, 16640 -> 5, 26880 -> 7 on 256 CUs), 73728 -> 6 or 9 with two or three
+# per CU; 8960 (560 slabs in workgroups of three), 17152 (1072 in fives) and 27904 (1744 in
+# sevens) leave a last workgroup short, and odd slab counts put first slabs at every offset
+# mod 4.  K = 128..384 so that some waves of a workgroup get no K tile at all.
 SKINNY_SHAPES = [(128, 9216), (256, 16640), (384, 26880), (1024, 16640), (4096, 8448),
-                 (2048, 73728), (640, 12544)]
+                 (2048, 73728), (640, 12544), (1024, 8192), (4096, 8960), (256, 17152),
+                 (384, 27904)]
 
 
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
