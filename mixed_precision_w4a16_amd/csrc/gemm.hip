@@ -54,9 +54,9 @@
 //   co-residency assumption is needed.
 // * M > 64 runs a second kernel with 128-row tiles (w4a16_gemm_wide_kernel, further down):
 //   every weight tile meets a whole 128-row block of A, A is brought into LDS by DMA.
-// * M <= 16 runs a third kernel (w4a16_gemm_skinny_kernel, further down) on most shapes: a
-//   workgroup owns a few 16-column slabs over all of K and its four waves split K, so no
-//   output is shared between workgroups and the reduction above is not needed.
+// * M <= 16 runs a third kernel (w4a16_gemm_skinny_kernel, further down) on most shapes, and
+//   M = 17..32 on weights of up to 7 slabs per CU: a workgroup owns a few 16-column slabs over
+//   all of K (or over one of a few K splits) and its four waves split that range.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -1194,7 +1194,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
 // ------------------------------------------------------------------------- skinny kernel
 //
-// `w4a16_gemm_skinny_kernel<NS, F>`, M <= 16, N a multiple of 256.  The weight stream bounds
+// `w4a16_gemm_skinny_kernel<MB, NS, F>`, MB 16-row blocks (M <= 16, or M = 17..32 on weights
+// of up to seven slabs per CU, where one workgroup per CU leaves registers to spare), N a
+// multiple of 256.  Each decoded weight fragment feeds MB matrix instructions.  The weight stream bounds
 // the product, and the stripe scheme's split slices cost a store, a counter and a read at the
 // very end, when every stripe finishes at once (on small weights that chain is most of the
 // time).  Here a workgroup owns NS consecutive 16-column slabs over the whole K range, so no
@@ -1236,15 +1238,15 @@ struct SkinnyGroups {
     static constexpr int depth = 2;
 };
 
-template <int NS, class F>
+template <int MB, int NS, class F>
 struct SkinnyBuf {
     u4 w[NS];                                // weight quads, one per slab
-    h8 a[4];                                 // A fragments of the 4 32-k steps
+    h8 a[MB][4];                             // A fragments of the 4 32-k steps per row block
     uint32_t p[F::COL ? 1 : SkinnyGroups<NS>::n][F::ZP ? 4 : 2];   // per-group parameters
 };
 
-template <int NS, class F>
-__global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p)
+template <int MB, int NS, class F>
+__global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_kernel(Params p)
 {
     using SG = SkinnyGroups<NS>;
     constexpr int NG = SG::n, NH = SG::nh;
@@ -1284,23 +1286,29 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
         return (static_cast<uint32_t>(u) * p.Gs + gs) * (16u * PB);
     };
     const uint32_t v_par = static_cast<uint32_t>(c) * PB;
-    // A operand: row c, k = 8 * (lane / 16) of each 32-k step
-    const uint32_t v_a = (static_cast<uint32_t>(c) * p.K + 8 * (lane >> 4)) * 2;
+    // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step
+    uint32_t v_a[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        v_a[mb] = (static_cast<uint32_t>(16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
     auto slab = [&](int i) __attribute__((always_inline)) {
         const int j = j0 + i;
         return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
     };
 
-    auto load = [&](SkinnyBuf<NS, F> &b, int g) __attribute__((always_inline)) {
+    auto load = [&](SkinnyBuf<MB, NS, F> &b, int g) __attribute__((always_inline)) {
         const bool live = g < g1;
         const uint32_t vw = live ? static_cast<uint32_t>(lane) * 16 : kOutside;
-        const uint32_t va = live ? v_a : kOutside;
         const uint32_t vp = live ? v_par : kOutside;
         const int gg = live ? g : g1 - 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            b.a[t] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rA, va, static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                b.a[mb][t] = __builtin_bit_cast(
+                    h8, __builtin_amdgcn_raw_buffer_load_b128(
+                            rA, live ? v_a[mb] : kOutside,
+                            static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
 #pragma unroll
         for (int i = 0; i < NS; ++i)
             b.w[i] = __builtin_bit_cast(
@@ -1360,12 +1368,14 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
             zcol[i] = col_param(slab(i), 1);
     }
 
-    f4 acc[NS];
+    f4 acc[MB][NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
-        acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const SkinnyBuf<NS, F> &b) __attribute__((always_inline)) {
+    auto compute = [&](const SkinnyBuf<MB, NS, F> &b) __attribute__((always_inline)) {
         float sf[NS];
         h2 zsub[NS], zadd[NS];
         uint32_t sh[NH], zh[NH];
@@ -1402,29 +1412,37 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int i = 0; i < NS; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        b.a[t], dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]), acc[i],
-                        0, 0, 0);
+                for (int i = 0; i < NS; ++i) {
+                    const h8 x = dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.a[mb][t], x,
+                                                                            acc[mb][i], 0, 0, 0);
+                }
         } else {
             // per group: the exact sum of A * (q - z) over the group, then one scale per output
-            f4 part[NS];
+            f4 part[MB][NS];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int i = 0; i < NS; ++i) {
-                    const f4 cin = t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : part[i];
-                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        b.a[t], dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]), cin, 0,
-                        0, 0);
+                    const h8 x = dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const f4 cin = t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : part[mb][i];
+                        part[mb][i] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(b.a[mb][t], x, cin, 0, 0, 0);
+                    }
                 }
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[i][q] = __builtin_fmaf(sf[i], part[i][q], acc[i][q]);
-                asm volatile("" : "+v"(acc[i]));
-            }
+                for (int i = 0; i < NS; ++i) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[mb][i][q] = __builtin_fmaf(sf[i], part[mb][i][q], acc[mb][i][q]);
+                    asm volatile("" : "+v"(acc[mb][i]));
+                }
         }
     };
 
@@ -1437,7 +1455,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
         // so each buffer's loads are issued right after the compute that frees it and are not
         // sunk toward their use.
         constexpr int D = SkinnyGroups<NS>::depth;
-        SkinnyBuf<NS, F> b[D];
+        SkinnyBuf<MB, NS, F> b[D];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             load(b[d], g0 + d);
@@ -1466,24 +1484,35 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // The four waves' partial sums meet in LDS; wave w then finishes slabs w, w + 4, ...
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-        red[(wave * NS + i) * 64 + lane] = acc[i];
-    __syncthreads();
+    // The four waves' partial sums meet in LDS, one row block at a time; wave w then
+    // finishes slabs w, w + 4, ...
     const uint32_t v_c = (static_cast<uint32_t>(4 * (lane >> 4)) * p.N + c) * 2;
     const uint32_t rowN = opaque(static_cast<uint32_t>(p.N) * 2);
-    auto write_slab = [&](int i, f4 v) __attribute__((always_inline)) {
+    auto write_slab = [&](int mb, int i, f4 v) __attribute__((always_inline)) {
         if constexpr (F::COL)
             v *= half_bits_to_float(col_param(j0 + i, 0));
-        uint32_t srow = static_cast<uint32_t>(j0 + i) * 32;
+        uint32_t srow = static_cast<uint32_t>(j0 + i) * 32 + static_cast<uint32_t>(16 * mb) * rowN;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(v[q]), rC, v_c, srow, 0);
             srow += rowN;
         }
     };
-    if (KS == 1) {
+    // Split K: the piece of row block mb of slab j0 + i from split k goes to slot
+    // ((jg * KS + k) * NS + i) * MB + mb.
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(p.partials, static_cast<uint32_t>(gridDim.x) * KS * NS * MB * 1024u);
+    auto slot = [&](int k, int i, int mb) __attribute__((always_inline)) {
+        return (((static_cast<uint32_t>(jg) * KS + k) * NS + i) * MB + mb) * 1024u;
+    };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (mb > 0)
+            __syncthreads();                   // the previous block's sums have been read
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            red[(wave * NS + i) * 64 + lane] = acc[mb][i];
+        __syncthreads();
 #pragma unroll
         for (int i0 = 0; i0 < NS; i0 += kWaves) {
             const int i = i0 + wave;
@@ -1492,28 +1521,18 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
 #pragma unroll
                 for (int w = 1; w < kWaves; ++w)
                     v += red[(w * NS + i) * 64 + lane];
-                write_slab(i, v);
+                if (KS == 1)
+                    write_slab(mb, i, v);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), rP,
+                                                           lane * 16, slot(ks, i, mb),
+                                                           kDeviceScope);
             }
         }
+    }
+    if (KS == 1)
         return;
-    }
 
-    // Split K: the piece of slab j0 + i from split k goes to slot (jg * KS + k) * NS + i.
-    const __amdgpu_buffer_rsrc_t rP =
-        make_rsrc(p.partials, static_cast<uint32_t>(gridDim.x) * KS * NS * 1024u);
-#pragma unroll
-    for (int i0 = 0; i0 < NS; i0 += kWaves) {
-        const int i = i0 + wave;
-        if (i < NS && j0 + i < S) {
-            f4 v = red[(0 * NS + i) * 64 + lane];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                v += red[(w * NS + i) * 64 + lane];
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u4, v), rP, lane * 16,
-                ((static_cast<uint32_t>(jg) * KS + ks) * NS + i) * 1024u, kDeviceScope);
-        }
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's pieces are stored
     __shared__ int arrived;
     __syncthreads();
@@ -1525,27 +1544,27 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_skinny_kernel(Params p
         return;
     // the last to arrive: every piece is stored; sum them in split order
 #pragma unroll
-    for (int i0 = 0; i0 < NS; i0 += kWaves) {
-        const int i = i0 + wave;
-        if (i < NS && j0 + i < S) {
-            f4 x[kSkinnyMaxKS];
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int k = 0; k < kSkinnyMaxKS; ++k) {
-                // splits past KS: a lane offset outside the buffer (reads zero, no access)
-                const uint32_t vo =
-                    k < KS ? ((static_cast<uint32_t>(jg) * KS + k) * NS + i) * 1024u + lane * 16
-                           : kOutside;
-                x[k] = __builtin_bit_cast(
-                    f4, __builtin_amdgcn_raw_buffer_load_b128(rP, vo, 0, kDeviceScope));
+        for (int i0 = 0; i0 < NS; i0 += kWaves) {
+            const int i = i0 + wave;
+            if (i < NS && j0 + i < S) {
+                f4 x[kSkinnyMaxKS];
+#pragma unroll
+                for (int k = 0; k < kSkinnyMaxKS; ++k) {
+                    // splits past KS: a lane offset outside the buffer (reads zero, no access)
+                    const uint32_t vo = k < KS ? slot(k, i, mb) + lane * 16 : kOutside;
+                    x[k] = __builtin_bit_cast(
+                        f4, __builtin_amdgcn_raw_buffer_load_b128(rP, vo, 0, kDeviceScope));
+                }
+                f4 v = x[0];
+#pragma unroll
+                for (int k = 1; k < kSkinnyMaxKS; ++k)
+                    if (k < KS)
+                        v += x[k];
+                write_slab(mb, i, v);
             }
-            f4 v = x[0];
-#pragma unroll
-            for (int k = 1; k < kSkinnyMaxKS; ++k)
-                if (k < KS)
-                    v += x[k];
-            write_slab(i, v);
         }
-    }
     if (tid == 0)
         __hip_atomic_store(p.counters + jg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1766,6 +1785,7 @@ struct Config {
     long long T;
     int NS;          // > 0: the skinny kernel, NS slabs per workgroup (W workgroups)
     int KS;          // the skinny kernel's K splits per slab group (1: none)
+    int SMB;         // the skinny kernel's 16-row blocks (1, or 2 for M = 17..32)
 };
 
 constexpr int kSkinnyMaxNS = 10;
@@ -1788,13 +1808,15 @@ constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this man
 // starts, so the weights and A must lie below that.
 int skinny_slabs(int M, int K, int N, int cus)
 {
-    if (M > 16 || N % 256)
+    if (M > 32 || N % 256)
         return 0;
     const long long S = N / 16;
     long long ns = (S + 2LL * cus - 1) / (2LL * cus);
     const long long ns1 = (S + cus - 1) / cus;
     if (ns1 <= kSkinnyOneMaxNS) {
         ns = ns1;
+    } else if (M > 16) {
+        return 0;                      // 32 rows: only at one workgroup per CU
     } else if (M <= 8) {
         const long long ns3 = (S + 3LL * cus - 1) / (3LL * cus);
         if (ns3 >= 2 && ns3 <= 7)
@@ -1802,7 +1824,7 @@ int skinny_slabs(int M, int K, int N, int cus)
     }
     if (ns > kSkinnyMaxNS ||
         static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
-        static_cast<uint64_t>(16) * static_cast<uint64_t>(K) * 2 >= kOutside)
+        static_cast<uint64_t>(32) * static_cast<uint64_t>(K) * 2 >= kOutside)
         return 0;
     return static_cast<int>(ns);
 }
@@ -1810,8 +1832,9 @@ int skinny_slabs(int M, int K, int N, int cus)
 // Slabs and K splits for the skinny kernel once it runs at most one workgroup per CU.  There
 // its time follows the K tiles each wave walks one after the other: about 2.5 us, plus per tile
 // a + b * NS (a = 0.27, b = 0.075 us at M <= 8; a = 0.45, b = 0.06 at M = 16), plus ~2.1 us for
-// the split's store, count and reload when K is split (fitted to timings of K 6144..28672,
-// N 256..7168, NS 1..4, KS 1..8 on MI355X; past four slabs the model is too optimistic).  The
+// the split's store, count and reload when K is split; with two row blocks (M = 17..32)
+// 1.9 us + (0.90 + 0.057 NS) per tile + 3.4 us per split (fitted to timings of K 4096..28672,
+// N 256..10240, NS 1..4, KS 1..8 on MI355X; past four slabs the model is too optimistic).  The
 // search keeps at most one workgroup per CU, up to 4 slabs and kSkinnyMaxKS splits (summed in
 // one load round), never below two tiles per wave, and leaves the one-per-CU choice only for a
 // predicted gain of 15%.  Measured: 8192 x 1280 at M = 16 10.3 -> 6.5-6.8 us, 11008 x 4096
@@ -1819,8 +1842,12 @@ int skinny_slabs(int M, int K, int N, int cus)
 // the slab groups.
 double skinny_model_us(int G, int NS, int KS, int M)
 {
-    const double a = M <= 8 ? 0.27 : 0.45, b = M <= 8 ? 0.075 : 0.06;
-    return 2.5 + static_cast<double>(G) / (kWaves * KS) * (a + b * NS) + (KS > 1 ? 2.1 : 0.0);
+    // fixed time, per-tile time a + b * NS, split cost; fitted per row range
+    const double c0 = M <= 16 ? 2.5 : 1.93;
+    const double a = M <= 8 ? 0.27 : (M <= 16 ? 0.45 : 0.90);
+    const double b = M <= 8 ? 0.075 : (M <= 16 ? 0.06 : 0.057);
+    const double cs = M <= 16 ? 2.1 : 3.44;
+    return c0 + static_cast<double>(G) / (kWaves * KS) * (a + b * NS) + (KS > 1 ? cs : 0.0);
 }
 
 void skinny_split(int S, int G, int M, int cus, int &ns, int &ks)
@@ -1940,11 +1967,15 @@ Config choose_config(int M, int K, int N, int cus)
     c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, false), cus);
     c.NS = skinny_slabs(M, K, N, cus);
     c.KS = 1;
+    c.SMB = M > 16 ? 2 : 1;
     if (c.NS > 0) {
         skinny_split(N / 16, c.G, M, cus, c.NS, c.KS);
         const int wn = (N / 16 + c.NS - 1) / c.NS;
         if (c.NS == 1 && c.KS == 1 && c.G > 128)
             c.NS = 0;                  // one slab a workgroup over a long K: the stripe kernel
+        else if (M > 16 && c.G > 16 * kWaves * c.KS)
+            c.NS = 0;                  // 32 rows over more than 16 tiles a wave: the stripe
+                                       // kernel (28672 x 8192: 37.2 vs 39.1 us)
         else
             c.W = wn * c.KS;
     }
@@ -1971,8 +2002,9 @@ Config choose_config_24(int M, int K, int N, int cus)
 
 size_t workspace_for(const Config &c)
 {
-    if (c.NS > 0)                      // the skinny kernel: one 1 KiB piece per slab when split
-        return kCounterBytes + (c.KS > 1 ? static_cast<size_t>(c.W) * c.NS * 1024 : 0);
+    if (c.NS > 0)       // the skinny kernel: one 1 KiB piece per slab and row block when split
+        return kCounterBytes +
+               (c.KS > 1 ? static_cast<size_t>(c.W) * c.NS * c.SMB * 1024 : 0);
     const size_t slot = static_cast<size_t>(16 * c.MB) * (16 * c.waves * c.NBW) * sizeof(float);
     return kCounterBytes + 2 * static_cast<size_t>(c.W) * slot;
 }
@@ -2007,28 +2039,40 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int NS, class F>
+template <int MB, int NS, class F>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<NS, F>), dim3(p.W / p.KS, p.KS), dim3(kThreads),
-                       0, stream, p);
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F>), dim3(p.W / p.KS, p.KS),
+                       dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <class F>
-hipError_t dispatch_skinny(int ns, const Params &p, hipStream_t s)
+hipError_t dispatch_skinny(int mb, int ns, const Params &p, hipStream_t s)
 {
+    if (mb == 2) {
+        switch (ns) {
+        case 1: return launch_skinny<2, 1, F>(p, s);
+        case 2: return launch_skinny<2, 2, F>(p, s);
+        case 3: return launch_skinny<2, 3, F>(p, s);
+        case 4: return launch_skinny<2, 4, F>(p, s);
+        case 5: return launch_skinny<2, 5, F>(p, s);
+        case 6: return launch_skinny<2, 6, F>(p, s);
+        case 7: return launch_skinny<2, 7, F>(p, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (ns) {
-    case 1: return launch_skinny<1, F>(p, s);
-    case 2: return launch_skinny<2, F>(p, s);
-    case 3: return launch_skinny<3, F>(p, s);
-    case 4: return launch_skinny<4, F>(p, s);
-    case 5: return launch_skinny<5, F>(p, s);
-    case 6: return launch_skinny<6, F>(p, s);
-    case 7: return launch_skinny<7, F>(p, s);
-    case 8: return launch_skinny<8, F>(p, s);
-    case 9: return launch_skinny<9, F>(p, s);
-    case 10: return launch_skinny<10, F>(p, s);
+    case 1: return launch_skinny<1, 1, F>(p, s);
+    case 2: return launch_skinny<1, 2, F>(p, s);
+    case 3: return launch_skinny<1, 3, F>(p, s);
+    case 4: return launch_skinny<1, 4, F>(p, s);
+    case 5: return launch_skinny<1, 5, F>(p, s);
+    case 6: return launch_skinny<1, 6, F>(p, s);
+    case 7: return launch_skinny<1, 7, F>(p, s);
+    case 8: return launch_skinny<1, 8, F>(p, s);
+    case 9: return launch_skinny<1, 9, F>(p, s);
+    case 10: return launch_skinny<1, 10, F>(p, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -2039,7 +2083,7 @@ int dispatch(const Config &c, const Params &p, hipStream_t s)
 {
     hipError_t e;
     if (c.NS > 0) {
-        e = dispatch_skinny<F>(c.NS, p, s);
+        e = dispatch_skinny<F>(c.SMB, c.NS, p, s);
         return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
     }
     switch (c.MB * 10 + c.NBW) {
