@@ -51,8 +51,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
 # 16-column slabs over all of K up to M = 16, 32-row tiles up to 32, 64-row up to 64, then
 # 128-row tiles on this shape), and the roof that bounds it.
 KERNELS = [
-    ("w4a16_gemm_skinny_kernel<6> (whole-K workgroups, 6 slabs, 3 per CU)", (1, 2, 4, 8), "hbm"),
-    ("w4a16_gemm_skinny_kernel<9> (whole-K workgroups, 9 slabs, 2 per CU)", (16,), "hbm"),
+    ("w4a16_gemm_skinny_kernel<1,6> (whole-K workgroups, 6 slabs, 3 per CU)", (1, 2, 4, 8), "hbm"),
+    ("w4a16_gemm_skinny_kernel<1,9> (whole-K workgroups, 9 slabs, 2 per CU)", (16,), "hbm"),
     ("w4a16_gemm_kernel<2,4> (32-row tiles)", (32,), "hbm"),
     ("w4a16_gemm_kernel<4,4> (64-row tiles)", (64,), "hbm"),
     ("w4a16_gemm_wide_kernel<4,2> (128-row tiles)", (128,), "mfma"),
@@ -487,20 +487,28 @@ def stream_read_rate(w4, torch, dev, stream):
             "GBps": round(best, 1), "frac_of_spec": round(best / HBM_PEAK_GBPS, 4)}
 
 
-def device_state(torch, props):
-    """Software and clock state of the run (clocks and power through rocm-smi when present)."""
+def clock_state():
+    """Clocks and power through rocm-smi, queried before this process touches the GPU (the
+    tool runs as a child process) and skipped under a profiler, whose preloaded library would
+    have initialised the GPU in that child before it starts the tool."""
     import subprocess
-    st = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__,
-          "name": props.name, "arch": getattr(props, "gcnArchName", ""),
-          "cus": props.multi_processor_count}
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF")
+                                                             for k in os.environ):
+        return "skipped under a profiler"
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
                             "--showmemuse"], capture_output=True, text=True, timeout=20)
-        st["rocm_smi"] = [ln.strip() for ln in r.stdout.splitlines()
-                          if ":" in ln and ("clk" in ln.lower() or "power" in ln.lower())][:16]
+        return [ln.strip() for ln in r.stdout.splitlines()
+                if ":" in ln and ("clk" in ln.lower() or "power" in ln.lower())][:16]
     except Exception as exc:            # tool missing or not permitted: note it and go on
-        st["rocm_smi"] = f"unavailable ({type(exc).__name__})"
-    return st
+        return f"unavailable ({type(exc).__name__})"
+
+
+def device_state(torch, props, clocks):
+    """Software and clock state of the run."""
+    return {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__,
+            "name": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "cus": props.multi_processor_count, "rocm_smi": clocks}
 
 
 def main():
@@ -528,6 +536,7 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
+    clocks = clock_state()              # before anything touches the GPU
     import torch
     import mixed_precision_w4a16_amd as w4
     from workloads import LARGE, draw
@@ -667,7 +676,7 @@ def main():
         "compute_sweep": compute_sweep,
         "tp8_rank_shapes": tp8,
         "stream_read_reference": stream_ref,
-        "device": device_state(torch, props),
+        "device": device_state(torch, props, clocks),
     }
     if args.cpu_cols > 0:
         nthreads = min(16, os.cpu_count() or 1)
