@@ -297,7 +297,9 @@ int w4a16_moe_align(const int32_t *topk_ids, int T, int topk, int E, int32_t *so
  * for every assignment a listed in sorted_ids, with Bhat_e = s_e (q_e - z_e) as in
  * w4a16_gemm_ex (group 128; z = 8, or per group and column with zero_points = 1).  Each
  * token row is read where it lies in A and each result written to its own row of C: no
- * permuted copy is made.  Experts without rows cost nothing but an early exit.
+ * permuted copy is made.  Experts without rows cost nothing but early exits; with no more
+ * assignments than experts (T*topk <= E) the launch holds only min(E, T*topk) rows of
+ * workgroups and the experts in use take the lowest workgroup ids.
  *
  *   A              [in]  device [T*K] row-major, fp16 or bf16 (act_dtype)
  *   packed         [in]  device uint32 [E][K*N/8]: expert e's w4a16_pack / w4a16_pack_zp
@@ -312,10 +314,11 @@ int w4a16_moe_align(const int32_t *topk_ids, int T, int topk, int E, int32_t *so
  *   zero_points    0 or 1;  act_dtype  W4A16_ACT_F16 or W4A16_ACT_BF16
  * fp32 sums, one rounding of C to nearest-even.  fp16: the dense path's exact decode, so a
  * row equals w4a16_gemm's result for that token and expert bit for bit when w4a16_gemm
- * takes its whole-K kernel (M <= 16).  bf16: codes enter the matrix unit as 128 + q and
+ * takes its whole-K kernel without a K split (M <= 16).  bf16: codes enter the matrix unit as 128 + q and
  * (128 + z) * sum_k A is subtracted per row and group before the scale.
  * Results do not depend on how the rows are grouped.  Limits: K a multiple of 128, N a
- * multiple of 256, and K*N/2, T*K*2, T*topk*N*2 and (K/128)*N*4 below 2^31 bytes.  T == 0
+ * multiple of 256, E at most 1024, and K*N/2, T*K*2, T*topk*N*2 and (K/128)*N*4 below 2^31
+ * bytes.  T == 0
  * is a no-op.  Errors: W4A16_EINVAL (null pointer other than row_scale, negative size,
  * topk or E below 1, zero_points or act_dtype out of range), W4A16_ESHAPE (shape or
  * limit), W4A16_EUNSUPPORTED (not gfx950), W4A16_EHIP (launch failure).

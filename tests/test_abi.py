@@ -366,6 +366,12 @@ def test_moe_routing_entry_rejects_bad_arguments_before_any_device_call():
                                    None) == w4.ESHAPE        # more than 2048 assignments
     assert lib.w4a16_moe_gemm_topk(d, d, d, d, None, d, 4, 2, 8, 1024, 1000, 0, 0,
                                    None) == w4.ESHAPE
+    assert lib.w4a16_moe_gemm_topk(d, d, d, d, None, d, 4, 2, 1025, 1024, 1024, 0, 0,
+                                   None) == w4.ESHAPE        # more than 1024 experts
+    # w4a16_moe_gemm(A, packed, params, sorted_ids, offsets, row_scale, C, T, topk, E, K, N,
+    #                zero_points, act_dtype, stream)
+    assert lib.w4a16_moe_gemm(d, d, d, d, d, None, d, 4, 2, 1025, 1024, 1024, 0, 0,
+                              None) == w4.ESHAPE
     assert w4.MOE_ROUTE_MAX == 2048
 
 

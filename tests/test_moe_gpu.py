@@ -179,6 +179,23 @@ def test_f16_rows_equal_the_dense_product_of_their_token_and_expert():
         assert torch.equal(De.cpu(), C[torch.from_numpy(rows)]), e
 
 
+# The workgroups of the experts in use come first whatever their numbers: a few scattered
+# experts of 64 (the last one among them), and two of 1024 (the most experts the entries take).
+@pytest.mark.parametrize("routed", [False, True])
+@pytest.mark.parametrize("E,ids", [(64, [[63, 5], [17, 63], [5, 40]]),
+                                   (1024, [[1023, 0], [0, 1023], [511, 1023]])])
+def test_scattered_experts_in_use(E, ids, routed):
+    ids = np.array(ids, dtype=np.int32)
+    T, topk = ids.shape
+    d = draw_moe(E, topk, 128, 256, T, seed=E + 1, act="f16")
+    d["topk_ids"] = ids
+    W = Moe(d)
+    C = W.run(d, routed=routed)
+    want, done = ref(d)
+    assert done.all()
+    check(values(C), want, "f16", f"E={E} experts {sorted(set(ids.ravel().tolist()))}")
+
+
 def test_routing_entry_at_its_limit():
     # T * topk = 2048, the most the routing entry takes
     E, topk, K, N, T = 16, 8, 256, 512, 256
