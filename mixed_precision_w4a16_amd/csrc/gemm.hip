@@ -55,7 +55,7 @@
 // * M > 64 runs a second kernel with 128-row tiles (w4a16_gemm_wide_kernel, further down):
 //   every weight tile meets a whole 128-row block of A, A is brought into LDS by DMA.
 // * M <= 16 runs a third kernel (w4a16_gemm_skinny_kernel, further down) on most shapes, and
-//   M = 17..32 on weights of up to 7 slabs per CU: a workgroup owns a few 16-column slabs over
+//   M = 17..64 on weights of up to 7 (4 above 32 rows) slabs per CU: a workgroup owns a few 16-column slabs over
 //   all of K (or over one of a few K splits) and its four waves split that range.
 #include <hip/hip_runtime.h>
 
@@ -1194,9 +1194,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 
 // ------------------------------------------------------------------------- skinny kernel
 //
-// `w4a16_gemm_skinny_kernel<MB, NS, F>`, MB 16-row blocks (M <= 16, or M = 17..32 on weights
-// of up to seven slabs per CU, where one workgroup per CU leaves registers to spare), N a
-// multiple of 256.  Each decoded weight fragment feeds MB matrix instructions.  The weight stream bounds
+// `w4a16_gemm_skinny_kernel<MB, NS, F>`, MB 16-row blocks (M <= 16; M = 17..32 on weights of
+// up to seven slabs per CU and M = 33..64 on weights of up to four, where one workgroup per CU
+// leaves registers to spare), N a multiple of 256.  Each decoded weight fragment feeds MB
+// matrix instructions.  The weight stream bounds
 // the product, and the stripe scheme's split slices cost a store, a counter and a read at the
 // very end, when every stripe finishes at once (on small weights that chain is most of the
 // time).  Here a workgroup owns NS consecutive 16-column slabs over the whole K range, so no
@@ -1808,11 +1809,13 @@ constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this man
 // starts, so the weights and A must lie below that.
 int skinny_slabs(int M, int K, int N, int cus)
 {
-    if (M > 32 || N % 256)
+    if (M > 64 || N % 256)
         return 0;
     const long long S = N / 16;
     long long ns = (S + 2LL * cus - 1) / (2LL * cus);
     const long long ns1 = (S + cus - 1) / cus;
+    if (M > 32 && ns1 > 4)
+        return 0;                      // 64 rows: only up to 4 slabs (registers)
     if (ns1 <= kSkinnyOneMaxNS) {
         ns = ns1;
     } else if (M > 16) {
@@ -1824,7 +1827,7 @@ int skinny_slabs(int M, int K, int N, int cus)
     }
     if (ns > kSkinnyMaxNS ||
         static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
-        static_cast<uint64_t>(32) * static_cast<uint64_t>(K) * 2 >= kOutside)
+        static_cast<uint64_t>(64) * static_cast<uint64_t>(K) * 2 >= kOutside)
         return 0;
     return static_cast<int>(ns);
 }
@@ -1833,7 +1836,8 @@ int skinny_slabs(int M, int K, int N, int cus)
 // its time follows the K tiles each wave walks one after the other: about 2.5 us, plus per tile
 // a + b * NS (a = 0.27, b = 0.075 us at M <= 8; a = 0.45, b = 0.06 at M = 16), plus ~2.1 us for
 // the split's store, count and reload when K is split; with two row blocks (M = 17..32)
-// 1.9 us + (0.90 + 0.057 NS) per tile + 3.4 us per split (fitted to timings of K 4096..28672,
+// 1.9 us + (0.90 + 0.057 NS) per tile + 3.4 us per split, with four (M = 33..64) 4.9 us +
+// (1.60 + 0.079 NS) per tile + 3.4 us per split (fitted to timings of K 1024..28672,
 // N 256..10240, NS 1..4, KS 1..8 on MI355X; past four slabs the model is too optimistic).  The
 // search keeps at most one workgroup per CU, up to 4 slabs and kSkinnyMaxKS splits (summed in
 // one load round), never below two tiles per wave, and leaves the one-per-CU choice only for a
@@ -1843,10 +1847,10 @@ int skinny_slabs(int M, int K, int N, int cus)
 double skinny_model_us(int G, int NS, int KS, int M)
 {
     // fixed time, per-tile time a + b * NS, split cost; fitted per row range
-    const double c0 = M <= 16 ? 2.5 : 1.93;
-    const double a = M <= 8 ? 0.27 : (M <= 16 ? 0.45 : 0.90);
-    const double b = M <= 8 ? 0.075 : (M <= 16 ? 0.06 : 0.057);
-    const double cs = M <= 16 ? 2.1 : 3.44;
+    const double c0 = M <= 16 ? 2.5 : (M <= 32 ? 1.93 : 4.89);
+    const double a = M <= 8 ? 0.27 : (M <= 16 ? 0.45 : (M <= 32 ? 0.90 : 1.60));
+    const double b = M <= 8 ? 0.075 : (M <= 16 ? 0.06 : (M <= 32 ? 0.057 : 0.079));
+    const double cs = M <= 16 ? 2.1 : (M <= 32 ? 3.44 : 3.39);
     return c0 + static_cast<double>(G) / (kWaves * KS) * (a + b * NS) + (KS > 1 ? cs : 0.0);
 }
 
@@ -1967,15 +1971,16 @@ Config choose_config(int M, int K, int N, int cus)
     c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, false), cus);
     c.NS = skinny_slabs(M, K, N, cus);
     c.KS = 1;
-    c.SMB = M > 16 ? 2 : 1;
+    c.SMB = M > 32 ? 4 : (M > 16 ? 2 : 1);
     if (c.NS > 0) {
         skinny_split(N / 16, c.G, M, cus, c.NS, c.KS);
         const int wn = (N / 16 + c.NS - 1) / c.NS;
         if (c.NS == 1 && c.KS == 1 && c.G > 128)
             c.NS = 0;                  // one slab a workgroup over a long K: the stripe kernel
-        else if (M > 16 && c.G > 16 * kWaves * c.KS)
-            c.NS = 0;                  // 32 rows over more than 16 tiles a wave: the stripe
-                                       // kernel (28672 x 8192: 37.2 vs 39.1 us)
+        else if (M > 16 && c.G > (M > 32 ? 8 : 16) * kWaves * c.KS)
+            c.NS = 0;                  // 32 rows over more than 16 tiles a wave, 64 over more
+                                       // than 8: the stripe kernel (28672 x 8192 at M = 32:
+                                       // 37.2 vs 39.1 us; 8192 x 10240 at M = 64: 31.7 vs 36.1)
         else
             c.W = wn * c.KS;
     }
@@ -2050,6 +2055,15 @@ hipError_t launch_skinny(const Params &p, hipStream_t stream)
 template <class F>
 hipError_t dispatch_skinny(int mb, int ns, const Params &p, hipStream_t s)
 {
+    if (mb == 4) {
+        switch (ns) {
+        case 1: return launch_skinny<4, 1, F>(p, s);
+        case 2: return launch_skinny<4, 2, F>(p, s);
+        case 3: return launch_skinny<4, 3, F>(p, s);
+        case 4: return launch_skinny<4, 4, F>(p, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (mb == 2) {
         switch (ns) {
         case 1: return launch_skinny<2, 1, F>(p, s);

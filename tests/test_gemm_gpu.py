@@ -424,7 +424,8 @@ def test_no_write_past_the_rows_of_c(M, K, N, fmt):
 
 # ------------------------------------------------------------------ M <= 16: whole-K workgroups
 
-# M = 20 and 32 run the kernel's two-row-block form (one workgroup per CU only).
+# M = 20 and 32 run the kernel's two-row-block form (one workgroup per CU only), M = 40 and
+# 64 its four-row-block form where N takes at most four slabs per CU.
 # N chosen for 2 to 9 slabs per workgroup: one workgroup per CU up to 7 slabs (8192 -> 2,
 # 9216 -> 3, 12544 -> 4, 16640 -> 5, 26880 -> 7 on 256 CUs), 73728 -> 6 or 9 with two or three
 # per CU; 8960 (560 slabs in workgroups of three), 17152 (1072 in fives) and 27904 (1744 in
@@ -437,7 +438,7 @@ SKINNY_SHAPES = [(128, 9216), (256, 16640), (384, 26880), (1024, 16640), (4096, 
 
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
 @pytest.mark.parametrize("K,N", SKINNY_SHAPES)
-@pytest.mark.parametrize("M", [1, 5, 16, 20, 32])
+@pytest.mark.parametrize("M", [1, 5, 16, 20, 32, 40, 64])
 def test_whole_k_workgroups_against_oracle(M, K, N, fmt):
     if fmt == "group128":
         A, q, s = draw(K, N, M, seed=M + K + N)
@@ -471,7 +472,7 @@ def test_whole_k_workgroups_one_hot_rows_are_bit_exact(fmt):
 
 
 # Whole-K workgroups with K split between several workgroups (few slab groups over a long K;
-# M = 17..32 runs the kernel's two-row-block form):
+# M = 17..32 and 33..64 run the kernel's two- and four-row-block forms):
 # 8192 x 1280 (80 slab groups, three splits), 14336 x 2048 (128 groups, two), 28672 x 1024
 # (64 groups, four: one slab per workgroup over a long K), 6144 x 256 (16 groups, six).  The
 # last workgroup to finish a slab group sums the pieces: two calls on one workspace check
@@ -481,7 +482,7 @@ SPLIT_K_SHAPES = [(8192, 1280), (14336, 2048), (28672, 1024), (6144, 256)]
 
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
 @pytest.mark.parametrize("K,N", SPLIT_K_SHAPES)
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 33, 64])
 def test_whole_k_split_k_against_oracle(M, K, N, fmt):
     if fmt == "group128":
         A, q, s = draw(K, N, M, seed=M + K + N + 1)
