@@ -472,12 +472,12 @@ def test_whole_k_workgroups_one_hot_rows_are_bit_exact(fmt):
 
 
 # Whole-K workgroups with K split between several workgroups (few slab groups over a long K;
-# M = 17..32 and 33..64 run the kernel's two- and four-row-block forms):
-# 8192 x 1280 (80 slab groups, three splits), 14336 x 2048 (128 groups, two), 28672 x 1024
-# (64 groups, four: one slab per workgroup over a long K), 6144 x 256 (16 groups, six).  The
-# last workgroup to finish a slab group sums the pieces: two calls on one workspace check
-# that the counters come back to zero and that results repeat bit for bit.
-SPLIT_K_SHAPES = [(8192, 1280), (14336, 2048), (28672, 1024), (6144, 256)]
+# M = 17..32 and 33..64 run the kernel's two- and four-row-block forms).  The selection takes,
+# as (slabs per workgroup, splits): 8192 x 1280 (2, 6) or (4, 8); 14336 x 2048 (4, 8);
+# 28672 x 1024 (2, 8); 6144 x 256 (1, 6); 11008 x 4096 (4, 4), whose 86 K tiles make splits of
+# 21 and 22.  The last workgroup to finish a slab group sums the pieces: two calls on one
+# workspace check that the counters come back to zero and that results repeat bit for bit.
+SPLIT_K_SHAPES = [(8192, 1280), (14336, 2048), (28672, 1024), (6144, 256), (11008, 4096)]
 
 
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
