@@ -23,6 +23,8 @@ every M, alternated call by call with the dense path; `moe`, the mixture-of-expe
 product on two layer shapes, fp16 and bf16 activations; `compute_sweep`, the compute-bound
 8192 x 28672 weight at M = 256, 512, 1024 with its fraction of the fp16 matrix peak;
 `tp8_rank_shapes`, one 8-way tensor-parallel rank's share of the Llama-2-70B block;
+`layer_shapes`, the Llama-2-7B block's layers at M = 1, 16, 64 and the 70B block's at M = 16,
+32, 128, each with its fraction of the roofline bound;
 `stream_read_reference`, the HBM read rate of a plain streaming read, for context.
 
 Prints one JSON line on stdout.  Single GPU only.
@@ -429,16 +431,17 @@ def time_compute_sweep(w4, torch, dev, steps, stream):
     return rows
 
 
-def time_tp8_rank(w4, torch, dev, steps, stream):
-    """One 8-way tensor-parallel rank's share of the Llama-2-70B block (the kernel at the
-    local shapes a sharded layer runs), M = 16, 32, 128: back-to-back calls between one event
+def time_shapes(w4, torch, dev, steps, stream, workload, tag):
+    """Per-call time of every shape and M of a workload: back-to-back calls between one event
     pair, queued behind a spin so the host's launch rate does not set the time (these kernels
-    run for a few us); enough weight copies rotate that each call's weights come from HBM."""
-    from workloads import LLAMA2_70B_TP8, draw_shape
+    run for a few to a few hundred us); enough weight copies rotate (600 MB or more) that each
+    call's weights come from HBM."""
+    from workloads import draw_shape
     rows = []
-    for sh in LLAMA2_70B_TP8.shapes:
+    for sh in workload.shapes:
         A, q, s = draw_shape(sh, seed=0)
         pd, sd = w4.to_device(*w4.pack(q, s), dev)
+        del q, s
         wbytes = sh.K * sh.N // 2 + sh.K // GROUP * sh.N * 2
         ncp = max(2, -(-600_000_000 // wbytes))
         cps = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(ncp - 1)]
@@ -453,15 +456,34 @@ def time_tp8_rank(w4, torch, dev, steps, stream):
                 w4.gemm(Am, p_, s_, sh.N, out=out, ws=ws, stream=stream)
             calls.n = steps
             us, queued = queued_batch(torch, stream, calls)
-            D = algorithmic_bytes(M, sh.K, sh.N)
+            D, F = algorithmic_bytes(M, sh.K, sh.N), flops(M, sh.K, sh.N)
+            t_bound = max(D / (HBM_PEAK_GBPS * 1e3), F / (MFMA_F16_PEAK_TFLOPS * 1e6))
             rows.append({"shape": sh.name, "M": M, "K": sh.K, "N": sh.N, "us": round(us, 2),
                          "GBps": round(D / us / 1e3, 1),
                          "hbm_frac": round(D / us / 1e3 / HBM_PEAK_GBPS, 4),
+                         "TFLOPs": round(F / us / 1e6, 1),
+                         "roofline_frac": round(t_bound / us, 4),
                          "weight_copies_rotated": ncp, "queued_ahead_of_gpu": queued})
-            log(f"tp8 {sh.name:16s} M={M:4d} {us:7.1f} us  {D / us / 1e3:6.0f} GB/s")
-        del cps, pd, sd
+            log(f"{tag} {sh.name:16s} M={M:4d} {us:7.1f} us  {D / us / 1e3:6.0f} GB/s  "
+                f"roofline {t_bound / us:5.1%}")
+        del cps, pd, sd, Ad
         torch.cuda.empty_cache()
     return rows
+
+
+def time_tp8_rank(w4, torch, dev, steps, stream):
+    """One 8-way tensor-parallel rank's share of the Llama-2-70B block (the kernel at the
+    local shapes a sharded layer runs), M = 16, 32, 128."""
+    from workloads import LLAMA2_70B_TP8
+    return time_shapes(w4, torch, dev, steps, stream, LLAMA2_70B_TP8, "tp8")
+
+
+def time_layers(w4, torch, dev, steps, stream):
+    """The Llama-2-7B block's layers at M = 1, 16, 64 and the Llama-2-70B block's at M = 16,
+    32, 128 (the model-layer configurations of the benchmark's workload list)."""
+    from workloads import LLAMA2_70B, LLAMA2_7B
+    return {wl.name: time_shapes(w4, torch, dev, steps, stream, wl, "layer")
+            for wl in (LLAMA2_7B, LLAMA2_70B)}
 
 
 def stream_read_rate(w4, torch, dev, stream):
@@ -526,8 +548,8 @@ def main():
     ap.add_argument("--moe-steps", type=int, default=20,
                     help="timed calls per token count of each MoE layer shape (0 skips them)")
     ap.add_argument("--extra-steps", type=int, default=20,
-                    help="timed calls per M of the compute sweep and the tensor-parallel rank "
-                         "shapes, plus the stream-read reference (0 skips them)")
+                    help="timed calls per M of the compute sweep, the tensor-parallel rank and the "
+                         "model-layer shapes, plus the stream-read reference (0 skips them)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     args = ap.parse_args()
@@ -648,10 +670,11 @@ def main():
         sparse = time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, args.format_steps,
                              max(2, args.warmup // 4), args.copies, stream, copies)
     moe = time_moe(w4, torch, dev, args.moe_steps, stream) if args.moe_steps > 0 else None
-    compute_sweep = tp8 = stream_ref = None
+    compute_sweep = tp8 = layers = stream_ref = None
     if args.extra_steps > 0:
         compute_sweep = time_compute_sweep(w4, torch, dev, args.extra_steps, stream)
         tp8 = time_tp8_rank(w4, torch, dev, args.extra_steps, stream)
+        layers = time_layers(w4, torch, dev, args.extra_steps, stream)
         stream_ref = stream_read_rate(w4, torch, dev, stream)
         log(f"stream read reference: {stream_ref}")
     formats = None
@@ -675,6 +698,7 @@ def main():
         "moe": moe,
         "compute_sweep": compute_sweep,
         "tp8_rank_shapes": tp8,
+        "layer_shapes": layers,
         "stream_read_reference": stream_ref,
         "device": device_state(torch, props, clocks),
     }
