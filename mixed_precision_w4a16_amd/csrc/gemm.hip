@@ -1792,7 +1792,8 @@ struct Config {
 constexpr int kSkinnyMaxNS = 10;
 constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this many slabs
 
-// Skinny kernel (M <= 16, N a multiple of 256).  Weights of up to 7 slabs per CU (N up to
+// Skinny kernel (M <= 64, N a multiple of 256; 17..64 rows only in the one-per-CU regime below,
+// at most 4 slabs per workgroup above 32 rows).  Weights of up to 7 slabs per CU (N up to
 // 28672 on 256 CUs) take the fewest slabs that leave at most one workgroup per CU: measured
 // on K 4096..8192, N 7168..28672 this beats two or three per CU by 1.1-1.5x (8192 x 10240 at
 // M = 16: 13.6 us with 3 slabs, 20.7 with 2; 8192 x 28672: 23.8 us with 7, 29.5 with 4); a
