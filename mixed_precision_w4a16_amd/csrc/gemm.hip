@@ -90,6 +90,7 @@ struct Params {
     int gens;                 // workgroups resident per CU (1..3), for wave priorities
     int KS;                   // whole-K kernel: workgroups sharing one slab group's K range
     int Kq, Kr;               // ... and G = KS * Kq + Kr: split k gets Kq (+1 if k < Kr) tiles
+    int SP;                   // whole-K kernel: row sub-problems of 16 * MB rows (grid z)
     int W;                    // workgroups = stripes
     long long T;              // total tiles = (N / Nt) * P * G
 };
@@ -653,6 +654,13 @@ __device__ __forceinline__ void slice_end(const Params &p, __amdgpu_buffer_rsrc_
         own = sigma;
     } else {
         store_partial<MB, NBW, WAVES>(rP, stripe, 0, wave, lane, acc);
+        // The caller zeroes the accumulators next.  A 128-bit store reads its data registers
+        // after it issues, and the compiler put the reset of the last stored fragment's first
+        // register right behind its store with no wait states in between (seen in the ISA of
+        // the 128-row kernel: element 0 of row block 7 then went out as zero now and then).
+        // Wait states here keep the reset behind the stores' register reads.
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         nonown = sigma;
     }
 }
@@ -1264,6 +1272,8 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
     const int KS = p.KS;
     const int jg = blockIdx.x;                           // slab group
     const int ks = blockIdx.y;                           // its K split
+    const int row0 = static_cast<int>(blockIdx.z) * 16 * MB;   // its row sub-problem
+    const int grp = static_cast<int>(blockIdx.z * gridDim.x + blockIdx.x);  // counter, pieces
     const int j0 = jg * NS;                              // the workgroup's first slab
     const int u0 = j0 >> 2, r = j0 & 3;
     const int gk0 = ks * p.Kq + (ks < p.Kr ? ks : p.Kr);            // the split's K tiles
@@ -1291,7 +1301,7 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
     uint32_t v_a[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        v_a[mb] = (static_cast<uint32_t>(16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
+        v_a[mb] = (static_cast<uint32_t>(row0 + 16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
     auto slab = [&](int i) __attribute__((always_inline)) {
         const int j = j0 + i;
         return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
@@ -1492,7 +1502,8 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
     auto write_slab = [&](int mb, int i, f4 v) __attribute__((always_inline)) {
         if constexpr (F::COL)
             v *= half_bits_to_float(col_param(j0 + i, 0));
-        uint32_t srow = static_cast<uint32_t>(j0 + i) * 32 + static_cast<uint32_t>(16 * mb) * rowN;
+        uint32_t srow =
+            static_cast<uint32_t>(j0 + i) * 32 + static_cast<uint32_t>(row0 + 16 * mb) * rowN;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(v[q]), rC, v_c, srow, 0);
@@ -1500,11 +1511,11 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
         }
     };
     // Split K: the piece of row block mb of slab j0 + i from split k goes to slot
-    // ((jg * KS + k) * NS + i) * MB + mb.
+    // ((grp * KS + k) * NS + i) * MB + mb, grp = the slab group within its row sub-problem.
     const __amdgpu_buffer_rsrc_t rP =
-        make_rsrc(p.partials, static_cast<uint32_t>(gridDim.x) * KS * NS * MB * 1024u);
+        make_rsrc(p.partials, static_cast<uint32_t>(gridDim.x * gridDim.z) * KS * NS * MB * 1024u);
     auto slot = [&](int k, int i, int mb) __attribute__((always_inline)) {
-        return (((static_cast<uint32_t>(jg) * KS + k) * NS + i) * MB + mb) * 1024u;
+        return (((static_cast<uint32_t>(grp) * KS + k) * NS + i) * MB + mb) * 1024u;
     };
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -1538,7 +1549,7 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
     __shared__ int arrived;
     __syncthreads();
     if (tid == 0)
-        arrived = __hip_atomic_fetch_add(p.counters + jg, 1, __ATOMIC_RELAXED,
+        arrived = __hip_atomic_fetch_add(p.counters + grp, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrived != KS - 1)
@@ -1567,7 +1578,7 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
             }
         }
     if (tid == 0)
-        __hip_atomic_store(p.counters + jg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ 2:4-sparse weights
@@ -1786,7 +1797,8 @@ struct Config {
     long long T;
     int NS;          // > 0: the skinny kernel, NS slabs per workgroup (W workgroups)
     int KS;          // the skinny kernel's K splits per slab group (1: none)
-    int SMB;         // the skinny kernel's 16-row blocks (1, or 2 for M = 17..32)
+    int SMB;         // the skinny kernel's 16-row blocks (1, 2 or 4)
+    int SP;          // the skinny kernel's row sub-problems (2 for M = 65..128)
 };
 
 constexpr int kSkinnyMaxNS = 10;
@@ -1810,11 +1822,12 @@ constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this man
 // starts, so the weights and A must lie below that.
 int skinny_slabs(int M, int K, int N, int cus)
 {
-    if (M > 64 || N % 256)
+    if (M > 128 || N % 256)
         return 0;
     const long long S = N / 16;
+    const long long P = M > 64 ? 2 : 1;   // 64-row sub-problems side by side
     long long ns = (S + 2LL * cus - 1) / (2LL * cus);
-    const long long ns1 = (S + cus - 1) / cus;
+    const long long ns1 = (P * S + cus - 1) / cus;
     if (M > 32 && ns1 > 4)
         return 0;                      // 64 rows: only up to 4 slabs (registers)
     if (ns1 <= kSkinnyOneMaxNS) {
@@ -1855,19 +1868,19 @@ double skinny_model_us(int G, int NS, int KS, int M)
     return c0 + static_cast<double>(G) / (kWaves * KS) * (a + b * NS) + (KS > 1 ? cs : 0.0);
 }
 
-void skinny_split(int S, int G, int M, int cus, int &ns, int &ks)
+void skinny_split(int S, int G, int M, int P, int cus, int &ns, int &ks)
 {
     ks = 1;
-    if ((S + ns - 1) / ns > cus)
+    if (P * ((S + ns - 1) / ns) > cus)
         return;                                   // more than one workgroup per CU
     const double base = skinny_model_us(G, ns, 1, M);
     double best = 0.85 * base;
     const int ns0 = ns;
     for (int n = ns0; n <= 4; n = n < 2 ? 2 : n + 2) {
         const int wn = (S + n - 1) / n;
-        if (wn > kMaxWGs)
+        if (P * wn > kMaxWGs)
             continue;
-        const int kmax = std::min({kSkinnyMaxKS, cus / wn, G / (2 * kWaves)});
+        const int kmax = std::min({kSkinnyMaxKS, cus / (P * wn), G / (2 * kWaves)});
         for (int k = 2; k <= kmax; ++k) {
             const double t = skinny_model_us(G, n, k, M);
             if (t < best) {
@@ -1973,8 +1986,9 @@ Config choose_config(int M, int K, int N, int cus)
     c.NS = skinny_slabs(M, K, N, cus);
     c.KS = 1;
     c.SMB = M > 32 ? 4 : (M > 16 ? 2 : 1);
+    c.SP = M > 64 ? 2 : 1;
     if (c.NS > 0) {
-        skinny_split(N / 16, c.G, M, cus, c.NS, c.KS);
+        skinny_split(N / 16, c.G, M, c.SP, cus, c.NS, c.KS);
         const int wn = (N / 16 + c.NS - 1) / c.NS;
         if (c.NS == 1 && c.KS == 1 && c.G > 128)
             c.NS = 0;                  // one slab a workgroup over a long K: the stripe kernel
@@ -1983,7 +1997,7 @@ Config choose_config(int M, int K, int N, int cus)
                                        // than 8: the stripe kernel (28672 x 8192 at M = 32:
                                        // 37.2 vs 39.1 us; 8192 x 10240 at M = 64: 31.7 vs 36.1)
         else
-            c.W = wn * c.KS;
+            c.W = wn * c.KS * c.SP;
     }
     return c;
 }
@@ -2048,7 +2062,7 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
 template <int MB, int NS, class F>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F>), dim3(p.W / p.KS, p.KS),
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F>), dim3(p.W / (p.KS * p.SP), p.KS, p.SP),
                        dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
@@ -2209,6 +2223,7 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     p.T = c.T;
     p.gens = std::min(3, (c.W + d.cus - 1) / d.cus);
     p.KS = c.KS;
+    p.SP = c.NS > 0 ? c.SP : 1;
     p.Kq = c.G / c.KS;
     p.Kr = c.G % c.KS;
 

@@ -255,6 +255,25 @@ def test_workspace_shared_across_shapes_stays_clean():
         assert int(ws[:4096].count_nonzero()) == 0      # counters back to zero
 
 
+# The 128-row kernel on the 72k x 18k weight at M = 128 splits column slices between stripes.
+# Its pieces once went out with element 0 of row block 7 zeroed now and then (a 128-bit store's
+# data register reset right behind the store): the same call must give the same bits on every
+# run, and rows 112..127 must match the oracle on columns at every lane position of a slab.
+def test_128_row_tiles_repeat_bit_for_bit_and_last_row_block_on_the_full_weight():
+    K, N, M = 18432, 73728, 128
+    A, q, s = draw(K, N, M, seed=5)
+    W = Weights(q, s)
+    first = W.run(A)
+    for _ in range(4):
+        assert np.array_equal(bits(W.run(A)), bits(first))
+    cols = np.concatenate([np.arange(16 * j, 16 * j + 16) for j in (0, 1011, 2303, 4607)])
+    ref = oracle.gemm(A[112:128], np.ascontiguousarray(q[:, cols]), np.ascontiguousarray(s[:, cols]))
+    check(first[112:128, cols], ref, "M=128 rows 112..127")
+    del W, q
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _sampled_check(shape, seed=0, ncols=48):
@@ -425,7 +444,8 @@ def test_no_write_past_the_rows_of_c(M, K, N, fmt):
 # ------------------------------------------------------------------ M <= 16: whole-K workgroups
 
 # M = 20 and 32 run the kernel's two-row-block form (one workgroup per CU only), M = 40 and
-# 64 its four-row-block form where N takes at most four slabs per CU.
+# 64 its four-row-block form where N takes at most four slabs per CU, M = 100 and 128 two
+# 64-row sub-problems of it side by side where that still fits (1024 x 8192 here).
 # N chosen for 2 to 9 slabs per workgroup: one workgroup per CU up to 7 slabs (8192 -> 2,
 # 9216 -> 3, 12544 -> 4, 16640 -> 5, 26880 -> 7 on 256 CUs), 73728 -> 6 or 9 with two or three
 # per CU; 8960 (560 slabs in workgroups of three), 17152 (1072 in fives) and 27904 (1744 in
@@ -438,7 +458,7 @@ SKINNY_SHAPES = [(128, 9216), (256, 16640), (384, 26880), (1024, 16640), (4096, 
 
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
 @pytest.mark.parametrize("K,N", SKINNY_SHAPES)
-@pytest.mark.parametrize("M", [1, 5, 16, 20, 32, 40, 64])
+@pytest.mark.parametrize("M", [1, 5, 16, 20, 32, 40, 64, 100, 128])
 def test_whole_k_workgroups_against_oracle(M, K, N, fmt):
     if fmt == "group128":
         A, q, s = draw(K, N, M, seed=M + K + N)
@@ -472,7 +492,8 @@ def test_whole_k_workgroups_one_hot_rows_are_bit_exact(fmt):
 
 
 # Whole-K workgroups with K split between several workgroups (few slab groups over a long K;
-# M = 17..32 and 33..64 run the kernel's two- and four-row-block forms).  The selection takes,
+# M = 17..32 and 33..64 run the kernel's two- and four-row-block forms, M = 65..128 two 64-row
+# sub-problems side by side, each with its own counters and pieces).  The selection takes,
 # as (slabs per workgroup, splits): 8192 x 1280 (2, 6) or (4, 8); 14336 x 2048 (4, 8);
 # 28672 x 1024 (2, 8); 6144 x 256 (1, 6); 11008 x 4096 (4, 4), whose 86 K tiles make splits of
 # 21 and 22.  The last workgroup to finish a slab group sums the pieces: two calls on one
@@ -482,7 +503,7 @@ SPLIT_K_SHAPES = [(8192, 1280), (14336, 2048), (28672, 1024), (6144, 256), (1100
 
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
 @pytest.mark.parametrize("K,N", SPLIT_K_SHAPES)
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 33, 64, 65, 128])
 def test_whole_k_split_k_against_oracle(M, K, N, fmt):
     if fmt == "group128":
         A, q, s = draw(K, N, M, seed=M + K + N + 1)
