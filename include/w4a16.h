@@ -154,7 +154,7 @@ int w4a16_workspace_size(int M, int K, int N, size_t *bytes);
  * The weight matrix is split into column slices and each slice's K range into 128-row
  * tiles; workgroups take equal runs of consecutive tiles ("stripes", deep-dive page
  * section "Split-K 与全局归约"; MARLIN README page, striped partitioning).  For M <= 16,
- * and up to M = 64 on narrower weights, workgroups instead own a few 16-column slabs over
+ * and up to M = 128 on narrower weights, workgroups instead own a few 16-column slabs over
  * all of K or over one of a few equal K splits.  Output shared by several workgroups is
  * summed in fp32 in a fixed order, so results are identical from run to run.
  *

@@ -55,7 +55,7 @@
 // * M > 64 runs a second kernel with 128-row tiles (w4a16_gemm_wide_kernel, further down):
 //   every weight tile meets a whole 128-row block of A, A is brought into LDS by DMA.
 // * M <= 16 runs a third kernel (w4a16_gemm_skinny_kernel, further down) on most shapes, and
-//   M = 17..64 on weights of up to 7 (4 above 32 rows) slabs per CU: a workgroup owns a few 16-column slabs over
+//   M = 17..128 on weights of up to 7 (4 above 32 rows) slabs per CU: a workgroup owns a few 16-column slabs over
 //   all of K (or over one of a few K splits) and its four waves split that range.
 #include <hip/hip_runtime.h>
 
@@ -1203,8 +1203,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // ------------------------------------------------------------------------- skinny kernel
 //
 // `w4a16_gemm_skinny_kernel<MB, NS, F>`, MB 16-row blocks (M <= 16; M = 17..32 on weights of
-// up to seven slabs per CU and M = 33..64 on weights of up to four, where one workgroup per CU
-// leaves registers to spare), N a multiple of 256.  Each decoded weight fragment feeds MB
+// up to seven slabs per CU and M = 33..128 on weights of up to four, as two 64-row
+// sub-problems above 64 rows (grid z), where one workgroup per CU leaves registers to spare), N
+// a multiple of 256.  Each decoded weight fragment feeds MB
 // matrix instructions.  The weight stream bounds
 // the product, and the stripe scheme's split slices cost a store, a counter and a read at the
 // very end, when every stripe finishes at once (on small weights that chain is most of the
@@ -1804,8 +1805,8 @@ struct Config {
 constexpr int kSkinnyMaxNS = 10;
 constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this many slabs
 
-// Skinny kernel (M <= 64, N a multiple of 256; 17..64 rows only in the one-per-CU regime below,
-// at most 4 slabs per workgroup above 32 rows).  Weights of up to 7 slabs per CU (N up to
+// Skinny kernel (M <= 128, N a multiple of 256; 17..128 rows only in the one-per-CU regime
+// below, at most 4 slabs per workgroup above 32 rows, two 64-row sub-problems above 64).  Weights of up to 7 slabs per CU (N up to
 // 28672 on 256 CUs) take the fewest slabs that leave at most one workgroup per CU: measured
 // on K 4096..8192, N 7168..28672 this beats two or three per CU by 1.1-1.5x (8192 x 10240 at
 // M = 16: 13.6 us with 3 slabs, 20.7 with 2; 8192 x 28672: 23.8 us with 7, 29.5 with 4); a
