@@ -274,6 +274,19 @@ def test_128_row_tiles_repeat_bit_for_bit_and_last_row_block_on_the_full_weight(
     torch.cuda.empty_cache()
 
 
+# Every kernel that splits slices between stripes, on a weight whose 16-tile slices split
+# unevenly: the same call repeats bit for bit (a race in the piece stores shows as differing
+# elements from run to run, whatever the oracle's tolerance).
+@pytest.mark.parametrize("M", [24, 48, 64, 96, 113, 128])
+def test_split_slices_repeat_bit_for_bit(M):
+    K, N = 2048, 73728
+    A, q, s = draw(K, N, M, seed=6)
+    W = Weights(q, s)
+    first = W.run(A)
+    for _ in range(3):
+        assert np.array_equal(bits(W.run(A)), bits(first)), M
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _sampled_check(shape, seed=0, ncols=48):
