@@ -1219,10 +1219,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // (zero, no memory access).  No per-tile barrier.
 //
 // Split K (p.KS > 1), for weights with too few slab groups to give every CU work: the grid's
-// second dimension is the split, and the KS workgroups (x, 0 .. KS - 1) share slab group x,
-// each taking a contiguous 1/KS of the K tiles.  Each
-// stores its fp32 sums as one piece (device-scope stores, a 1 KiB slot per slab), counts in on
-// the group's counter, and the last to arrive sums the KS pieces in split order -- a fixed
+// second dimension is the split (the third, above 64 rows, the 64-row sub-problem), and the
+// KS workgroups (x, 0 .. KS - 1, z) share slab group x of sub-problem z, each taking a
+// contiguous 1/KS of the K tiles.  Each stores its fp32 sums as one piece (device-scope
+// stores, a 1 KiB slot per slab and row block), counts in on the group's counter, and the
+// last to arrive sums the KS pieces in split order -- a fixed
 // order, so results repeat bit for bit -- scales, writes C and resets the counter, the
 // protocol of the stripe kernel's split slices (see settle()).  Nobody waits for another
 // workgroup.
