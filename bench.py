@@ -7,27 +7,22 @@ bytes per call: D = 2MK (A) + KN/2 (codes) + KN/64 (scales) + 2MN (C); flops F =
 Roofline per call: T_bound = max(D / 8 TB/s, F / 2.5 PFLOP/s); fp16-weight byte bound
 D16 = 2MK + 2KN + 2MN (the MARLIN paper's uncompressed reference point).
 
-`roofline` covers the dominant kernel: the whole-K-workgroup kernel as it serves M = 1..8
-(six 16-column slabs per workgroup on this weight, three workgroups per CU), four of the eight
-calls and about 40% of the sweep's time; HBM-bound, so achieved = its algorithmic bytes per
-launch / its mean launch time.  `roofline_by_kernel` gives the same for every kernel of the
-sweep (M = 16 runs the same kernel with nine slabs, two workgroups per CU), the 128-row
-(M = 128) kernel against the fp16 MFMA peak.
+`roofline` covers the dominant kernel: the whole-K-workgroup kernel as it serves M = 1..8,
+four of the eight calls; HBM-bound, so achieved = its algorithmic bytes per launch / its mean
+launch time (HIP events on the launch stream around every call).  `roofline_by_kernel` gives
+the same for every kernel of the sweep, the compute-bound ones against the fp16 MFMA peak;
+`traffic` is the measured HBM bytes per launch from the committed counter runs, while the
+kernel source is the one they were taken on.
 
-Also reported, outside `value`: `formats`, the per-call time of the other packed formats
-(one scale per column, zero points, both) on the same weight at M = 1, 16, 64, 128, timed
-call by call alternately with the group-128 symmetric format; `repack`, the load-time
-conversion of a checkpoint-style packed weight of the same size into the multiply's layout;
-`sparse_24`, the 2:4-sparse path on the same weight with two of every four codes pruned, at
-every M, alternated call by call with the dense path; `moe`, the mixture-of-experts grouped
-product on two layer shapes, fp16 and bf16 activations; `compute_sweep`, the compute-bound
-8192 x 28672 weight at M = 256, 512, 1024 with its fraction of the fp16 matrix peak;
-`tp8_rank_shapes`, one 8-way tensor-parallel rank's share of the Llama-2-70B block;
-`layer_shapes`, the Llama-2-7B block's layers at M = 1, 16, 64 and the 70B block's at M = 16,
-32, 128, each with its fraction of the roofline bound;
-`stream_read_reference`, the HBM read rate of a plain streaming read, for context.
+The stdout line (kept to a few KB) also holds the per-M `sweep`, the compute-bound
+8192 x 28672 sweep at M = 256, 512, 1024 (`compute_sweep`), the measured stream-read and
+random-operand MFMA rates (`references`), the CPU baseline (the oracle on a column sample)
+and the run state (clocks, power cap and ECC state from sysfs, CPU model, core counts).
+The rest goes to stderr and to the `--details` JSON file: the other packed formats, the
+load-time repack, the 2:4-sparse path, the MoE layers, the tensor-parallel rank and
+model-layer shapes, each with its fraction of the roofline bound.
 
-Prints one JSON line on stdout.  Single GPU only.
+Single GPU only.
 """
 from __future__ import annotations
 
@@ -509,28 +504,162 @@ def stream_read_rate(w4, torch, dev, stream):
             "GBps": round(best, 1), "frac_of_spec": round(best / HBM_PEAK_GBPS, 4)}
 
 
-def clock_state():
-    """Clocks and power through rocm-smi, queried before this process touches the GPU (the
-    tool runs as a child process) and skipped under a profiler, whose preloaded library would
-    have initialised the GPU in that child before it starts the tool."""
-    import subprocess
-    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF")
-                                                             for k in os.environ):
-        return "skipped under a profiler"
+def _read(path, limit=400):
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
-                            "--showmemuse"], capture_output=True, text=True, timeout=20)
-        return [ln.strip() for ln in r.stdout.splitlines()
-                if ":" in ln and ("clk" in ln.lower() or "power" in ln.lower())][:16]
-    except Exception as exc:            # tool missing or not permitted: note it and go on
-        return f"unavailable ({type(exc).__name__})"
+        with open(path) as f:
+            return f.read(limit).strip()
+    except OSError:
+        return None
 
 
-def device_state(torch, props, clocks):
-    """Software and clock state of the run."""
+def gpu_sysfs_state(pci_bus_id=None):
+    """Clocks, power cap and ECC state of the GPU from sysfs (amdgpu's files; reading them
+    starts no process and does not touch the GPU).  The card is the one at `pci_bus_id`
+    when known, else the only amdgpu card with clock tables."""
+    import glob
+    cards = []
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        if os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+            cards.append(dev)
+    pick = None
+    if pci_bus_id is not None:
+        for dev in cards:
+            if os.path.realpath(dev).lower().endswith(f":{pci_bus_id:02x}:00.0"):
+                pick = dev
+    if pick is None and len(cards) == 1:
+        pick = cards[0]
+    if pick is None:
+        return {"sysfs": f"{len(cards)} amdgpu cards with clock tables, none matched"}
+
+    def levels(table):
+        # the DPM levels ("0: 500Mhz", ...); which one is current at the moment of reading
+        # says nothing about the timed region, so it is not reported
+        if not table:
+            return None
+        return [ln.strip().rstrip("*").strip() for ln in table.splitlines() if ln.strip()]
+
+    state = {"card": os.path.realpath(pick).rsplit("/", 1)[-1],
+             "sclk_levels": levels(_read(os.path.join(pick, "pp_dpm_sclk"))),
+             "mclk_levels": levels(_read(os.path.join(pick, "pp_dpm_mclk")))}
+    caps = sorted(glob.glob(os.path.join(pick, "hwmon", "hwmon*", "power1_cap")))
+    if caps:
+        cap = _read(caps[0])
+        state["power_cap_w"] = int(cap) / 1e6 if cap and cap.isdigit() else cap
+    feats = _read(os.path.join(pick, "ras", "features"))
+    umc = _read(os.path.join(pick, "ras", "umc_err_count"))
+    if feats is None and umc is None:
+        # no per-device RAS files: the driver's module parameters (ras_enable -1 = auto,
+        # 0 = off, 1 = on; ras_mask: the RAS blocks asked for, bit 0 = memory/UMC)
+        par = "/sys/module/amdgpu/parameters"
+        state["ecc"] = {"ras_files": "absent",
+                        "amdgpu_ras_enable": _read(os.path.join(par, "ras_enable")),
+                        "amdgpu_ras_mask": _read(os.path.join(par, "ras_mask"))}
+    else:
+        # RAS feature mask: bit 0 is the memory controller block (UMC), i.e. HBM ECC on
+        mask = None
+        if feats:
+            for tok in feats.replace(":", " ").split():
+                if tok.lower().startswith("0x"):
+                    mask = int(tok, 16)
+                    break
+        state["ecc"] = {"ras_features": feats,
+                        "hbm_ecc_enabled": None if mask is None else bool(mask & 1),
+                        "umc_err_count": umc}
+    return state
+
+
+def host_state():
+    """The host the CPU baseline runs on: CPU model and core counts."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count()
+    return {"cpu_model": model, "host_cores": os.cpu_count(), "cores_allowed": allowed,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_threads(host):
+    """Threads for the CPU baseline: every core this process may use, capped by
+    OMP_NUM_THREADS where the environment sets the process's CPU share (the GPU machines give a
+    one-GPU job 16 threads, whatever the host's core count)."""
+    n = host["cores_allowed"] or 1
+    omp = host["omp_num_threads"]
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
+def device_state(torch, props, sysfs, host):
+    """Software, device, clock, ECC and host state of the run."""
     return {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__,
-            "name": props.name, "arch": getattr(props, "gcnArchName", ""),
-            "cus": props.multi_processor_count, "rocm_smi": clocks}
+            "gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "cus": props.multi_processor_count, "gpu_sysfs": sysfs, **host}
+
+
+def mfma_rate(w4, torch, dev, stream):
+    """Context for the compute-bound fraction: the sustained fp16 matrix rate on random
+    operands (w4a16_mfma_probe: 1024 workgroups of 4 waves, 64 independent instructions per
+    round), both instruction shapes, best of 3 launches each."""
+    g = torch.Generator(device=dev).manual_seed(0)
+    src = (torch.randn(1 << 20, device=dev, generator=g) * 0.5).half()
+    res = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        best = 0.0
+        for _ in range(4):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _, fl = w4.mfma_probe(src, shape=shape, workgroups=1024, iters=400, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[name] = round(best, 1)
+    del src
+    return {"kernel": "w4a16_mfma_probe, random fp16 operands", "TFLOPs": res,
+            "frac_of_spec": {k: round(v / MFMA_F16_PEAK_TFLOPS, 4) for k, v in res.items()}}
+
+
+SHORT_NAMES = {
+    "w4a16_gemm_skinny_kernel": "skinny",
+    "w4a16_gemm_kernel": "stripe",
+    "w4a16_gemm_wide_kernel": "wide",
+}
+
+
+def compose_line(args, value, ms_per_step, config, kernels, sweep, cpu, refs, state,
+                 compute_sweep, details_path):
+    """The one JSON line bench.py prints: headline, roofline of the dominant kernel and of
+    each kernel of the sweep, the per-M sweep, the CPU baseline, reference rates and the run
+    state.  Everything else goes to the details file (kept to a few KB so that a driver
+    reading the tail of stdout gets the whole line)."""
+    by_kernel = [{k: v for k, v in r.items() if k in ("kernel", "M", "bound", "achieved", "unit",
+                                                      "frac", "traffic", "mean_launch_us")}
+                 for r in kernels]
+    line = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": config,
+        "roofline": kernels[0],
+        "roofline_by_kernel": by_kernel,
+        "sweep": sweep,
+        "compute_sweep": compute_sweep,
+        "references": refs,
+        "cpu_baseline": cpu,
+        "run_state": state,
+        "details": details_path,
+    }
+    return json.dumps(line, separators=(",", ":"))
 
 
 def main():
@@ -549,16 +678,18 @@ def main():
                     help="timed calls per token count of each MoE layer shape (0 skips them)")
     ap.add_argument("--extra-steps", type=int, default=20,
                     help="timed calls per M of the compute sweep, the tensor-parallel rank and the "
-                         "model-layer shapes, plus the stream-read reference (0 skips them)")
+                         "model-layer shapes, plus the reference rates (0 skips them)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
+    ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
+                    help="file for the sections not in the stdout line ('' skips it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
-    clocks = clock_state()              # before anything touches the GPU
+    host = host_state()
     import torch
     import mixed_precision_w4a16_amd as w4
     from workloads import LARGE, draw
@@ -569,6 +700,8 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    state = device_state(torch, props, gpu_sysfs_state(getattr(props, "pci_bus_id", None)), host)
+    log(f"run state: {json.dumps(state)}")
 
     t = time.perf_counter()
     A, q, s = draw(K, N, max(Ms), seed=0, sigma=shape.sigma)
@@ -617,6 +750,7 @@ def main():
         for _ in range(2):
             torch.mul(x, 1.0, out=y)
         torch.cuda.synchronize()
+        del x, y
 
     sweep = []
     tot_bytes = 0.0
@@ -628,11 +762,10 @@ def main():
         sweep.append({
             "M": M, "us": round(us, 2), "GBps": round(gbps, 1),
             "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "TFLOPs": round(F / us / 1e6, 2),
+            "TFLOPs": round(F / us / 1e6, 1),
             "mfma_frac": round(F / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
             "roofline_frac": round(t_bound / us, 4),
-            "bound": "hbm" if D / HBM_PEAK_GBPS >= F / (MFMA_F16_PEAK_TFLOPS * 1e3) else "mfma",
-            "speedup_vs_fp16_weight_bound": round(D16 / (HBM_PEAK_GBPS * 1e3) / us, 3),
+            "x_fp16_bound": round(D16 / (HBM_PEAK_GBPS * 1e3) / us, 3),
         })
         tot_bytes += D
         log(f"M={M:4d}  {us:8.1f} us  {gbps:7.0f} GB/s ({gbps / HBM_PEAK_GBPS:5.1%} HBM)  "
@@ -642,9 +775,6 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = tot_bytes * args.steps / wall / 1e9
     traffic = measured_traffic()
-    if traffic is not None:
-        for row in sweep:
-            row["hbm_bytes_measured"] = traffic["per_M"][str(row["M"])]["hbm_bytes"]
     by_M = {row["M"]: row for row in sweep}
 
     def roof(name, ms, bound):
@@ -664,49 +794,57 @@ def main():
                 "mean_launch_us": round(us, 2)}
 
     kernels = [roof(*k) for k in KERNELS]
-    repack = time_repack(w4, torch, dev, K, N, 10, stream) if args.format_steps > 0 else None
-    sparse = None
+    details = {"sweep_traffic_source": None if traffic is None else os.path.relpath(TRAFFIC_FILE, ROOT)}
+    if traffic is not None:
+        details["hbm_bytes_measured_by_M"] = {m: traffic["per_M"][str(m)]["hbm_bytes"] for m in Ms}
+
     if args.format_steps > 0:
-        sparse = time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, args.format_steps,
-                             max(2, args.warmup // 4), args.copies, stream, copies)
-    moe = time_moe(w4, torch, dev, args.moe_steps, stream) if args.moe_steps > 0 else None
-    compute_sweep = tp8 = layers = stream_ref = None
+        details["repack"] = time_repack(w4, torch, dev, K, N, 10, stream)
+        details["sparse_24"] = time_sparse(w4, torch, dev, Ad, q, s, K, N, Ms, args.format_steps,
+                                           max(2, args.warmup // 4), args.copies, stream, copies)
+    if args.moe_steps > 0:
+        details["moe"] = time_moe(w4, torch, dev, args.moe_steps, stream)
+    refs = None
+    compute_sweep = None
     if args.extra_steps > 0:
         compute_sweep = time_compute_sweep(w4, torch, dev, args.extra_steps, stream)
-        tp8 = time_tp8_rank(w4, torch, dev, args.extra_steps, stream)
-        layers = time_layers(w4, torch, dev, args.extra_steps, stream)
-        stream_ref = stream_read_rate(w4, torch, dev, stream)
-        log(f"stream read reference: {stream_ref}")
-    formats = None
+        details["compute_sweep"] = compute_sweep
+        details["tp8_rank_shapes"] = time_tp8_rank(w4, torch, dev, args.extra_steps, stream)
+        details["layer_shapes"] = time_layers(w4, torch, dev, args.extra_steps, stream)
+        sref = stream_read_rate(w4, torch, dev, stream)
+        mref = mfma_rate(w4, torch, dev, stream)
+        log(f"stream read reference: {sref}")
+        log(f"MFMA reference: {mref}")
+        refs = {"stream_read_GBps": sref["GBps"], "stream_read_frac_of_spec": sref["frac_of_spec"],
+                "mfma_f16_TFLOPs": mref["TFLOPs"], "mfma_f16_frac_of_spec": mref["frac_of_spec"]}
+        details["stream_read_reference"] = sref
+        details["mfma_reference"] = mref
+        compute_sweep = [{k: r[k] for k in ("M", "us", "TFLOPs", "mfma_frac")} for r in compute_sweep]
     if args.format_steps > 0:
-        formats = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
-                               max(2, args.warmup // 4), args.copies, stream, copies)
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": LARGE.name, "K": K, "N": N, "M": list(Ms), "group": GROUP,
-                   "weights": "int4 codes + fp16 scales (4.125 bits/weight)",
-                   "weight_copies_rotated": args.copies},
-        "roofline": kernels[0],
-        "roofline_by_kernel": kernels,
-        "sweep": sweep,
-        "formats": formats,
-        "repack": repack,
-        "sparse_24": sparse,
-        "moe": moe,
-        "compute_sweep": compute_sweep,
-        "tp8_rank_shapes": tp8,
-        "layer_shapes": layers,
-        "stream_read_reference": stream_ref,
-        "device": device_state(torch, props, clocks),
-    }
+        details["formats"] = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
+                                          max(2, args.warmup // 4), args.copies, stream, copies)
+    del copies, pd, sd, Ad, outs, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    cpu = None
     if args.cpu_cols > 0:
-        nthreads = min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(A, q, s, Ms, args.cpu_cols, nthreads)
-        log(f"cpu baseline: {out['cpu_baseline']}")
-    print(json.dumps(out), flush=True)
+        cpu = cpu_baseline(A, q, s, Ms, args.cpu_cols, oracle_threads(host))
+        cpu.update(cpu_model=host["cpu_model"], host_cores=host["host_cores"])
+        log(f"cpu baseline: {cpu}")
+    config = {"workload": LARGE.name, "K": K, "N": N, "M": list(Ms), "group": GROUP,
+              "weights": "int4 codes + fp16 scales (4.125 bits/weight)",
+              "weight_copies_rotated": args.copies}
+    details_path = None
+    if args.details:
+        os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
+        with open(args.details, "w") as f:
+            json.dump({"config": config, "sweep": sweep, "roofline_by_kernel": kernels,
+                       **details}, f, indent=1)
+        details_path = os.path.relpath(os.path.abspath(args.details), ROOT)
+        log(f"details written to {details_path}")
+    print(compose_line(args, round(value, 1), round(ms_per_step, 4), config, kernels, sweep, cpu,
+                       refs, state, compute_sweep, details_path), flush=True)
 
 
 if __name__ == "__main__":

@@ -99,7 +99,10 @@ int w4a16_pack(const uint8_t *codes, const uint16_t *scales, int K, int N, int g
 
 /*
  * Exact inverse of w4a16_pack (host, synchronous).  For tests and tooling; not on the
- * multiply path.  Same arguments and errors as w4a16_pack with inputs and outputs swapped.
+ * multiply path: the layout check the deep-dive page lists among its validation levels
+ * (section "适用边界与工程陷阱", level "布局": unpacking what was packed or repacked must give
+ * back the same codes, scales and zero points).  Same arguments and errors as w4a16_pack with
+ * inputs and outputs swapped.
  */
 int w4a16_unpack(const uint32_t *packed, const uint16_t *scales_packed, int K, int N, int group,
                  uint8_t *codes_out, uint16_t *scales_out);
@@ -137,6 +140,41 @@ int w4a16_unpack_zp(const uint32_t *packed, const uint16_t *params, int K, int N
  * (as w4a16_gemm), W4A16_EUNSUPPORTED (current device is not gfx950) or W4A16_EHIP.
  */
 int w4a16_workspace_size(int M, int K, int N, size_t *bytes);
+
+/*
+ * A bound on w4a16_workspace_size(M, K, N) that needs no device: never smaller than what any
+ * device of at most 512 compute units asks for (MI355X has 256), for any of the multiply
+ * entry points that take a workspace.  For sizing a workspace before a GPU is chosen or
+ * where the exact call cannot be made (the pages allocate and zero the workspace once, when
+ * the layer is loaded: deep-dive page, "可复现的调用链与实现伪代码").  Sizes as w4a16_gemm;
+ * returns 0 for a negative size or K not a positive multiple of 128.
+ *
+ * Terms: the 4 KiB counter area, plus the larger of
+ *   - the stripe kernels' fp32 partial tiles: two Mt x Nt tiles per stripe, at most 1024
+ *     stripes and at most one stripe per 128 x Nt x Mt tile, Mt = 16, 32, 64 or 128 rows as M
+ *     is at most 16, 32, 64 or larger, Nt = 256 columns (N if smaller);
+ *   - the whole-K kernels' split-K pieces: 1 KiB per 16 x 16 output block per K split, at
+ *     most 64 pieces per 16-column slab (M <= 128 only), and at most 40 MiB.
+ */
+static inline size_t w4a16_workspace_bound(int M, int K, int N)
+{
+    if (M < 0 || K <= 0 || N < 0 || K % 128)
+        return 0;
+    const size_t mt = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
+    const size_t nt = N < 256 ? (size_t)N : 256;
+    const size_t mcov = M <= 64 ? mt : 128 * (((size_t)M + 127) / 128);
+    size_t stripes = 2 * 1024 * mt * nt * 4;
+    const size_t by_tiles = 8 * (size_t)N * ((size_t)K / 128) * mcov;
+    if (by_tiles < stripes)
+        stripes = by_tiles;
+    size_t pieces = 0;
+    if (M <= 128) {
+        pieces = ((size_t)N / 16 + 9) * 64 * 1024;
+        if (pieces > ((size_t)40 << 20))
+            pieces = (size_t)40 << 20;
+    }
+    return 4096 + (stripes > pieces ? stripes : pieces);
+}
 
 /*
  * C = A * Bhat on the current HIP device, enqueued on `stream` (a hipStream_t passed as
@@ -353,6 +391,26 @@ int w4a16_moe_gemm_topk(const void *A, const uint32_t *packed, const uint16_t *p
  * or not a multiple of 16, src not 16-byte aligned), W4A16_EUNSUPPORTED, W4A16_EHIP.
  */
 int w4a16_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream);
+
+/*
+ * Measurement support, not part of the multiply: the matrix cores' sustained fp16 rate on
+ * operands that change from one instruction to the next, for a measured peak to set the
+ * compute-bound sweep against beside the nominal 2.5 PFLOP/s (deep-dive page, "适用边界与工程陷阱",
+ * validation level "Kernel": record the matrix units' utilisation beside HBM bandwidth).
+ * `workgroups` workgroups of 4 waves each run `iters` rounds of 64 fp16 matrix instructions
+ * (8 independent fp32 accumulators), each wave on 16 operand fragments of its own taken from
+ * `src` (random fp16 values give the power draw of real data; constant ones run faster).
+ *   shape      0: v_mfma_f32_16x16x32_f16 (16384 flops each), 1: v_mfma_f32_32x32x16_f16
+ *              (32768 flops each)
+ *   src        device, src_bytes bytes (a multiple of 16, at least 16), 16-byte aligned
+ *   out        device float [workgroups * 256]: one sum of accumulators per lane (keeps the
+ *              work alive)
+ * Flops = workgroups * 4 * iters * 64 * (16384 or 32768).  Device, asynchronous on `stream`.
+ * Errors: W4A16_EINVAL (null pointer, src_bytes not a positive multiple of 16, misaligned
+ * src, workgroups or iters not positive, shape not 0 or 1), W4A16_EUNSUPPORTED, W4A16_EHIP.
+ */
+int w4a16_mfma_probe(const void *src, size_t src_bytes, int shape, int workgroups, int iters,
+                     float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,7 @@ layout on the GPU.  2:4-sparse weights: pack_24(codes, scales) and gemm_24(A, pa
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 
@@ -74,6 +75,8 @@ _lib.w4a16_moe_gemm_topk.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
 _lib.w4a16_moe_gemm_topk.restype = _i
 _lib.w4a16_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _p]
 _lib.w4a16_read_probe.restype = _i
+_lib.w4a16_mfma_probe.argtypes = [_p, ctypes.c_size_t, _i, _i, _i, _p, _p]
+_lib.w4a16_mfma_probe.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
@@ -81,7 +84,8 @@ ACT_F16, ACT_BF16 = 0, 1
 EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp",
             "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
             "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24",
-            "w4a16_moe_align", "w4a16_moe_gemm", "w4a16_moe_gemm_topk", "w4a16_read_probe")
+            "w4a16_moe_align", "w4a16_moe_gemm", "w4a16_moe_gemm_topk", "w4a16_read_probe",
+            "w4a16_mfma_probe")
 
 
 class W4A16Error(RuntimeError):
@@ -177,28 +181,65 @@ def to_device(packed: np.ndarray, scales_p: np.ndarray, device="cuda"):
 
 
 def workspace_bytes(M: int, K: int, N: int) -> int:
+    """Exact workspace bytes for (M, K, N) on the current device (w4a16_workspace_size)."""
     n = ctypes.c_size_t(0)
     _check("w4a16_workspace_size", _lib.w4a16_workspace_size(M, K, N, ctypes.byref(n)))
     return n.value
+
+
+@functools.lru_cache(maxsize=4096)
+def _ws_need(M: int, K: int, N: int, device_index: int) -> int:
+    # the answer depends only on the shape and the device (its compute-unit count); the
+    # caller has made device_index current
+    return workspace_bytes(M, K, N)
+
+
+def workspace_bound(M: int, K: int, N: int) -> int:
+    """The header's device-independent bound on workspace_bytes (w4a16_workspace_bound, a
+    static inline function of include/w4a16.h), evaluated as the header writes it."""
+    if M < 0 or K <= 0 or N < 0 or K % 128:
+        return 0
+    mt = 16 if M <= 16 else 32 if M <= 32 else 64 if M <= 64 else 128
+    nt = min(N, 256)
+    mcov = mt if M <= 64 else 128 * ((M + 127) // 128)
+    stripes = min(2 * 1024 * mt * nt * 4, 8 * N * (K // 128) * mcov)
+    pieces = min((N // 16 + 9) * 64 * 1024, 40 << 20) if M <= 128 else 0
+    return 4096 + max(stripes, pieces)
 
 
 _ws_lock = threading.Lock()
 _ws = {}
 
 
-def workspace(M: int, K: int, N: int, device=None):
-    """A zeroed workspace large enough for (M, K, N), cached per device and grown on demand.
-    Calls on different streams that may overlap need workspaces of their own (see
-    new_workspace)."""
+def workspace(M: int, K: int, N: int, device=None, stream=None):
+    """A zeroed workspace large enough for (M, K, N), cached per (device, stream) and grown on
+    demand: calls queued on one stream never overlap, so they can share one; another stream
+    gets its own."""
     import torch
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
     need = workspace_bytes(M, K, N)
+    key = (dev, stream.cuda_stream)
     with _ws_lock:
-        buf = _ws.get(dev)
+        buf = _ws.get(key)
         if buf is None or buf.numel() < need:
             buf = torch.zeros(need, dtype=torch.uint8, device=dev)
-            _ws[dev] = buf
+            _ws[key] = buf
         return buf
+
+
+def _check_ws(ws, A, M: int, K: int, N: int):
+    """A caller's workspace must be a contiguous uint8 tensor on A's device holding at least
+    workspace_bytes(M, K, N) bytes (the kernels size their partial tiles from the shape, not
+    from the allocation)."""
+    import torch
+    if (not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous()
+            or ws.device != A.device):
+        raise ValueError("ws must be a contiguous uint8 tensor on A's device")
+    need = _ws_need(M, K, N, A.device.index)
+    if ws.numel() < need:
+        raise ValueError(f"ws holds {ws.numel()} bytes; this shape needs {need}")
 
 
 def new_workspace(M: int, K: int, N: int, device="cuda"):
@@ -206,14 +247,8 @@ def new_workspace(M: int, K: int, N: int, device="cuda"):
     return torch.zeros(workspace_bytes(M, K, N), dtype=torch.uint8, device=device)
 
 
-def gemm(A, packed, params, N: int, out=None, ws=None, stream=None, group: int = GROUP,
-         zero_points: bool = False):
-    """C[M, N] = A[M, K] @ dequant(packed, params) on A's device and the current stream.
-
-    A: fp16 [M, K] contiguous CUDA tensor.  packed: int32 [K*N/8], params: fp16, both from
-    to_device(pack(...)) with the same group and zeros-or-not.  out: optional fp16 [M, N]
-    contiguous tensor.
-    """
+def _gemm_args(A, packed, params, N, out, group, zero_points):
+    """Checks of gemm()'s tensors; returns (M, K, out), out allocated if None."""
     import torch
     if A.dtype != torch.float16 or not A.is_cuda or A.dim() != 2 or not A.is_contiguous():
         raise ValueError("A must be a contiguous fp16 CUDA tensor of shape [M, K]")
@@ -231,13 +266,28 @@ def gemm(A, packed, params, N: int, out=None, ws=None, stream=None, group: int =
     elif (out.dtype != torch.float16 or out.shape != (M, N) or not out.is_contiguous()
           or out.device != A.device):
         raise ValueError("out must be a contiguous fp16 tensor [M, N] on A's device")
+    return M, K, out
+
+
+def gemm(A, packed, params, N: int, out=None, ws=None, stream=None, group: int = GROUP,
+         zero_points: bool = False):
+    """C[M, N] = A[M, K] @ dequant(packed, params) on A's device and the current stream.
+
+    A: fp16 [M, K] contiguous CUDA tensor.  packed: int32 [K*N/8], params: fp16, both from
+    to_device(pack(...)) with the same group and zeros-or-not.  out: optional fp16 [M, N]
+    contiguous tensor.
+    """
+    import torch
+    M, K, out = _gemm_args(A, packed, params, N, out, group, zero_points)
     if M == 0:
         return out
     with torch.cuda.device(A.device):
-        if ws is None:
-            ws = workspace(M, K, N, A.device)
         if stream is None:
             stream = torch.cuda.current_stream(A.device)
+        if ws is None:
+            ws = workspace(M, K, N, A.device, stream)
+        else:
+            _check_ws(ws, A, M, K, N)
         if group == GROUP and not zero_points:
             _check("w4a16_gemm", _lib.w4a16_gemm(A.data_ptr(), packed.data_ptr(),
                                                  params.data_ptr(), out.data_ptr(), M, K, N,
@@ -346,10 +396,12 @@ def gemm_24(A, packed, scales, N: int, out=None, ws=None, stream=None):
     if M == 0:
         return out
     with torch.cuda.device(A.device):
-        if ws is None:
-            ws = workspace(M, K, N, A.device)
         if stream is None:
             stream = torch.cuda.current_stream(A.device)
+        if ws is None:
+            ws = workspace(M, K, N, A.device, stream)
+        else:
+            _check_ws(ws, A, M, K, N)
         _check("w4a16_gemm_24", _lib.w4a16_gemm_24(A.data_ptr(), packed.data_ptr(),
                                                    scales.data_ptr(), out.data_ptr(), M, K, N,
                                                    ws.data_ptr(), stream.cuda_stream))
@@ -445,6 +497,25 @@ def moe_gemm(A, packed, params, sorted_ids, offsets, topk: int, E: int, N: int, 
             offsets.data_ptr(), None if row_scale is None else row_scale.data_ptr(),
             out.data_ptr(), T, topk, E, K, N, int(bool(zero_points)), act, stream.cuda_stream))
     return out
+
+
+def mfma_probe(src, shape: int = 0, workgroups: int = 1024, iters: int = 2000, out=None,
+               stream=None):
+    """Measurement support (w4a16_mfma_probe): fp16 matrix instructions on operand fragments
+    from CUDA tensor src (random fp16 values), shape 0 = 16x16x32, 1 = 32x32x16.  Returns
+    (out float32 [workgroups*256], flops of the launch)."""
+    import torch
+    if not src.is_cuda or not src.is_contiguous() or (src.numel() * src.element_size()) % 16:
+        raise ValueError("src must be a contiguous CUDA tensor of a multiple of 16 bytes")
+    if out is None:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device=src.device)
+    with torch.cuda.device(src.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(src.device)
+        _check("w4a16_mfma_probe", _lib.w4a16_mfma_probe(
+            src.data_ptr(), src.numel() * src.element_size(), int(shape), int(workgroups),
+            int(iters), out.data_ptr(), stream.cuda_stream))
+    return out, workgroups * 4 * iters * 64 * (16384 if shape == 0 else 32768)
 
 
 def read_probe(x, out=None, stream=None):

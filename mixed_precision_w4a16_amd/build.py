@@ -20,8 +20,8 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             # code object v5 loads in the HIP runtime PyTorch bundles as well as the system one
             "-mcode-object-version=5",
             "-Wall", "-Wno-unused-function",
@@ -30,22 +30,48 @@ def command(out: str = LIB, extra=()) -> list:
             # MFMA results in ordinary VGPRs: the fp32 epilogue math reads them directly
             # instead of copying each accumulator out of the AGPR file first
             "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", out, *extra]
+            "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def command(out: str = LIB, extra=()) -> list:
+    """One hipcc line that compiles every source and links the library."""
+    return [hipcc(), *flags(), "-shared", *SOURCES, "-o", out, *extra]
+
+
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (res.stdout + res.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in l]
-    if res.returncode != 0:
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile each source to an object in parallel, then link libw4a16.so (the same flags as
+    command(), one compiler process per source)."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
+    cmds = [[hipcc(), *flags(), "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, msgs), c in zip(results, cmds):
+        if rc != 0:
+            sys.stderr.write("\n".join(msgs) + "\n")
+            raise RuntimeError(f"hipcc failed with exit code {rc}: {c[-3]}")
+        if verbose and msgs:
+            print("\n".join(msgs))
+    tmp = LIB + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, msgs = _run(link)
+    if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and msgs:
-        print("\n".join(msgs))
+        raise RuntimeError(f"hipcc link failed with exit code {rc}")
     os.replace(tmp, LIB)
     return LIB
 

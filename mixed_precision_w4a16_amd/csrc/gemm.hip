@@ -2186,25 +2186,28 @@ extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
     return W4A16_OK;
 }
 
-extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params,
-                             void *C, int M, int K, int N, int group, int zero_points,
-                             void *workspace, void *stream)
+namespace {
+
+// Arguments of w4a16_gemm_ex other than the workspace, checked; the current device in *d.
+int check_gemm_args(const void *A, const uint32_t *packed, const uint16_t *params, void *C,
+                    int M, int K, int N, int group, int zero_points, DeviceInfo *d)
 {
-    if (!A || !packed || !params || !C || !workspace || (zero_points != 0 && zero_points != 1))
+    if (!A || !packed || !params || !C || (zero_points != 0 && zero_points != 1))
         return W4A16_EINVAL;
     int rc = check_gemm_shape(M, K, N);
     if (rc != W4A16_OK)
         return rc;
     if (group != kGroup && group != K)
         return W4A16_ESHAPE;
-    DeviceInfo d;
-    rc = current_device(&d);
-    if (rc != W4A16_OK)
-        return rc;
-    if (M == 0)
-        return W4A16_OK;
+    return current_device(d);
+}
 
-    const Config c = choose_config(M, K, N, d.cus);
+// The product with checked arguments, configuration c and a workspace of workspace_for(c)
+// bytes whose counter area is zero.
+int gemm_run(const Config &c, const void *A, const uint32_t *packed, const uint16_t *params,
+             void *C, int M, int K, int N, int group, int zero_points, void *workspace,
+             const DeviceInfo &d, void *stream)
+{
     // K = 128 makes the two scale granularities the same thing; take the grouped path
     const bool col = group != kGroup;
     Params p{};
@@ -2233,6 +2236,22 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     if (zero_points)
         return col ? dispatch<Fmt<true, true>>(c, p, s) : dispatch<Fmt<true, false>>(c, p, s);
     return col ? dispatch<Fmt<false, true>>(c, p, s) : dispatch<FmtSym>(c, p, s);
+}
+
+}  // namespace
+
+extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params,
+                             void *C, int M, int K, int N, int group, int zero_points,
+                             void *workspace, void *stream)
+{
+    if (!workspace)
+        return W4A16_EINVAL;
+    DeviceInfo d;
+    const int rc = check_gemm_args(A, packed, params, C, M, K, N, group, zero_points, &d);
+    if (rc != W4A16_OK || M == 0)
+        return rc;
+    return gemm_run(choose_config(M, K, N, d.cus), A, packed, params, C, M, K, N, group,
+                    zero_points, workspace, d, stream);
 }
 
 namespace {
@@ -2336,3 +2355,4 @@ extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t 
 {
     return w4a16_gemm_ex(A, packed, scales, C, M, K, N, kGroup, 0, workspace, stream);
 }
+

@@ -6,12 +6,20 @@
 //
 // Access pattern: each workgroup streams one contiguous chunk of the buffer, its 256 lanes
 // reading 4 KiB per step with 128-bit non-temporal loads, eight steps in flight.  Among the
-// patterns measured on MI355X this one reads fastest (about 7.1-7.2 TB/s over 4 GiB, against
-// 6.0-6.8 TB/s for grid-stride loops), so it serves as the achievable read rate.
+// patterns measured on MI355X this one reads fastest (6.80-6.85 TB/s over 4 GiB in every
+// recorded run, against 6.0-6.8 TB/s for grid-stride loops), so it serves as the achievable
+// read rate.
+//
+// The second probe times the matrix cores on operands that change from one instruction to
+// the next: each wave cycles eight independent fp32 accumulators through pairs of 16 operand
+// fragments loaded from a buffer of random fp16 values, so the multipliers see data like a
+// GEMM's (the sustained rate with random data is well below the rate with constant data: the
+// chip lowers its clock under the higher power).
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 #include "w4a16.h"
 #include "device.h"
@@ -55,7 +63,73 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u4 *__r
         out[blockIdx.x] = x;
 }
 
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// shape 0: 16x16x32 (acc 4 floats), 1: 32x32x16 (acc 16 floats).  Fragment f of lane l of
+// global wave w is 16-byte chunk ((w * 64 + l) * 16 + f) mod n16 of src.
+template <int SHAPE>
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(const u4 *__restrict__ src,
+                                                                   uint32_t n16, int iters,
+                                                                   float *__restrict__ out)
+{
+    const uint32_t gl = blockIdx.x * kProbeThreads + threadIdx.x;     // global lane
+    h8 a[8], b[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        a[f] = __builtin_bit_cast(h8, src[(gl * 16u + f) % n16]);
+        b[f] = __builtin_bit_cast(h8, src[(gl * 16u + 8 + f) % n16]);
+    }
+    using Acc = std::conditional_t<SHAPE == 0, f4, f16v>;
+    Acc acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = Acc{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (SHAPE == 0)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[(i + j) & 7], acc[i],
+                                                                    0, 0, 0);
+                else
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[(i + j) & 7], acc[i],
+                                                                    0, 0, 0);
+            }
+    }
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < (SHAPE == 0 ? 4 : 16); ++e)
+            x += acc[i][e];
+    out[gl] = x;
+}
+
 }  // namespace
+
+extern "C" int w4a16_mfma_probe(const void *src, size_t src_bytes, int shape, int workgroups,
+                                int iters, float *out, void *stream)
+{
+    if (!src || !out || src_bytes == 0 || src_bytes % 16 || (src_bytes >> 4) > 0xffffffffu ||
+        (reinterpret_cast<uintptr_t>(src) & 15) || workgroups <= 0 || iters <= 0 ||
+        (shape != 0 && shape != 1))
+        return W4A16_EINVAL;
+    w4a16_detail::DeviceInfo d;
+    const int rc = w4a16_detail::current_device(&d);
+    if (rc != W4A16_OK)
+        return rc;
+    const uint32_t n16 = static_cast<uint32_t>(src_bytes >> 4);
+    if (shape == 0)
+        hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3(workgroups), dim3(kProbeThreads), 0,
+                           static_cast<hipStream_t>(stream), static_cast<const u4 *>(src), n16,
+                           iters, out);
+    else
+        hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(workgroups), dim3(kProbeThreads), 0,
+                           static_cast<hipStream_t>(stream), static_cast<const u4 *>(src), n16,
+                           iters, out);
+    return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}
 
 extern "C" int w4a16_read_probe(const void *src, size_t bytes, uint32_t *out, void *stream)
 {

@@ -95,6 +95,20 @@ def _c(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(a)
 
 
+def default_threads() -> int:
+    """Threads for the C oracle when the caller names none: the cores this process may use,
+    capped by OMP_NUM_THREADS where the environment sets the process's CPU share.  (Any
+    count gives the same bits: each output is summed by one thread in a fixed order.)"""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
 def gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128, mode: str = "f32",
          nthreads: int = 0, zeros: np.ndarray | None = None) -> np.ndarray:
     """C = A @ Bhat with A fp16 [M, K], q uint8 [K, N], s fp16 [K/group, N] and optional zero
@@ -107,6 +121,8 @@ def gemm(A: np.ndarray, q: np.ndarray, s: np.ndarray, group: int = 128, mode: st
     if K2 != K or s.shape != (K // group, N):
         raise ValueError(f"shape mismatch A{A.shape} q{q.shape} s{s.shape} group={group}")
     C = np.empty((M, N), dtype=np.float16)
+    if nthreads <= 0:
+        nthreads = default_threads()
     if zeros is None:
         fn = {"f32": _load().oracle_gemm_f32, "f64": _load().oracle_gemm_f64}[mode]
         rc = fn(A.ctypes.data, q.ctypes.data, s.ctypes.data, M, K, N, group, C.ctypes.data,

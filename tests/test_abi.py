@@ -20,10 +20,20 @@ HEADER = os.path.join(ROOT, "include", "w4a16.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "paper_constants.json")
 
 
+def _header_code():
+    return re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+
+
+def header_inline_functions():
+    """Functions the header defines itself (static inline): evaluated by the caller, not
+    exported by the library."""
+    return sorted(set(re.findall(r"static\s+inline\s+[a-z_0-9 ]+?\b(w4a16_[a-z0-9_]+)\s*\(",
+                                 _header_code())))
+
+
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+    names = set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", _header_code()))
+    return sorted(names - set(header_inline_functions()))
 
 
 def test_library_exports_every_declared_function():
@@ -32,6 +42,44 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(w4.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_header_inline_workspace_bound_matches_the_binding(tmp_path):
+    # the header's w4a16_workspace_bound, compiled as C, against the binding's statement of
+    # the same formula, over shapes on both sides of every branch
+    assert header_inline_functions() == ["w4a16_workspace_bound"]
+    shapes = [(M, K, N) for M in (0, 1, 16, 17, 32, 33, 64, 65, 128, 129, 1024, -1)
+              for K, N in ((128, 64), (1024, 1024), (18432, 73728), (8192, 28672), (4096, 192),
+                           (100, 256), (0, 256))]
+    src = tmp_path / "bound.c"
+    src.write_text('#include <stdio.h>\n#include "w4a16.h"\nint main(void){\n' + "".join(
+        f'printf("%zu\\n", w4a16_workspace_bound({M}, {K}, {N}));\n' for M, K, N in shapes)
+        + "return 0;}\n")
+    exe = tmp_path / "bound"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [w4.workspace_bound(M, K, N) for M, K, N in shapes]
+    # values written out by hand: M = 1 on 1024 x 1024 is bounded by its 64 tiles of 16 x 256;
+    # M = 128 on the 72k x 18k weight by 1024 stripes of two 128 x 256 tiles
+    assert w4.workspace_bound(1, 1024, 1024) == 4096 + max(8 * 1024 * 8 * 16, (64 + 9) * 65536)
+    assert w4.workspace_bound(128, 18432, 73728) == 4096 + 2 * 1024 * 128 * 256 * 4
+    assert w4.workspace_bound(5, 1000, 256) == 0
+
+
+def test_mfma_probe_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(256)
+    assert lib.w4a16_mfma_probe(None, 4096, 0, 1, 1, d, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(d, 4096, 0, 1, 1, None, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(d, 0, 0, 1, 1, d, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(d, 4100, 0, 1, 1, d, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(ctypes.c_void_p(264), 4096, 0, 1, 1, d, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(d, 4096, 2, 1, 1, d, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(d, 4096, 0, 0, 1, d, None) == w4.EINVAL
+    assert lib.w4a16_mfma_probe(d, 4096, 1, 1, 0, d, None) == w4.EINVAL
 
 
 def test_status_strings():

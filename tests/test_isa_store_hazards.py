@@ -5,8 +5,9 @@ instruction (across a basic-block boundary the compiler did not pad) wrote one o
 registers, the store now and then sent the new value: element 0 of row block 7 of a 128-row
 piece went out as zero.  The kernels now keep wait states there; this test compiles every
 kernel source to gfx950 assembly with the library's own flags and checks that no store of
-three or four dwords has a data register written by a VALU instruction within the next two
-instructions without an s_nop or s_waitcnt in between.  Host-only: it needs hipcc, no GPU.
+three or four dwords has a data register written by a VALU or matrix instruction (one register
+or a register range) within the next two instructions without an s_nop or s_waitcnt in
+between.  Host-only: it needs hipcc, no GPU.
 """
 import os
 import re
@@ -48,11 +49,23 @@ def unpadded_store_data_writes(asm: str):
         for nxt in lines[k + 1:k + 3]:
             if nxt.startswith("s_nop") or nxt.startswith("s_waitcnt"):
                 break
-            w = re.match(r"v_\S+\s+v(\d+)\b", nxt)
-            if w and lo <= int(w[1]) <= hi:
+            d = vector_dest(nxt)
+            if d and d[0] <= hi and lo <= d[1]:
                 found.append((l, nxt))
                 break
     return found
+
+
+def vector_dest(line: str):
+    """The VGPR range (first, last) a VALU or matrix instruction writes, or None: a single
+    register (v_mov_b32 v2, ...), a range (v_mov_b64 v[2:3], ..., v_mfma_... v[0:3], ...)."""
+    w = re.match(r"v_\S+\s+v\[(\d+):(\d+)\]", line)
+    if w:
+        return int(w[1]), int(w[2])
+    w = re.match(r"v_\S+\s+v(\d+)\b", line)
+    if w:
+        return int(w[1]), int(w[1])
+    return None
 
 
 def test_scanner_flags_the_pattern_and_passes_padded_code():
@@ -62,6 +75,17 @@ def test_scanner_flags_the_pattern_and_passes_padded_code():
     assert len(unpadded_store_data_writes(bad)) == 1
     assert unpadded_store_data_writes(ok) == []
     assert unpadded_store_data_writes(other) == []
+    # writes of register ranges: a 64-bit move and a matrix instruction's destination
+    st = "buffer_store_dwordx4 v[2:5], v254, s[28:31], s1 offen sc1\n"
+    assert len(unpadded_store_data_writes(st + "v_mov_b64 v[4:5], 0\n")) == 1
+    assert len(unpadded_store_data_writes(st + "v_mov_b64 v[0:1], 0\n")) == 0
+    assert len(unpadded_store_data_writes(st + "v_mov_b64 v[0:1], 0\nv_mov_b64 v[0:1], 0\n")) == 0
+    assert len(unpadded_store_data_writes(
+        st + "s_add_u32 s0, s0, 4\nv_mfma_f32_16x16x32_f16 v[0:3], v[10:13], v[14:17], v[0:3]\n")) == 1
+    assert len(unpadded_store_data_writes(
+        st + "v_mfma_f32_16x16x32_f16 v[6:9], v[10:13], v[14:17], v[6:9]\n")) == 0
+    assert len(unpadded_store_data_writes(
+        "global_store_dwordx3 v0, v[2:4], s[0:1]\nv_mov_b64 v[3:4], 0\n")) == 1
 
 
 @pytest.mark.skipif(shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()),
