@@ -225,6 +225,24 @@ int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16_t *params,
                   void *stream);
 
 /*
+ * w4a16_gemm_ex with no workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * library keeps one scratch area per GPU in a device array of W4A16_NOALLOC_SCRATCH_BYTES
+ * (128 MiB + 4 KiB, reserved on each GPU the library runs on until the process ends); it
+ * covers every shape w4a16_gemm_ex accepts on MI355X.  Nothing is allocated: no hipMalloc,
+ * hipFree or allocating library call.  The first call on a GPU clears the scratch's counter
+ * area with a small kernel on `stream`; every call leaves it clear.
+ * All calls on one GPU share that GPU's scratch: calls that can overlap in time (two streams,
+ * two threads) race and give wrong results -- serialise them, or use w4a16_gemm_ex with a
+ * workspace each.  Other arguments, results (bit for bit the same as w4a16_gemm_ex's for the
+ * same inputs) and errors as w4a16_gemm_ex; a shape whose workspace would exceed the scratch
+ * (w4a16_workspace_size above W4A16_NOALLOC_SCRATCH_BYTES) is W4A16_ESHAPE.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (((size_t)128 << 20) + 4096)
+int w4a16_gemm_noalloc(const void *A, const uint32_t *packed, const uint16_t *params, void *C,
+                       int M, int K, int N, int group, int zero_points, void *stream);
+
+/*
  * 2:4-sparse weights (Sparse-MARLIN: MARLIN paper sec. 1 "Contribution" and sec. 2.1.1, the
  * 2:4 format of two non-zeros in every 4 consecutive weights with their positions as
  * metadata; deep-dive page, Sparse-MARLIN section: 4-bit non-zeros plus 2-bit positions, the

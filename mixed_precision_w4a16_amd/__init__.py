@@ -77,6 +77,8 @@ _lib.w4a16_read_probe.argtypes = [_p, ctypes.c_size_t, _p, _p]
 _lib.w4a16_read_probe.restype = _i
 _lib.w4a16_mfma_probe.argtypes = [_p, ctypes.c_size_t, _i, _i, _i, _p, _p]
 _lib.w4a16_mfma_probe.restype = _i
+_lib.w4a16_gemm_noalloc.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.w4a16_gemm_noalloc.restype = _i
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
 PACKED_ALONG_K, PACKED_ALONG_N = 0, 1
@@ -85,7 +87,8 @@ EXPORTED = ("w4a16_status_string", "w4a16_pack", "w4a16_unpack", "w4a16_pack_zp"
             "w4a16_unpack_zp", "w4a16_workspace_size", "w4a16_gemm", "w4a16_gemm_ex",
             "w4a16_repack", "w4a16_pack_24", "w4a16_unpack_24", "w4a16_gemm_24",
             "w4a16_moe_align", "w4a16_moe_gemm", "w4a16_moe_gemm_topk", "w4a16_read_probe",
-            "w4a16_mfma_probe")
+            "w4a16_mfma_probe", "w4a16_gemm_noalloc")
+NOALLOC_SCRATCH_BYTES = (128 << 20) + 4096
 
 
 class W4A16Error(RuntimeError):
@@ -297,6 +300,24 @@ def gemm(A, packed, params, N: int, out=None, ws=None, stream=None, group: int =
                                                        params.data_ptr(), out.data_ptr(), M, K,
                                                        N, group, int(bool(zero_points)),
                                                        ws.data_ptr(), stream.cuda_stream))
+    return out
+
+
+def gemm_noalloc(A, packed, params, N: int, out=None, stream=None, group: int = GROUP,
+                 zero_points: bool = False):
+    """gemm() through w4a16_gemm_noalloc: the library's own per-GPU scratch instead of a
+    workspace.  Calls that can overlap on one GPU (several streams or threads) race on that
+    scratch: serialise them.  Same arguments and result as gemm() without ws."""
+    import torch
+    M, K, out = _gemm_args(A, packed, params, N, out, group, zero_points)
+    if M == 0:
+        return out
+    with torch.cuda.device(A.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        _check("w4a16_gemm_noalloc", _lib.w4a16_gemm_noalloc(
+            A.data_ptr(), packed.data_ptr(), params.data_ptr(), out.data_ptr(), M, K, N, group,
+            int(bool(zero_points)), stream.cuda_stream))
     return out
 
 

@@ -2356,3 +2356,71 @@ extern "C" int w4a16_gemm(const void *A, const uint32_t *packed, const uint16_t 
     return w4a16_gemm_ex(A, packed, scales, C, M, K, N, kGroup, 0, workspace, stream);
 }
 
+// ------------------------------------------------------- entry point that allocates nothing
+//
+// w4a16_gemm_noalloc is w4a16_gemm_ex with the workspace taken from a file-scope device array
+// (one per GPU, held until the process ends), for callers that cannot allocate.  In host code
+// the array's name stands for a host-side shadow, not a device address: each device's address
+// is fetched once with hipGetSymbolAddress, with that device current, and only that address
+// is ever handed to a kernel.  The counter area starts at zero (a device global without an
+// initialiser is zero-filled when the code object loads, and the first call on a device
+// clears it again on the caller's stream with a small kernel, not a memset); every call
+// leaves it zero.  The partial slots need no clearing.
+constexpr size_t kScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes == kCounterBytes + (size_t(128) << 20), "counters + 128 MiB");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch[64];           // per device: the array's device address, once fetched
+
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    const int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n)
+        p[i] = 0u;
+}
+
+// This device's scratch address (fetching it, and clearing the counters on `stream`, on the
+// first call per device).
+int scratch_for_device(hipStream_t stream, void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return W4A16_EHIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return W4A16_EHIP;
+        constexpr int words = static_cast<int>(kCounterBytes / 4);
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(ptr), words);
+        if (hipGetLastError() != hipSuccess)
+            return W4A16_EHIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" int w4a16_gemm_noalloc(const void *A, const uint32_t *packed, const uint16_t *params,
+                                  void *C, int M, int K, int N, int group, int zero_points,
+                                  void *stream)
+{
+    DeviceInfo d;
+    const int rc = check_gemm_args(A, packed, params, C, M, K, N, group, zero_points, &d);
+    if (rc != W4A16_OK || M == 0)
+        return rc;
+    const Config c = choose_config(M, K, N, d.cus);
+    if (workspace_for(c) > kScratchBytes)
+        return W4A16_ESHAPE;
+    void *ws = nullptr;
+    const int rs = scratch_for_device(static_cast<hipStream_t>(stream), &ws);
+    if (rs != W4A16_OK)
+        return rs;
+    return gemm_run(c, A, packed, params, C, M, K, N, group, zero_points, ws, d, stream);
+}

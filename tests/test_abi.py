@@ -69,6 +69,19 @@ def test_header_inline_workspace_bound_matches_the_binding(tmp_path):
     assert w4.workspace_bound(5, 1000, 256) == 0
 
 
+def test_noalloc_gemm_rejects_bad_arguments_before_any_device_call():
+    lib = w4.library()
+    d = ctypes.c_void_p(16)
+    assert lib.w4a16_gemm_noalloc(None, d, d, d, 16, 1024, 1024, 128, 0, None) == w4.EINVAL
+    assert lib.w4a16_gemm_noalloc(d, None, d, d, 16, 1024, 1024, 128, 0, None) == w4.EINVAL
+    assert lib.w4a16_gemm_noalloc(d, d, d, d, -1, 1024, 1024, 128, 0, None) == w4.EINVAL
+    assert lib.w4a16_gemm_noalloc(d, d, d, d, 16, 1024, 1024, 128, 3, None) == w4.EINVAL
+    assert lib.w4a16_gemm_noalloc(d, d, d, d, 16, 1000, 1024, 128, 0, None) == w4.ESHAPE
+    assert lib.w4a16_gemm_noalloc(d, d, d, d, 16, 1024, 1000, 128, 0, None) == w4.ESHAPE
+    assert lib.w4a16_gemm_noalloc(d, d, d, d, 16, 1024, 1024, 256, 0, None) == w4.ESHAPE
+    assert w4.NOALLOC_SCRATCH_BYTES == (128 << 20) + 4096
+
+
 def test_mfma_probe_rejects_bad_arguments_before_any_device_call():
     lib = w4.library()
     d = ctypes.c_void_p(256)
