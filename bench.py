@@ -42,6 +42,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix
 GROUP = 128
 CALIB_BYTES = 512 << 20
+SETTLE_S = 1.0                  # untimed sweep before the warm-up steps (clock ramp)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
 
 # The kernel each M of the sweep runs (the library picks it from M: workgroups that own nine
@@ -722,6 +723,16 @@ def main():
         ncall[0] += 1
         w4.gemm(Ad[:M], p_, s_, N, out=outs[M], ws=ws, stream=stream)
 
+    # Settle: untimed sweep steps for SETTLE_S seconds before the W warm-up steps.  Under a
+    # sustained load the GPU's clocks take about a tenth of a second to reach their steady
+    # state; without this the first timed steps of a short run (5 warm-up steps are ~7 ms)
+    # run at the ramping clock.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for M in Ms:
+            call(M)
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         for M in Ms:
             call(M)
@@ -834,7 +845,7 @@ def main():
         log(f"cpu baseline: {cpu}")
     config = {"workload": LARGE.name, "K": K, "N": N, "M": list(Ms), "group": GROUP,
               "weights": "int4 codes + fp16 scales (4.125 bits/weight)",
-              "weight_copies_rotated": args.copies}
+              "weight_copies_rotated": args.copies, "untimed_settle_s": round(settle_s, 2)}
     details_path = None
     if args.details:
         os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)

@@ -337,13 +337,17 @@ template <int MB, class F>
 struct ScaleMode {
     static constexpr bool kWeights = !F::COL && (MB >= 4 || F::SP);
     static constexpr bool kPartial = !F::COL && MB < 4 && !F::SP;
+    // raw decode (raw8: no per-weight arithmetic) for the symmetric formats on 16- and 32-row
+    // tiles: the tile's sums of A * raw codes and of A * offsets are formed by two chains in
+    // the same order and subtracted, then scaled (per group) or added (one scale per column)
+    static constexpr bool kRaw = !F::ZP && !F::SP && MB <= 2;
 };
 
 template <int MB, int NBW, class F>
 __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const WQuad<F> (&wq)[NBW],
                                              const uint32_t (&pr)[TileRegs<NBW, F>::n],
                                              f4 (&acc)[MB][NBW], uint32_t mlo, uint32_t mhi,
-                                             uint32_t magic)
+                                             uint32_t magic, uint32_t magic_hi)
 {
     // Parameters first: converting them here ends the loaded registers' live range before
     // the next tile's loads reuse them (the empty asm keeps the conversion from being sunk).
@@ -375,7 +379,41 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const WQ
         for (int t = 0; t < 4; ++t)
             a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
 
-    if constexpr (F::SP) {
+    if constexpr (ScaleMode<MB, F>::kRaw) {
+        const h8 off = raw_offsets();
+        f4 P[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                P[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    a[mb][t], off, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : P[mb], 0, 0, 0);
+        f4 D[MB][NBW];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const h8 x = raw8(wq[b][t], mlo, mhi, magic, magic_hi);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    D[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        a[mb][t], x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb][b], 0, 0, 0);
+            }
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const f4 part = D[mb][b] - P[mb];
+                if constexpr (F::COL)
+                    acc[mb][b] += part;
+                else
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[mb][b][r] = __builtin_fmaf(sf[b], part[r], acc[mb][b][r]);
+                asm volatile("" : "+v"(acc[mb][b]));    // finish the update here
+            }
+        return;
+    } else if constexpr (F::SP) {
         // The transposed product on the sparse instruction (see the 2:4 kernel below): the
         // lane's decoded weights are the sparse operand (row = the lane's column), A fragments
         // 2h and 2h + 1 together are the dense operand of 64-k step h.
@@ -782,7 +820,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
 
     // dequant constants in VGPRs for v_and_or_b32
-    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+    const uint32_t mlo = in_vgpr(0x000f000fu), mhi = in_vgpr(0x00f000f0u);
+    const uint32_t magic = in_vgpr(0x64006400u);
+    const uint32_t magic_hi = in_vgpr(0x54005400u);   // raw decode of the high nibbles
 
     f4 acc[MB][NBW];
 #pragma unroll
@@ -886,7 +926,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
-        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic,
+                                 magic_hi);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
@@ -898,7 +939,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
-        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq1, sc1, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq1, sc1, acc, mlo, mhi, magic,
+                                 magic_hi);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         end_of_tile();
@@ -909,7 +951,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     }
     if (t < t1) {
         __syncthreads();
-        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic);
+        compute_tile<MB, NBW, F>(lds + st_cp * TL::kStageQuads, lane, wq0, sc0, acc, mlo, mhi, magic,
+                                 magic_hi);
         end_of_tile();
     }
     slice_end<MB, NBW, F>(p, rP, rC, rS, stripe, t0, t1 - 1, sigma, wave, lane, acc, nonown, own);
@@ -1072,7 +1115,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
         make_rsrc(p.partials, static_cast<uint32_t>(2u * p.W * TL::kSlotFloats * 4u));
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
-    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+    const uint32_t mlo = in_vgpr(0x000f000fu), mhi = in_vgpr(0x00f000f0u);
+    const uint32_t magic = in_vgpr(0x64006400u);
 
     f4 acc[MB][NBW];
 #pragma unroll
@@ -1256,8 +1300,12 @@ struct SkinnyBuf {
     uint32_t p[F::COL ? 1 : SkinnyGroups<NS>::n][F::ZP ? 4 : 2];   // per-group parameters
 };
 
-template <int MB, int NS, class F>
-__global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_kernel(Params p)
+// TWO: 32 rows at two workgroups per CU (weights of more than seven slabs per CU, symmetric
+// formats): the raw-decode chains are then formed one slab at a time, so that only one slab's
+// sums are live beside the running ones and the registers fit 256 per lane.
+template <int MB, int NS, class F, bool TWO = false>
+__global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm_skinny_kernel(
+    Params p)
 {
     using SG = SkinnyGroups<NS>;
     constexpr int NG = SG::n, NH = SG::nh;
@@ -1292,7 +1340,9 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
 
-    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+    const uint32_t mlo = in_vgpr(0x000f000fu), mhi = in_vgpr(0x00f000f0u);
+    const uint32_t magic = in_vgpr(0x64006400u);
+    const uint32_t magic_hi = in_vgpr(0x54005400u);   // raw decode of the high nibbles
 
     // byte offset of parameter block (group u, scale group gs); the lane's column adds c * PB
     auto par_soff = [&](int u, int gs) __attribute__((always_inline)) {
@@ -1399,7 +1449,7 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
         }
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            if constexpr (!F::COL) {
+            if constexpr (!F::COL && !TWO) {
                 sf[i] = half_bits_to_float(static_cast<uint16_t>(sh[i >> 1] >> (16 * (i & 1))));
                 asm volatile("" : "+v"(sf[i]));
             }
@@ -1420,7 +1470,76 @@ __global__ __launch_bounds__(kThreads, MB == 1 ? 2 : 1) void w4a16_gemm_skinny_k
                 zadd[i] = sym_zadd();
             }
         }
-        if constexpr (F::COL) {
+        if constexpr (!F::ZP) {
+            // Symmetric formats, raw decode: per row block the chain P sums A * offsets over
+            // the tile's four 32-k steps, per slab the chain D sums A * raw codes in the same
+            // order, and D - P is the tile's sum of A * (q - 8) (exactly 0 when every code is 8:
+            // the two chains then see the same values).  Per group it is scaled into the
+            // running sums; with one scale per column it is added, the scale coming at the end.
+            const h8 off = raw_offsets();
+            f4 P[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    P[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        b.a[mb][t], off, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : P[mb], 0, 0, 0);
+            if constexpr (TWO) {
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    f4 D[MB];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const h8 x = raw8(b.w[i][t], mlo, mhi, magic, magic_hi);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            D[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                b.a[mb][t], x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb], 0, 0, 0);
+                    }
+                    // (the scale converted here, where it is used: no nine live at once)
+                    float sfi = 1.0f;
+                    if constexpr (!F::COL)
+                        sfi = half_bits_to_float(
+                            static_cast<uint16_t>(sh[i >> 1] >> (16 * (i & 1))));
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const f4 part = D[mb] - P[mb];
+                        if constexpr (F::COL)
+                            acc[mb][i] += part;
+                        else
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                acc[mb][i][q] = __builtin_fmaf(sfi, part[q], acc[mb][i][q]);
+                        asm volatile("" : "+v"(acc[mb][i]));
+                    }
+                }
+                return;
+            }
+            f4 D[MB][NS];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    const h8 x = raw8(b.w[i][t], mlo, mhi, magic, magic_hi);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        D[mb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            b.a[mb][t], x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb][i], 0, 0, 0);
+                }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    const f4 part = D[mb][i] - P[mb];
+                    if constexpr (F::COL)
+                        acc[mb][i] += part;
+                    else
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[mb][i][q] = __builtin_fmaf(sf[i], part[q], acc[mb][i][q]);
+                    asm volatile("" : "+v"(acc[mb][i]));
+                }
+        } else if constexpr (F::COL) {
             // one scale per column: sum A * (q - z) over the whole K range, scale at the end
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -1639,7 +1758,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(p.C, static_cast<uint32_t>(p.M) * static_cast<uint32_t>(p.N) * 2u);
 
-    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u, magic = 0x64006400u;
+    const uint32_t mlo = in_vgpr(0x000f000fu), mhi = in_vgpr(0x00f000f0u);
+    const uint32_t magic = in_vgpr(0x64006400u);
     const uint32_t v_par = static_cast<uint32_t>(c) * 8;
     // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step
     uint32_t v_a[MB];
@@ -1801,10 +1921,13 @@ struct Config {
     int KS;          // the skinny kernel's K splits per slab group (1: none)
     int SMB;         // the skinny kernel's 16-row blocks (1, 2 or 4)
     int SP;          // the skinny kernel's row sub-problems (2 for M = 65..128)
+    bool TWO;        // the skinny kernel's 32-row form at two workgroups per CU
 };
 
 constexpr int kSkinnyMaxNS = 10;
 constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this many slabs
+constexpr int kSkinnyTwoMaxNS = 9;        // 32 rows at two per CU, symmetric formats
+constexpr int kSkinnyTwoMinNS = 7;
 
 // Skinny kernel (M <= 128, N a multiple of 256; 17..128 rows only in the one-per-CU regime
 // below, at most 4 slabs per workgroup above 32 rows, two 64-row sub-problems above 64).  Weights of up to 7 slabs per CU (N up to
@@ -1822,8 +1945,9 @@ constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this man
 // M = 1) unless K is split (choose_config), while on every shorter or wider weight measured
 // the skinny kernel is faster (1.1x to 4x).  Its dead loads point 2 GiB past the buffer
 // starts, so the weights and A must lie below that.
-int skinny_slabs(int M, int K, int N, int cus)
+int skinny_slabs(int M, int K, int N, int cus, bool zp, bool *two)
 {
+    *two = false;
     if (M > 128 || N % 256)
         return 0;
     const long long S = N / 16;
@@ -1835,7 +1959,14 @@ int skinny_slabs(int M, int K, int N, int cus)
     if (ns1 <= kSkinnyOneMaxNS) {
         ns = ns1;
     } else if (M > 16) {
-        return 0;                      // 32 rows: only at one workgroup per CU
+        // 32 rows on a larger weight: two workgroups per CU of seven to nine slabs, symmetric
+        // formats only (their raw decode leaves the registers for it).  Against the 32-row
+        // stripe tiles, measured in the same runs: 72k x 18k 142 vs 161 us at M = 17, 144 vs
+        // 155 at M = 24, a tie at 32; 8192 x 57344 52 vs 57 at M = 24.  With fewer slabs a
+        // wave's tiles are too light (8192 x 32768, four slabs: 47 vs 38 us at M = 32).
+        if (zp || ns > kSkinnyTwoMaxNS || ns < kSkinnyTwoMinNS)
+            return 0;
+        *two = true;
     } else if (M <= 8) {
         const long long ns3 = (S + 3LL * cus - 1) / (3LL * cus);
         if (ns3 >= 2 && ns3 <= 7)
@@ -1843,8 +1974,10 @@ int skinny_slabs(int M, int K, int N, int cus)
     }
     if (ns > kSkinnyMaxNS ||
         static_cast<uint64_t>(K) * static_cast<uint64_t>(N) / 2 >= kOutside ||
-        static_cast<uint64_t>(64) * static_cast<uint64_t>(K) * 2 >= kOutside)
+        static_cast<uint64_t>(64) * static_cast<uint64_t>(K) * 2 >= kOutside) {
+        *two = false;
         return 0;
+    }
     return static_cast<int>(ns);
 }
 
@@ -1954,7 +2087,7 @@ double tile_bytes(int MB, int NBW, bool sparse)
     return nt * kGroup * (sparse ? 0.375 : 0.5) + 16.0 * MB * kGroup * 2 + nt * 2;
 }
 
-Config choose_config(int M, int K, int N, int cus)
+Config choose_config(int M, int K, int N, int cus, bool zp)
 {
     Config c{};
     c.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -1985,11 +2118,13 @@ Config choose_config(int M, int K, int N, int cus)
     c.S = N / (16 * c.waves * c.NBW);
     c.T = static_cast<long long>(c.S) * c.P * c.G;
     c.W = choose_stripes(c.T, c.G, c.MB, tile_bytes(c.MB, c.NBW, false), cus);
-    c.NS = skinny_slabs(M, K, N, cus);
+    c.NS = skinny_slabs(M, K, N, cus, zp, &c.TWO);
     c.KS = 1;
     c.SMB = M > 32 ? 4 : (M > 16 ? 2 : 1);
     c.SP = M > 64 ? 2 : 1;
-    if (c.NS > 0) {
+    if (c.NS > 0 && c.TWO) {
+        c.W = (N / 16 + c.NS - 1) / c.NS;          // two per CU, no K split
+    } else if (c.NS > 0) {
         skinny_split(N / 16, c.G, M, c.SP, cus, c.NS, c.KS);
         const int wn = (N / 16 + c.NS - 1) / c.NS;
         if (c.NS == 1 && c.KS == 1 && c.G > 128)
@@ -2061,17 +2196,30 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int MB, int NS, class F>
+template <int MB, int NS, class F, bool TWO = false>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F>), dim3(p.W / (p.KS * p.SP), p.KS, p.SP),
-                       dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO>),
+                       dim3(p.W / (p.KS * p.SP), p.KS, p.SP), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <class F>
-hipError_t dispatch_skinny(int mb, int ns, const Params &p, hipStream_t s)
+hipError_t dispatch_skinny(int mb, int ns, bool two, const Params &p, hipStream_t s)
 {
+    if (two) {
+        if constexpr (!F::ZP) {
+            if (mb == 2) {
+                switch (ns) {
+                case 7: return launch_skinny<2, 7, F, true>(p, s);
+                case 8: return launch_skinny<2, 8, F, true>(p, s);
+                case 9: return launch_skinny<2, 9, F, true>(p, s);
+                default: break;
+                }
+            }
+        }
+        return hipErrorInvalidValue;
+    }
     if (mb == 4) {
         switch (ns) {
         case 1: return launch_skinny<4, 1, F>(p, s);
@@ -2114,7 +2262,7 @@ int dispatch(const Config &c, const Params &p, hipStream_t s)
 {
     hipError_t e;
     if (c.NS > 0) {
-        e = dispatch_skinny<F>(c.SMB, c.NS, p, s);
+        e = dispatch_skinny<F>(c.SMB, c.NS, c.TWO, p, s);
         return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
     }
     switch (c.MB * 10 + c.NBW) {
@@ -2179,9 +2327,14 @@ extern "C" int w4a16_workspace_size(int M, int K, int N, size_t *bytes)
     rc = current_device(&d);
     if (rc != W4A16_OK)
         return rc;
-    size_t b = M == 0 ? kCounterBytes : workspace_for(choose_config(M, K, N, d.cus));
-    if (M > 0 && N % 256 == 0)
-        b = std::max(b, workspace_for(choose_config_24(M, K, N, d.cus)));
+    // the most any format's choice of kernel needs
+    size_t b = kCounterBytes;
+    if (M > 0) {
+        b = std::max(workspace_for(choose_config(M, K, N, d.cus, false)),
+                     workspace_for(choose_config(M, K, N, d.cus, true)));
+        if (N % 256 == 0)
+            b = std::max(b, workspace_for(choose_config_24(M, K, N, d.cus)));
+    }
     *bytes = b;
     return W4A16_OK;
 }
@@ -2250,8 +2403,8 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
     const int rc = check_gemm_args(A, packed, params, C, M, K, N, group, zero_points, &d);
     if (rc != W4A16_OK || M == 0)
         return rc;
-    return gemm_run(choose_config(M, K, N, d.cus), A, packed, params, C, M, K, N, group,
-                    zero_points, workspace, d, stream);
+    return gemm_run(choose_config(M, K, N, d.cus, zero_points != 0), A, packed, params, C, M, K,
+                    N, group, zero_points, workspace, d, stream);
 }
 
 namespace {
@@ -2415,7 +2568,7 @@ extern "C" int w4a16_gemm_noalloc(const void *A, const uint32_t *packed, const u
     const int rc = check_gemm_args(A, packed, params, C, M, K, N, group, zero_points, &d);
     if (rc != W4A16_OK || M == 0)
         return rc;
-    const Config c = choose_config(M, K, N, d.cus);
+    const Config c = choose_config(M, K, N, d.cus, zero_points != 0);
     if (workspace_for(c) > kScratchBytes)
         return W4A16_ESHAPE;
     void *ws = nullptr;

@@ -44,14 +44,22 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x)
     return x;
 }
 
-// (a & m) | o in one VALU op.  gfx9 VOP3 encodings take no literal and read at most one
-// SGPR, so left to itself the compiler splits this into v_and + v_or; the "v" constraints
-// keep both constants in (loop-invariant) VGPRs instead.
+// A value the compiler must keep in a VGPR and cannot treat as a known constant.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// (a & m) | o in one VALU op (v_and_or_b32) when m and o are in VGPRs (in_vgpr): gfx9 VOP3
+// encodings take no literal and read at most one SGPR, so given two constants the compiler
+// would split it into v_and + v_or.  Written in C, not inline asm: a matrix instruction that
+// reads a VGPR as an operand needs two wait states after the VALU write of it, and the
+// compiler's hazard recognizer inserts them only for instructions it knows (an inline-asm
+// write right before the MFMA was read stale now and then).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o)
 {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-    return r;
+    return (a & m) | o;
 }
 
 // 8 codes -> 8 fp16 values q - z, in MFMA B-operand order (see pack.cpp for the nibbles).
@@ -96,6 +104,28 @@ __device__ __forceinline__ h8 dequant8_scaled(uint32_t w, h2 s, uint32_t mlo, ui
     r[0] = y0[0]; r[1] = y0[1]; r[2] = y1[0]; r[3] = y1[1];
     r[4] = y2[0]; r[5] = y2[1]; r[6] = y3[0]; r[7] = y3[1];
     return r;
+}
+
+// 8 codes -> raw fp16 values in MFMA B-operand order, 5 VALU ops (4 mask-and-OR, 1 shift) and
+// no arithmetic: codes 0, 1, 4, 5 (the low nibble of a byte, the last 4 mantissa bits) ORed into
+// the exponent field of 1024 (0x6400) read as 1024 + q; codes 2, 3, 6, 7 (the high nibble, 4
+// bits further up) ORed into the field of 64 (0x5400) read as 64 + q.  The matrix instruction
+// sums A * raw; the symmetric format's offsets, 1032 and 72 at those positions (raw8 of code 8
+// everywhere, raw_offsets() below), are summed against the same A by a second chain and
+// subtracted from the first (see the kernels).  mag_lo = 0x64006400, mag_hi = 0x54005400.
+__device__ __forceinline__ h8 raw8(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t mag_lo,
+                                   uint32_t mag_hi)
+{
+    const uint32_t w8 = w >> 8;
+    const u4 x = {and_or(w, mlo, mag_lo), and_or(w, mhi, mag_hi), and_or(w8, mlo, mag_lo),
+                  and_or(w8, mhi, mag_hi)};
+    return __builtin_bit_cast(h8, x);
+}
+
+// raw8 of eight codes 8: {1032, 1032, 72, 72, 1032, 1032, 72, 72}
+__device__ __forceinline__ h8 raw_offsets()
+{
+    return __builtin_bit_cast(h8, u4{0x64086408u, 0x54805480u, 0x64086408u, 0x54805480u});
 }
 
 // Decode constants (zsub, zadd) of the symmetric format, z = 8.

@@ -354,8 +354,9 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
         p.C, static_cast<uint32_t>(p.T) * static_cast<uint32_t>(p.topk) *
                  static_cast<uint32_t>(p.N) * 2u);
 
-    const uint32_t mlo = 0x000f000fu, mhi = 0x00f000f0u;
-    const uint32_t magic = BF ? 0x43004300u : 0x64006400u;
+    const uint32_t mlo = in_vgpr(0x000f000fu), mhi = in_vgpr(0x00f000f0u);
+    const uint32_t magic = in_vgpr(BF ? 0x43004300u : 0x64006400u);
+    const uint32_t magic_hi = in_vgpr(0x54005400u);   // fp16 raw decode of the high nibbles
     const uint32_t v_par = static_cast<uint32_t>(c) * PB;
     auto slab = [&](int i) __attribute__((always_inline)) {
         const int j = j0 + i;
@@ -485,6 +486,41 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
                         for (int q = 0; q < 4; ++q)
                             acc[mb][i][q] = __builtin_fmaf(
                                 sf[i], __builtin_fmaf(nz, rs[mb][q], part[mb][q]), acc[mb][i][q]);
+                        asm volatile("" : "+v"(acc[mb][i]));
+                    }
+                }
+            } else if constexpr (!ZP) {
+                // symmetric: the dense whole-K kernel's raw decode, the same arithmetic in the
+                // same order (per row block the chain of A * offsets, per slab the chain of
+                // A * raw codes, their difference scaled into the sums), so a row equals the
+                // dense product's bit for bit
+                const h8 off = raw_offsets();
+                f4 P[MB];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        P[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(h8, b.a[mb][t]), off,
+                            t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : P[mb], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    f4 D[MB];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const h8 x = raw8(b.w[i][t], mlo, mhi, magic, magic_hi);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            D[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(h8, b.a[mb][t]), x,
+                                t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const f4 part = D[mb] - P[mb];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[mb][i][q] = __builtin_fmaf(sf[i], part[q], acc[mb][i][q]);
                         asm volatile("" : "+v"(acc[mb][i]));
                     }
                 }

@@ -638,3 +638,45 @@ def test_mfma_probe_runs_on_random_operands():
         assert fl == 8 * 4 * 4 * 64 * (16384 if shape == 0 else 32768)
         assert torch.isfinite(out).all()
         assert out.abs().sum() > 0
+
+
+# ------------------------------------------------------------------ 32 rows, two per CU
+# M = 17..32 on weights of more than seven slabs per CU (symmetric formats): whole-K
+# workgroups of seven to nine slabs, two per CU, the raw-decode sums formed slab by slab.
+# N = 73472, 65536 and 57344 give 4592, 4096 and 3584 slabs (nine, eight and seven per
+# workgroup; the last workgroup of the first is two slabs short); K = 128 leaves three of four
+# waves without tiles.  N = 32768 (four slabs) takes the stripe kernel; the zero-point formats
+# take it everywhere; both are run too.
+@pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
+@pytest.mark.parametrize("K,N", [(1024, 32768), (256, 73472), (384, 65536), (128, 57344)])
+@pytest.mark.parametrize("M", [17, 24, 32])
+def test_32_row_two_per_cu_form_against_oracle(M, K, N, fmt):
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=M * 7 + K + N)
+        W, g, z = FmtWeights(q, s, 128), 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=M * 7 + K + N)
+        W = FmtWeights(q, s, g, z)
+    C = W.run(A)
+    check(C, oracle.gemm(A, q, s, group=g, zeros=z), f"two-per-CU {fmt} M={M} K={K} N={N}")
+    assert np.array_equal(bits(W.run(A)), bits(C))
+
+
+def test_32_row_two_per_cu_form_bit_exact_cases():
+    # one-hot rows, q = 8 everywhere and power-of-two scaling on the 9-slab form
+    K, N, M = 256, 73472, 32
+    _, q, s = draw(K, N, M, seed=91)
+    W = Weights(q, s)
+    A = np.zeros((M, K), dtype=np.float16)
+    ks = np.arange(M) * 7 % K
+    A[np.arange(M), ks] = 1.0
+    C = W.run(A)
+    want = (s[ks // 128].astype(np.float32) * (q[ks].astype(np.float32) - 8)).astype(np.float16)
+    assert same(C, want)
+    q8 = np.full_like(q, 8)
+    A2, _, _ = draw(K, N, M, seed=92)
+    assert (bits(Weights(q8, s).run(A2)) & 0x7FFF == 0).all()
+    C1 = W.run(A2).astype(np.float32)
+    C2 = W.run((A2.astype(np.float32) * 2).astype(np.float16)).astype(np.float32)
+    big = np.abs(C1) >= 2.0 ** -13
+    assert np.array_equal(C2[big], 2 * C1[big])

@@ -1,4 +1,5 @@
-"""The generated gfx950 code has no store-data race of the kind found in the split-slice pieces.
+"""The generated gfx950 code has no store-data race of the kind found in the split-slice pieces,
+and no matrix instruction reads an operand written right before it without wait states.
 
 A vector store of more than 64 bits reads its data registers after it issues.  When the next
 instruction (across a basic-block boundary the compiler did not pad) wrote one of those
@@ -7,7 +8,10 @@ piece went out as zero.  The kernels now keep wait states there; this test compi
 kernel source to gfx950 assembly with the library's own flags and checks that no store of
 three or four dwords has a data register written by a VALU or matrix instruction (one register
 or a register range) within the next two instructions without an s_nop or s_waitcnt in
-between.  Host-only: it needs hipcc, no GPU.
+between.  It also checks that every matrix instruction whose A or B operand register was
+written by a VALU instruction has at least two wait states after that write (the compiler
+inserts them for the instructions it knows; an inline-asm write feeding a matrix operand had
+none, and the instruction read stale values now and then).  Host-only: it needs hipcc, no GPU.
 """
 import os
 import re
@@ -68,6 +72,59 @@ def vector_dest(line: str):
     return None
 
 
+MFMA = re.compile(r"v_s?mfmac?_\S+\s+(.*)$")
+
+
+def _regs(op: str):
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", op)
+    if m:
+        return int(m[1]), int(m[2])
+    m = re.fullmatch(r"v(\d+)", op)
+    if m:
+        return int(m[1]), int(m[1])
+    return None
+
+
+def unpadded_mfma_operand_writes(asm: str, need: int = 2):
+    """Matrix instructions whose A or B operand was written by a VALU instruction fewer than
+    `need` wait states earlier (each instruction in between is one, s_nop n is n + 1),
+    within straight-line code.  The compiler pads such reads for the instructions it knows;
+    an inline-asm write right before the read is what this catches."""
+    lines = [l.split(";")[0].strip() for l in asm.splitlines()]
+    lines = [l for l in lines if l and not l.startswith(".")]
+    found = []
+    for k, l in enumerate(lines):
+        m = MFMA.match(l)
+        if not m or l.endswith(":"):
+            continue
+        ops = [o.strip() for o in m[1].split(",")]
+        srcs = [r for r in (_regs(o) for o in ops[1:3]) if r]
+        slots = 0
+        for prev in reversed(lines[max(0, k - need):k]):
+            if prev.endswith(":") or prev.startswith("s_cbranch") or prev.startswith("s_branch"):
+                break
+            if not MFMA.match(prev) and not prev.startswith("s_"):
+                d = vector_dest(prev)
+                if d and any(lo <= d[1] and d[0] <= hi for lo, hi in srcs):
+                    found.append((prev, l))
+                    break
+            n = re.match(r"s_nop\s+(\d+)", prev)
+            slots += int(n[1]) + 1 if n else 1
+            if slots >= need:
+                break
+    return found
+
+
+def test_mfma_scanner_flags_an_unpadded_operand_write():
+    mf = "v_mfma_f32_16x16x32_f16 v[0:3], v[4:7], v[8:11], v[0:3]\n"
+    assert len(unpadded_mfma_operand_writes("v_and_or_b32 v9, v1, v2, v3\n" + mf)) == 1
+    assert len(unpadded_mfma_operand_writes("v_and_or_b32 v5, v1, v2, v3\ns_waitcnt vmcnt(0)\n" + mf)) == 1
+    assert unpadded_mfma_operand_writes("v_and_or_b32 v9, v1, v2, v3\ns_nop 1\n" + mf) == []
+    assert unpadded_mfma_operand_writes("v_and_or_b32 v9, v1, v2, v3\ns_waitcnt vmcnt(0)\ns_nop 0\n" + mf) == []
+    assert unpadded_mfma_operand_writes("v_and_or_b32 v12, v1, v2, v3\n" + mf) == []
+    assert len(unpadded_mfma_operand_writes("v_mov_b64 v[6:7], 0\n" + mf)) == 1
+
+
 def test_scanner_flags_the_pattern_and_passes_padded_code():
     bad = "buffer_store_dwordx4 v[2:5], v254, s[28:31], s1 offen sc1\n.LBB0_1:\nv_mov_b32_e32 v2, 0\n"
     ok = "buffer_store_dwordx4 v[2:5], v254, s[28:31], s1 offen sc1\ns_nop 7\nv_mov_b32_e32 v2, 0\n"
@@ -97,6 +154,9 @@ def test_no_store_data_written_right_behind_a_wide_store():
             asms = list(ex.map(lambda s: device_asm(s, os.path.join(d, os.path.basename(s) + ".s")),
                                srcs))
     assert sum(len(STORE.findall(asm)) for asm in asms) > 1000     # the pieces' stores are there
+    assert sum(len(re.findall(r"v_mfma_", asm)) for asm in asms) > 10000
     for src, asm in zip(srcs, asms):
         found = unpadded_store_data_writes(asm)
+        assert not found, (os.path.basename(src), found[:3])
+        found = unpadded_mfma_operand_writes(asm)
         assert not found, (os.path.basename(src), found[:3])
