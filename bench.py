@@ -14,10 +14,12 @@ the same for every kernel of the sweep, the compute-bound ones against the fp16 
 `traffic` is the measured HBM bytes per launch from the committed counter runs, while the
 kernel source is the one they were taken on.
 
-The stdout line (kept to a few KB) also holds the per-M `sweep`, the compute-bound
-8192 x 28672 sweep at M = 256, 512, 1024 (`compute_sweep`), the measured stream-read and
-random-operand MFMA rates (`references`), the CPU baseline (the oracle on a column sample)
-and the run state (clocks, power cap and ECC state from sysfs, CPU model, core counts).
+The stdout line (kept to a few KB) also holds the per-M `sweep` (with each row's speed-up
+over torch.matmul on fp16 weights, hipBLASLt, the pages' comparison point: `x_fp16_gemm`),
+the compute-bound 8192 x 28672 sweep at M = 256, 512, 1024 (`compute_sweep`), the measured
+stream-read and random-operand MFMA rates (`references`), the CPU baseline (the oracle on a
+column sample) and the run state (clocks, power cap and ECC state from sysfs, CPU model, core
+counts).
 The rest goes to stderr and to the `--details` JSON file: the other packed formats, the
 load-time repack, the 2:4-sparse path, the MoE layers, the tensor-parallel rank and
 model-layer shapes, each with its fraction of the roofline bound.
@@ -51,7 +53,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
 KERNELS = [
     ("w4a16_gemm_skinny_kernel<1,6> (whole-K workgroups, 6 slabs, 3 per CU)", (1, 2, 4, 8), "hbm"),
     ("w4a16_gemm_skinny_kernel<1,9> (whole-K workgroups, 9 slabs, 2 per CU)", (16,), "hbm"),
-    ("w4a16_gemm_kernel<2,4> (32-row tiles)", (32,), "hbm"),
+    ("w4a16_gemm_skinny_kernel<2,9,two> (whole-K workgroups, 9 slabs, 32 rows, 2 per CU)", (32,),
+     "hbm"),
     ("w4a16_gemm_kernel<4,4> (64-row tiles)", (64,), "hbm"),
     ("w4a16_gemm_wide_kernel<4,2> (128-row tiles)", (128,), "mfma"),
 ]
@@ -427,6 +430,43 @@ def time_compute_sweep(w4, torch, dev, steps, stream):
     return rows
 
 
+def time_fp16_gemm(torch, dev, Ad, q, s, Ms, steps, stream, w4_us):
+    """The pages' comparison point (MARLIN paper, Figure 1; deep-dive page, "性能结果应该怎样读"):
+    the same product with uncompressed fp16 weights, torch.matmul (hipBLASLt) on a fp16 copy
+    of the dequantised weight, per M of the sweep, against the W4A16 call's time in this run.
+    The fp16 weight (K x N x 2 bytes, 2.7 GB on 72k x 18k) exceeds the memory-side cache."""
+    K, N = q.shape
+    g = torch.from_numpy(np.ascontiguousarray(s)).to(dev).float()
+    W = torch.empty((K, N), dtype=torch.float16, device=dev)
+    step = 2048
+    for k0 in range(0, K, step):            # dequantise on the GPU in K blocks
+        qk = torch.from_numpy(np.ascontiguousarray(q[k0:k0 + step])).to(dev).float()
+        W[k0:k0 + step] = (qk - 8.0).mul_(g[k0 // GROUP:(k0 + step) // GROUP].repeat_interleave(GROUP, 0)).half()
+        del qk
+    rows = []
+    for M in Ms:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+        for _ in range(3):
+            torch.matmul(Ad[:M], W, out=out)
+        evs = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.matmul(Ad[:M], W, out=out)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        rows.append({"M": M, "fp16_us": round(us, 2), "w4a16_us": w4_us[M],
+                     "speedup": round(us / w4_us[M], 3)})
+        log(f"fp16 torch.matmul M={M:4d} {us:8.1f} us   W4A16 {w4_us[M]:8.1f} us   "
+            f"speedup {us / w4_us[M]:.2f}x")
+    del W, g
+    torch.cuda.empty_cache()
+    return rows
+
+
 def time_shapes(w4, torch, dev, steps, stream, workload, tag):
     """Per-call time of every shape and M of a workload: back-to-back calls between one event
     pair, queued behind a spin so the host's launch rate does not set the time (these kernels
@@ -663,6 +703,97 @@ def compose_line(args, value, ms_per_step, config, kernels, sweep, cpu, refs, st
     return json.dumps(line, separators=(",", ":"))
 
 
+ABLATION_MS = (1, 16, 32, 64, 128)
+
+
+def run_ablation(args):
+    """The pages' Figure 12 on this chip: the shipped library against measurement-only builds
+    with one design choice undone each (build.py --ablation all), on the 72k x 18k weight,
+    every call of every build alternated so all see the same clock and cache state.  Prints
+    one JSON line of mean us per call and the ratio to the shipped build; checks that every
+    build's output equals the shipped one bit for bit (the switches change speed, not
+    results)."""
+    import ctypes
+    import torch
+    import mixed_precision_w4a16_amd as w4
+    from mixed_precision_w4a16_amd import build as B
+    from workloads import LARGE, draw
+    libs = {"shipped": w4.library()}
+    for name in B.ABLATIONS:
+        path = B.ablation_lib(name)
+        if not os.path.exists(path):
+            sys.exit(f"{path} is not built: python mixed_precision_w4a16_amd/build.py "
+                     "--ablation all")
+        lib = ctypes.CDLL(path)
+        lib.w4a16_gemm.argtypes = w4.library().w4a16_gemm.argtypes
+        lib.w4a16_gemm.restype = ctypes.c_int
+        libs[name] = lib
+    sh = LARGE.shapes[0]
+    K, N = sh.K, sh.N
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A, q, s = draw(K, N, max(ABLATION_MS), seed=0)
+    pd, sd = w4.to_device(*w4.pack(q, s), dev)
+    del q, s
+    copies = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(args.copies - 1)]
+    Ad = torch.from_numpy(A).to(dev)
+    ws = w4.new_workspace(max(ABLATION_MS), K, N, dev)
+    outs = {(v, M): torch.empty((M, N), dtype=torch.float16, device=dev)
+            for v in libs for M in ABLATION_MS}
+    stream = torch.cuda.current_stream(dev)
+    n = [0]
+
+    def call(v, M):
+        p_, s_ = copies[n[0] % len(copies)]
+        n[0] += 1
+        rc = libs[v].w4a16_gemm(Ad.data_ptr(), p_.data_ptr(), s_.data_ptr(),
+                                outs[(v, M)].data_ptr(), M, K, N, ws.data_ptr(),
+                                stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"{v}: w4a16_gemm returned {rc}")
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for M in ABLATION_MS:
+            for v in libs:
+                call(v, M)
+        torch.cuda.synchronize()
+    for M in ABLATION_MS:
+        ref = outs[("shipped", M)].cpu()
+        for v in libs:
+            if not torch.equal(outs[(v, M)].cpu().view(torch.int16), ref.view(torch.int16)):
+                raise RuntimeError(f"ablation build {v} differs from the shipped one at M={M}")
+    ev = {(v, M): [] for v in libs for M in ABLATION_MS}
+    for _ in range(args.steps):
+        for M in ABLATION_MS:
+            for v in libs:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call(v, M)
+                e1.record(stream)
+                ev[(v, M)].append((e0, e1))
+    torch.cuda.synchronize()
+    res = {}
+    for M in ABLATION_MS:
+        base = float(np.mean([a.elapsed_time(b) for a, b in ev[("shipped", M)]])) * 1e3
+        kern = next(k for k, ms, _ in KERNELS if M in ms)
+        row = {"kernel": kern, "shipped_us": round(base, 2),
+               "shipped_hbm_frac": round(algorithmic_bytes(M, K, N) / base / 1e3 / HBM_PEAK_GBPS, 4)}
+        for v in libs:
+            if v == "shipped":
+                continue
+            us = float(np.mean([a.elapsed_time(b) for a, b in ev[(v, M)]])) * 1e3
+            row[v] = {"us": round(us, 2), "time_vs_shipped": round(us / base, 3)}
+        res[M] = row
+        log(f"M={M:4d} shipped {base:7.1f} us  " + "  ".join(
+            f"{v} x{row[v]['time_vs_shipped']:.3f}" for v in libs if v != "shipped"))
+    print(json.dumps({"ablation": res, "workload": LARGE.name, "steps": args.steps,
+                      "weight_copies_rotated": args.copies,
+                      "builds": {v: os.path.basename(B.ablation_lib(v)) for v in B.ABLATIONS}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -684,11 +815,17 @@ def main():
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
                     help="file for the sections not in the stdout line ('' skips it)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the benchmark: the shipped library against the "
+                         "measurement-only builds (build.py --ablation all), M = 1..128")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.ablation:
+        run_ablation(args)
+        return
 
     host = host_state()
     import torch
@@ -831,6 +968,14 @@ def main():
         details["stream_read_reference"] = sref
         details["mfma_reference"] = mref
         compute_sweep = [{k: r[k] for k in ("M", "us", "TFLOPs", "mfma_frac")} for r in compute_sweep]
+    fp16 = None
+    if args.extra_steps > 0:
+        del copies
+        torch.cuda.empty_cache()
+        fp16 = time_fp16_gemm(torch, dev, Ad, q, s, Ms, args.extra_steps, stream,
+                              {r["M"]: r["us"] for r in sweep})
+        details["fp16_gemm_baseline"] = fp16
+        copies = [(pd, sd)] + [(pd.clone(), sd.clone()) for _ in range(args.copies - 1)]
     if args.format_steps > 0:
         details["formats"] = time_formats(w4, torch, dev, Ad, q, s, K, N, args.format_steps,
                                           max(2, args.warmup // 4), args.copies, stream, copies)
@@ -854,6 +999,9 @@ def main():
                        **details}, f, indent=1)
         details_path = os.path.relpath(os.path.abspath(args.details), ROOT)
         log(f"details written to {details_path}")
+    if fp16 is not None:
+        for row, f in zip(sweep, fp16):
+            row["x_fp16_gemm"] = f["speedup"]
     print(compose_line(args, round(value, 1), round(ms_per_step, 4), config, kernels, sweep, cpu,
                        refs, state, compute_sweep, details_path), flush=True)
 

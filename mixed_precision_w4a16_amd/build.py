@@ -45,14 +45,26 @@ def _run(cmd):
     return res.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
+ABLATIONS = ("cached_weights", "shallow", "no_swizzle")
+
+
+def ablation_lib(name: str) -> str:
+    """Path of a measurement-only build (see the W4A16_ABLATE_* switches in gemm.hip)."""
+    return os.path.join(PKG, f"libw4a16_ablate_{name}.so")
+
+
+def build(verbose: bool = False, ablation: str | None = None) -> str:
     """Compile each source to an object in parallel, then link libw4a16.so (the same flags as
-    command(), one compiler process per source)."""
+    command(), one compiler process per source).  ablation: one of ABLATIONS, for a
+    measurement-only library beside it (libw4a16_ablate_<name>.so)."""
     from concurrent.futures import ThreadPoolExecutor
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build" if ablation is None else f"_build_{ablation}")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
-    cmds = [[hipcc(), *flags(), "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    extra = [] if ablation is None else [f"-DW4A16_ABLATE_{ablation.upper()}"]
+    if ablation is not None and ablation not in ABLATIONS:
+        raise ValueError(f"unknown ablation {ablation!r}; one of {ABLATIONS}")
+    cmds = [[hipcc(), *flags(), *extra, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
     if verbose:
         for c in cmds:
             print(" ".join(c), flush=True)
@@ -64,7 +76,8 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed with exit code {rc}: {c[-3]}")
         if verbose and msgs:
             print("\n".join(msgs))
-    tmp = LIB + ".tmp"
+    out = LIB if ablation is None else ablation_lib(ablation)
+    tmp = out + ".tmp"
     link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
@@ -72,9 +85,18 @@ def build(verbose: bool = False) -> str:
     if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
         raise RuntimeError(f"hipcc link failed with exit code {rc}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--ablation", choices=ABLATIONS + ("all",),
+                    help="build a measurement-only library instead (all: each of them)")
+    a = ap.parse_args()
+    if a.ablation == "all":
+        for name in ABLATIONS:
+            print(build(verbose=True, ablation=name))
+    else:
+        print(build(verbose=True, ablation=a.ablation))

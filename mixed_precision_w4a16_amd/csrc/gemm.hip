@@ -72,6 +72,38 @@
 
 namespace {
 
+// Measurement-only builds, never the shipped library (build.py --ablation): the pages'
+// Figure 12 ablations as they map onto these kernels.
+//   W4A16_ABLATE_CACHED_WEIGHTS  weights loaded with the default cache policy, not streamed
+//                                (the pages' evict_first off)
+//   W4A16_ABLATE_SHALLOW         load pipelines one step shallower: the whole-K kernels keep
+//                                one tile of registers instead of two, the stripe kernel's A
+//                                ring has two stages instead of three (a second barrier per
+//                                tile keeps it safe) (the pages' pipeline depth 4 -> 2)
+//   W4A16_ABLATE_NO_SWIZZLE      A stored in LDS row-major, without the XOR swizzle
+#ifdef W4A16_ABLATE_CACHED_WEIGHTS
+constexpr int kWeightPolicy = 0;
+#else
+constexpr int kWeightPolicy = kNonTemporal;
+#endif
+#ifdef W4A16_ABLATE_SHALLOW
+constexpr int kLoadDepth = 1;             // whole-K kernels: tiles of registers in flight
+constexpr int kStripeStages = 2;          // stripe kernel: A ring stages
+#else
+constexpr int kLoadDepth = 2;
+constexpr int kStripeStages = 3;
+#endif
+// LDS position of 16-byte chunk c of A row r
+__device__ __forceinline__ int swz(int c, int r)
+{
+#ifdef W4A16_ABLATE_NO_SWIZZLE
+    (void)r;
+    return c;
+#else
+    return c ^ (r & 15);
+#endif
+}
+
 constexpr size_t kCounterBytes = 4096;        // fixed counter area at the workspace start
 constexpr int kMaxWGs = static_cast<int>(kCounterBytes / sizeof(int));
 
@@ -145,7 +177,7 @@ struct Tile {
     static constexpr int Mt = 16 * MB;                 // rows per M sub-problem
     static constexpr int Nt = 16 * NBW * WAVES;        // columns per slice
     static constexpr int kStageQuads = MB * 256;       // 16-byte LDS chunks per A stage
-    static constexpr int kStages = 3;                  // A ring depth (see the kernel loop)
+    static constexpr int kStages = kStripeStages;      // A ring depth (see the kernel loop)
     static constexpr int kSlotFloats = Mt * Nt;
 };
 
@@ -201,7 +233,7 @@ __device__ __forceinline__ void store_a(u4 *stage, int tid, const u4 (&ar)[MB])
     const int r = tid >> 4, c = tid & 15;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        stage[(16 * mb + r) * 16 + (c ^ r)] = ar[mb];
+        stage[(16 * mb + r) * 16 + swz(c, r)] = ar[mb];
 }
 
 // Per-column parameters of a wave's NBW slabs at one K step (its "scale group" sblk):
@@ -307,7 +339,7 @@ __device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffe
                                        int G, int lane, uint32_t wblk, uint32_t sblk,
                                        WQuad<F> (&wq)[NBW], uint32_t (&pr)[TileRegs<NBW, F>::n])
 {
-    constexpr int policy = ONCE ? kNonTemporal : 0;
+    constexpr int policy = ONCE ? kWeightPolicy : 0;
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
         const uint32_t blk = __builtin_amdgcn_readfirstlane(wblk + static_cast<uint32_t>(b * G));
@@ -377,7 +409,7 @@ __device__ __forceinline__ void compute_tile(const u4 *stage, int lane, const WQ
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
+            a[mb][t] = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + swz(4 * t + quad, row)]);
 
     if constexpr (ScaleMode<MB, F>::kRaw) {
         const h8 off = raw_offsets();
@@ -923,6 +955,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
     // next weight tile is requested.  The asm/scheduling barriers keep each tile's loads
     // after the last use of the registers they overwrite.
     while (t + 1 < t1) {
+        if constexpr (TL::kStages == 2)
+            __syncthreads();           // two stages: every wave is done with the one refilled
         store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
@@ -936,6 +970,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(Params p)
         st_cp = st_st;
         st_st = next_stage(st_st);
 
+        if constexpr (TL::kStages == 2)
+            __syncthreads();
         store_a<MB>(lds + st_st * TL::kStageQuads, tid, ar);  // A(t+1)
         load_a<MB>(rA, a_voff, lc.a_soff, ar);                // A(t+2)
         __syncthreads();
@@ -1009,7 +1045,7 @@ __device__ __forceinline__ void wide_dma_a(const Params &p, __amdgpu_buffer_rsrc
     uint32_t lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int c = (lane & 15) ^ ((4 * j + (lane >> 4)) & 15);
+        const int c = swz(lane & 15, 4 * j + (lane >> 4));
         lo[j] = (static_cast<uint32_t>(lane >> 4) * p.K + 8 * c) * 2;
     }
     const uint32_t row4 = static_cast<uint32_t>(p.K) * 8;         // 4 rows, in bytes
@@ -1059,7 +1095,7 @@ __device__ __forceinline__ void wide_compute(const u4 *stage, int lane,
         }
 #pragma unroll
         for (int mb = 0; mb < kWideMB; ++mb) {
-            const h8 a = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + ((4 * t + quad) ^ row)]);
+            const h8 a = __builtin_bit_cast(h8, stage[(16 * mb + row) * 16 + swz(4 * t + quad, row)]);
 #pragma unroll
             for (int b = 0; b < kWideNBW; ++b)
                 acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw[b], acc[mb][b], 0, 0, 0);
@@ -1290,7 +1326,7 @@ struct SkinnyGroups {
     static constexpr int nh = (NS + 1) / 2;  // dwords holding NS halves
     // tile buffers; deeper rings for few slabs measured no faster (the A loads, four per tile,
     // dominate the instruction stream there)
-    static constexpr int depth = 2;
+    static constexpr int depth = kLoadDepth;
 };
 
 template <int MB, int NS, class F>
@@ -1376,7 +1412,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         for (int i = 0; i < NS; ++i)
             b.w[i] = __builtin_bit_cast(
                 u4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rW, vw, (static_cast<uint32_t>(slab(i)) * p.G + gg) * 1024u, kNonTemporal));
+                        rW, vw, (static_cast<uint32_t>(slab(i)) * p.G + gg) * 1024u, kWeightPolicy));
         if constexpr (!F::COL) {
 #pragma unroll
             for (int k = 0; k < NG; ++k) {
@@ -1825,6 +1861,11 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p
         for (int i = 0; i < NS; ++i)
             acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
 
+    // The decoded weights are scaled in fp16 and the sparse instruction accumulates straight
+    // into the running sums, which are read only after the last tile.  (Per-tile sums started
+    // from zero in the accumulator and read right behind the instruction gave wrong results on
+    // gfx950: unlike the dense instruction, whose zero accumulator is an inline constant, the
+    // sparse one's accumulator is its destination register, written by a move just before.)
     auto compute = [&](const SparseBuf<MB, NS> &b) __attribute__((always_inline)) {
         uint32_t sh[NH];
         pick(b.p, sh);
@@ -2419,7 +2460,7 @@ hipError_t launch_sparse(const Params &p, hipStream_t stream)
 
 // Most slabs per workgroup each row-block count allows without spilling (1, 2, 4 blocks of
 // 16 rows hold 4, 8, 16 A registers per 32-k step and buffer).
-constexpr int kSparseMaxNS[3] = {8, 6, 3};
+constexpr int kSparseMaxNS[3] = {10, 6, 3};
 constexpr int kSparseWholeKRows = 16;   // more rows: the stripe kernel
 
 hipError_t dispatch_sparse(int mb, int ns, const Params &p, hipStream_t s)
@@ -2433,6 +2474,8 @@ hipError_t dispatch_sparse(int mb, int ns, const Params &p, hipStream_t s)
     case 22: return launch_sparse<1, 6>(p, s);
     case 23: return launch_sparse<1, 7>(p, s);
     case 24: return launch_sparse<1, 8>(p, s);
+    case 25: return launch_sparse<1, 9>(p, s);
+    case 26: return launch_sparse<1, 10>(p, s);
     case 33: return launch_sparse<2, 1>(p, s);
     case 34: return launch_sparse<2, 2>(p, s);
     case 35: return launch_sparse<2, 3>(p, s);

@@ -19,7 +19,8 @@ def _fake():
     args = types.SimpleNamespace(steps=50, warmup=20)
     Ms = (1, 2, 4, 8, 16, 32, 64, 128)
     sweep = [{"M": m, "us": 123456.78, "GBps": 12345.6, "hbm_frac": 0.12345, "TFLOPs": 1234.5,
-              "mfma_frac": 0.12345, "roofline_frac": 0.12345, "x_fp16_bound": 1.234} for m in Ms]
+              "mfma_frac": 0.12345, "roofline_frac": 0.12345, "x_fp16_bound": 1.234,
+              "x_fp16_gemm": 1.234} for m in Ms]
     kernels = [{"bound": "hbm", "achieved": 12345.6, "peak": 8000.0, "unit": "GB/s",
                 "frac": 0.12345, "traffic": 123456789012.5,
                 "kernel": name + " " * 40, "M": list(ms), "mean_launch_us": 123456.78}

@@ -115,6 +115,49 @@ def unpadded_mfma_operand_writes(asm: str, need: int = 2):
     return found
 
 
+def smfmac_accumulator_hazards(asm: str, before: int = 4, after: int = 10):
+    """Sparse matrix instructions (v_smfmac) whose accumulator -- their destination register,
+    read and written by the instruction -- was written by a VALU instruction within `before`
+    instructions before them, or is read by a non-matrix instruction within `after`
+    instructions behind them, in straight-line code.  Per-tile sums started from a zero moved
+    into the accumulator right before the instruction and read right behind it gave wrong
+    results on gfx950 with the compiler's own wait states; the kernels keep the sparse
+    instruction's accumulators loop-carried and read them only after the last tile."""
+    lines = [l.split(";")[0].strip() for l in asm.splitlines()]
+    lines = [l for l in lines if l and not l.startswith(".")]
+    found = []
+    for k, l in enumerate(lines):
+        if not l.startswith("v_smfmac"):
+            continue
+        d = _regs(l.split(None, 1)[1].split(",")[0].strip())
+        for prev in reversed(lines[max(0, k - before):k]):
+            if prev.endswith(":"):
+                break
+            w = vector_dest(prev)
+            if w and not MFMA.match(prev) and w[0] <= d[1] and d[0] <= w[1]:
+                found.append((prev, l))
+                break
+        for nxt in lines[k + 1:k + 1 + after]:
+            if nxt.endswith(":"):
+                break
+            if MFMA.match(nxt) or " " not in nxt:
+                continue
+            ops = [o.strip() for o in nxt.split(None, 1)[1].split(",")]
+            srcs = [r for r in (_regs(o) for o in (ops[1:] if nxt.startswith("v_") else ops)) if r]
+            if any(lo <= d[1] and d[0] <= hi for lo, hi in srcs):
+                found.append((l, nxt))
+                break
+    return found
+
+
+def test_smfmac_scanner_flags_fresh_and_early_read_accumulators():
+    sm = "v_smfmac_f32_16x16x64_f16 v[70:73], v[58:61], v[2:9], v40\n"
+    assert len(smfmac_accumulator_hazards("v_mov_b64_e32 v[70:71], s[28:29]\nv_lshrrev_b32 v1, 8, v2\n" + sm)) == 1
+    assert len(smfmac_accumulator_hazards(sm + "s_nop 7\nv_sub_f32_e32 v3, v73, v65\n")) == 1
+    assert smfmac_accumulator_hazards(sm + "v_smfmac_f32_16x16x64_f16 v[70:73], v[62:65], v[10:17], v38\n") == []
+    assert smfmac_accumulator_hazards("v_mov_b64_e32 v[80:81], 0\n" + sm + "v_add_f32 v3, v74, v65\n") == []
+
+
 def test_mfma_scanner_flags_an_unpadded_operand_write():
     mf = "v_mfma_f32_16x16x32_f16 v[0:3], v[4:7], v[8:11], v[0:3]\n"
     assert len(unpadded_mfma_operand_writes("v_and_or_b32 v9, v1, v2, v3\n" + mf)) == 1
@@ -159,4 +202,6 @@ def test_no_store_data_written_right_behind_a_wide_store():
         found = unpadded_store_data_writes(asm)
         assert not found, (os.path.basename(src), found[:3])
         found = unpadded_mfma_operand_writes(asm)
+        assert not found, (os.path.basename(src), found[:3])
+        found = smfmac_accumulator_hazards(asm)
         assert not found, (os.path.basename(src), found[:3])
