@@ -753,7 +753,7 @@ def run_ablation(args):
             raise RuntimeError(f"{v}: w4a16_gemm returned {rc}")
 
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < SETTLE_S:
+    while time.perf_counter() - t0 < args.settle_s:
         for M in ABLATION_MS:
             for v in libs:
                 call(v, M)
@@ -815,6 +815,9 @@ def main():
                     help="also run a plain fp16 copy kernel of known size (for counter scaling)")
     ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
                     help="file for the sections not in the stdout line ('' skips it)")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed sweep before the warm-up steps (0 under a counter "
+                         "profiler, where every dispatch is slow)")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the benchmark: the shipped library against the "
                          "measurement-only builds (build.py --ablation all), M = 1..128")
@@ -865,7 +868,7 @@ def main():
     # state; without this the first timed steps of a short run (5 warm-up steps are ~7 ms)
     # run at the ramping clock.
     t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < SETTLE_S:
+    while time.perf_counter() - t_settle < args.settle_s:
         for M in Ms:
             call(M)
         torch.cuda.synchronize()
