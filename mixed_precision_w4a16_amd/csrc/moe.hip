@@ -18,8 +18,9 @@
 //   expert in use, so the workgroups of the experts in use are dispatched first whichever
 //   experts they are.  Otherwise workgroup row e serves expert e, idle ones return at once.  Each lane gathers its own A row (row a / topk of A)
 //   and scatters its outputs to rows a of C, so no permuted copy of A or C is made.
-//   Experts with more rows than one block (16 MB) loop over blocks, re-reading the slab
-//   weights from cache.
+//   An expert's rows go through in passes of up to MBX 16-row blocks, each pass streaming
+//   the workgroup's slab weights once for all its blocks; the launch sizes MBX for the
+//   busiest expert expected, and each expert takes the fewest passes that cover its rows.
 // * fp16 activations: the dense kernels' exact decode (q - z in fp16 by mask-and-OR into
 //   the exponent 0x6400 and one packed add or FMA per pair), fp32 sums over each 128-row
 //   group, one scale FMA per output and group.
@@ -34,7 +35,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <climits>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 
@@ -278,13 +281,13 @@ __device__ __forceinline__ int kth_active_expert(const int *cnt, int E, int k, i
     return *out;
 }
 
-template <int MB, int NS, bool ZP, bool BF, bool RT>
+template <int MBX, int NS, bool ZP, bool BF, bool RT>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
 {
     using MG = MoeGroups<NS>;
     constexpr int NG = MG::n, NH = MG::nh;
     constexpr uint32_t PB = ZP ? 16 : 8;                 // parameter bytes per column and group
-    __shared__ f4 red[kWaves * MB * NS * 64];
+    __shared__ f4 red[kWaves * MBX * NS * 64];
     __shared__ int rlist[RT ? kRouteMax : 1];            // expert e's assignments (RT)
     __shared__ int wcnt[kWaves];
     __shared__ int ecnt[kMaxExperts];                    // rows per expert
@@ -379,7 +382,10 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
             out[m] = sel_half ? __builtin_amdgcn_alignbit(x[m + 1], x[m], 16) : x[m];
     };
 
-    for (int rb = 0; rb < rows; rb += 16 * MB) {
+    // One pass over the K tiles for the row blocks [rb, rb + 16 MB): each weight tile loaded
+    // feeds every row block of the pass.
+    auto pass = [&](auto mb_count, int rb) __attribute__((always_inline)) {
+        constexpr int MB = decltype(mb_count)::value;
         // the lane's A row in each 16-row block: token a / topk of assignment a
         uint32_t v_a[MB];
 #pragma unroll
@@ -623,7 +629,30 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
                 }
             }
         }
-        __syncthreads();                    // red is reused by the next row block
+        __syncthreads();                    // red is reused by the next pass
+    };
+
+    // Passes of MBX, MBX / 2 or one row block: while more rows are left than half the largest
+    // pass holds, the largest (so 17..32 rows take one pass of two blocks, 33..64 one of four,
+    // its blocks past the rows reading no memory), then the smallest that covers the rest.
+    for (int rb = 0; rb < rows;) {
+        const int left = rows - rb;
+        if constexpr (MBX >= 4) {
+            if (left > 32) {
+                pass(std::integral_constant<int, 4>{}, rb);
+                rb += 64;
+                continue;
+            }
+        }
+        if constexpr (MBX >= 2) {
+            if (left > 16) {
+                pass(std::integral_constant<int, 2>{}, rb);
+                rb += 32;
+                continue;
+            }
+        }
+        pass(std::integral_constant<int, 1>{}, rb);
+        rb += 16;
     }
 }
 
@@ -688,13 +717,19 @@ int moe_run(MoeParams &p, int zero_points, int act_dtype, bool routed, void *str
     if (T == 0)
         return W4A16_OK;
 
-    // Rows per block from the mean rows per expert (blocks sized for the busiest expert
-    // measure up to 2x slower: every block pays 4 A loads per 16 rows and 32-k step).  Four
-    // slabs per workgroup (as many weight loads per K step as A loads with 16-row blocks),
-    // fewer only while the experts in use -- at most min(E, T * topk) -- would not give
-    // every CU a workgroup.
-    const long long mean_rows = (static_cast<long long>(R) + E - 1) / E;
-    const int mb = mean_rows <= 16 ? 1 : (mean_rows <= 32 ? 2 : 4);
+    // Most row blocks per pass (mb): enough for the busiest expert expected, so that its
+    // weights are streamed once.  Under even routing the largest of E binomial counts of mean
+    // m lies near m + sqrt(2 m ln E); half that spread again allows for routers that favour
+    // some experts.  Each expert takes the fewest passes that cover its own rows (one 16-row
+    // pass for 16 rows or fewer, whatever mb is), but mb sets the kernel's registers: one
+    // block per pass leaves room for more workgroups per CU.  Four slabs per workgroup (as
+    // many weight loads per K step as A loads with 16-row blocks), two with 64-row passes
+    // (registers), fewer only while the experts in use -- at most min(E, T * topk) -- would
+    // not give every CU a workgroup.
+    const double mean_rows = static_cast<double>(R) / E;
+    const double busiest =
+        mean_rows + 1.5 * std::sqrt(2.0 * std::log(static_cast<double>(E)) * mean_rows);
+    const int mb = busiest <= 16.0 ? 1 : (busiest <= 32.0 ? 2 : 4);
     const long long S = N / 16;
     const long long active = std::min<long long>(E, static_cast<long long>(R));
     int ns = mb == 4 ? 2 : 4;

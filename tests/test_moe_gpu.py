@@ -142,6 +142,29 @@ def test_moe_against_oracle(E, topk, K, N, T, zp, act):
     assert torch.equal(W.run(d, routed=True), C)         # the routing entry: same bits
 
 
+# Experts with row counts on every side of the pass sizes: 8 experts at 16 mean rows take
+# passes of up to two 16-row blocks (0, 3, 16, 17, 32, 33 rows ...), 4 experts at 32 mean rows
+# passes of up to four (31, 33, 64 rows; 110 rows: a pass of four, then one more of four).
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("E,counts", [(8, [0, 3, 16, 17, 32, 33, 20, 7]),
+                                      (4, [0, 33, 64, 31]), (4, [1, 17, 110, 0])])
+def test_expert_row_counts_around_the_pass_sizes(E, counts, zp, act):
+    topk, K, N = 2, 512, 512
+    R = sum(counts)
+    T = R // topk
+    d = draw_moe(E, topk, K, N, T, seed=R + E + len(counts), act=act, zero_points=zp)
+    experts = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(E).shuffle(experts)
+    d["topk_ids"] = experts.reshape(T, topk)
+    W = Moe(d)
+    C = W.run(d)
+    want, done = ref(d)
+    assert done.all()
+    check(values(C), want, act, f"{act} zp={zp} E={E} rows per expert {counts}")
+    assert torch.equal(W.run(d, routed=True), C)
+
+
 @pytest.mark.parametrize("routed", [False, True])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_rows_of_no_expert_are_not_written(act, routed):
