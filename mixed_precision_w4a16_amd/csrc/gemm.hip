@@ -2029,11 +2029,18 @@ int skinny_slabs(int M, int K, int N, int cus, bool zp, bool *two)
 // 1.9 us + (0.90 + 0.057 NS) per tile + 3.4 us per split, with four (M = 33..64) 4.9 us +
 // (1.60 + 0.079 NS) per tile + 3.4 us per split (fitted to timings of K 1024..28672,
 // N 256..10240, NS 1..4, KS 1..8 on MI355X; past four slabs the model is too optimistic).  The
-// search keeps at most one workgroup per CU, up to 4 slabs and kSkinnyMaxKS splits (summed in
-// one load round), never below two tiles per wave, and leaves the one-per-CU choice only for a
-// predicted gain of 15%.  Measured: 8192 x 1280 at M = 16 10.3 -> 6.5-6.8 us, 11008 x 4096
-// 13.4 -> 9.6 us, 14336 x 2048 16.5 -> 8.4 us, 28672 x 1024 22 -> 10 us.  The counters bound
-// the slab groups.
+// search keeps at most one workgroup per CU and kSkinnyMaxKS splits (summed in one load
+// round), never below two tiles per wave, and leaves the one-per-CU choice only for a
+// predicted gain of 15%.  Up to 4 slabs, and where A has real rows (M = 9..16: 8 slabs;
+// M = 17..32: 5, the registers of two row blocks) more, but then only with at least 8 K tiles
+// a wave: more slabs per A fragment pay once the A loads carry data, short runs do not (at
+// M = 1 the 28672 x 8192 weight's 8 slabs x 4 splits ran 3% slower, and 11008 x 4096 at
+// M = 16 with 8 x 8, 2.7 tiles a wave, 11% slower).  Measured: 8192 x 1280 at M = 16 10.3 -> 6.5-6.8 us,
+// 11008 x 4096 13.4 -> 9.6 us, 14336 x 2048 16.5 -> 8.4 us, 28672 x 1024 22 -> 10 us; past
+// four slabs 28672 x 8192 at M = 12 / 16 25.7 -> 23.4 / 27.7 -> 23.9 us (8 slabs, 4 splits),
+// 8192 x 10240 at M = 16 / 24 / 32 13.4 -> 12.9 / 18.0 -> 16.3 / 20.4 -> 17.4 us (5, 2), the
+// other Llama-2 layer and rank shapes unchanged within 3%.  The counters bound the slab
+// groups.
 double skinny_model_us(int G, int NS, int KS, int M)
 {
     // fixed time, per-tile time a + b * NS, split cost; fitted per row range
@@ -2052,11 +2059,15 @@ void skinny_split(int S, int G, int M, int P, int cus, int &ns, int &ks)
     const double base = skinny_model_us(G, ns, 1, M);
     double best = 0.85 * base;
     const int ns0 = ns;
-    for (int n = ns0; n <= 4; n = n < 2 ? 2 : n + 2) {
+    const int nmax = M <= 8 ? 4 : (M <= 16 ? 8 : (M <= 32 ? 5 : 4));
+    for (int n = ns0; n <= nmax; n = n < 2 ? 2 : n + 2) {
         const int wn = (S + n - 1) / n;
         if (P * wn > kMaxWGs)
             continue;
-        const int kmax = std::min({kSkinnyMaxKS, cus / (P * wn), G / (2 * kWaves)});
+        // past four slabs only with at least 8 K tiles a wave (short runs of wide tiles
+        // measure slower than the model says)
+        const int kmax = std::min({kSkinnyMaxKS, cus / (P * wn), G / (2 * kWaves),
+                                   n > 4 ? std::max(1, G / (8 * kWaves)) : kSkinnyMaxKS});
         for (int k = 2; k <= kmax; ++k) {
             const double t = skinny_model_us(G, n, k, M);
             if (t < best) {

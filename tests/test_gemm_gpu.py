@@ -525,6 +525,25 @@ def test_whole_k_split_k_against_oracle(M, K, N, fmt):
     assert int(ws[:4096].count_nonzero()) == 0        # the counters are back at zero
 
 
+# More than four slabs per workgroup where A has real rows: 8192 x 10240 at M = 9..32 takes
+# 5 slabs and 2 splits, 28672 x 8192 at M = 9..16 8 slabs and 4 splits.
+@pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
+@pytest.mark.parametrize("K,N,M", [(8192, 10240, 12), (8192, 10240, 24), (8192, 10240, 32),
+                                   (28672, 8192, 16)])
+def test_whole_k_wide_slab_groups_against_oracle(K, N, M, fmt):
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=M + K + N + 2)
+        W, g, z = FmtWeights(q, s, 128), 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=M + K + N + 2)
+        W = FmtWeights(q, s, g, z)
+    ws = w4.workspace(M, K, N, torch.device("cuda"))
+    C = W.run(A, ws=ws)
+    check(C, oracle.gemm(A, q, s, group=g, zeros=z), f"wide slab groups {fmt} M={M} K={K} N={N}")
+    assert np.array_equal(bits(W.run(A, ws=ws)), bits(C))
+    assert int(ws[:4096].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("fmt", ["group128", "column_zeros"])
 def test_whole_k_split_k_one_hot_rows_are_bit_exact(fmt):
     # the other splits' pieces of a one-hot row are zeros: the sum is the one product
