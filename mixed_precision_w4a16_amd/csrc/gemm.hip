@@ -1324,9 +1324,6 @@ template <int NS>
 struct SkinnyGroups {
     static constexpr int n = (NS + 6) / 4;   // parameter groups NS slabs can touch
     static constexpr int nh = (NS + 1) / 2;  // dwords holding NS halves
-    // tile buffers; deeper rings for few slabs measured no faster (the A loads, four per tile,
-    // dominate the instruction stream there)
-    static constexpr int depth = kLoadDepth;
 };
 
 template <int MB, int NS, class F>
@@ -1339,7 +1336,7 @@ struct SkinnyBuf {
 // TWO: 32 rows at two workgroups per CU (weights of more than seven slabs per CU, symmetric
 // formats): the raw-decode chains are then formed one slab at a time, so that only one slab's
 // sums are live beside the running ones and the registers fit 256 per lane.
-template <int MB, int NS, class F, bool TWO = false>
+template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth>
 __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm_skinny_kernel(
     Params p)
 {
@@ -1622,7 +1619,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         // load in flight); the remaining tiles follow.  The empty asm statements fence memory,
         // so each buffer's loads are issued right after the compute that frees it and are not
         // sunk toward their use.
-        constexpr int D = SkinnyGroups<NS>::depth;
+        constexpr int D = DEPTH;
         SkinnyBuf<MB, NS, F> b[D];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -1963,12 +1960,14 @@ struct Config {
     int SMB;         // the skinny kernel's 16-row blocks (1, 2 or 4)
     int SP;          // the skinny kernel's row sub-problems (2 for M = 65..128)
     bool TWO;        // the skinny kernel's 32-row form at two workgroups per CU
+    bool DEEP;       // the skinny kernel with one more tile of registers in flight
 };
 
 constexpr int kSkinnyMaxNS = 10;
 constexpr int kSkinnyOneMaxNS = 7;        // one workgroup per CU up to this many slabs
 constexpr int kSkinnyTwoMaxNS = 9;        // 32 rows at two per CU, symmetric formats
 constexpr int kSkinnyTwoMinNS = 7;
+constexpr int kSkinnyDeepNS = 3;          // one more buffer at M <= 8 up to this many slabs
 
 // Skinny kernel (M <= 128, N a multiple of 256; 17..128 rows only in the one-per-CU regime
 // below, at most 4 slabs per workgroup above 32 rows, two 64-row sub-problems above 64).  Weights of up to 7 slabs per CU (N up to
@@ -2188,6 +2187,14 @@ Config choose_config(int M, int K, int N, int cus, bool zp)
         else
             c.W = wn * c.KS * c.SP;
     }
+    // At M <= 8 most A rows lie past M and read as zero without memory traffic, so with up
+    // to three slabs a wave's tile is little more than its weights: a third buffer, two weight
+    // tiles in flight instead of one, measured 2-8% faster there (M = 1 / 8: 4096 x 4096 5.5
+    // -> 5.2 / 6.0 -> 5.5 us, 8192 x 8192 9.5 -> 8.9 / 10.1 -> 10.0, 4096 x 12288 7.7 -> 7.5)
+    // and no faster with more slabs or real A rows (M = 16: up to 4% slower), nor where a
+    // wave walks only a few K tiles (1024 x 8192, two: 3.45 -> 3.7 us).
+    c.DEEP = c.NS > 0 && !c.TWO && c.SMB == 1 && M <= 8 && c.NS <= kSkinnyDeepNS &&
+             c.G >= 6 * kWaves * c.KS;
     return c;
 }
 
@@ -2248,17 +2255,28 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int MB, int NS, class F, bool TWO = false>
+template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO>),
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO, DEPTH>),
                        dim3(p.W / (p.KS * p.SP), p.KS, p.SP), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <class F>
-hipError_t dispatch_skinny(int mb, int ns, bool two, const Params &p, hipStream_t s)
+hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, const Params &p, hipStream_t s)
 {
+    if (deep) {
+        if (mb == 1) {
+            switch (ns) {
+            case 1: return launch_skinny<1, 1, F, false, kLoadDepth + 1>(p, s);
+            case 2: return launch_skinny<1, 2, F, false, kLoadDepth + 1>(p, s);
+            case 3: return launch_skinny<1, 3, F, false, kLoadDepth + 1>(p, s);
+            default: break;
+            }
+        }
+        return hipErrorInvalidValue;
+    }
     if (two) {
         if constexpr (!F::ZP) {
             if (mb == 2) {
@@ -2314,7 +2332,7 @@ int dispatch(const Config &c, const Params &p, hipStream_t s)
 {
     hipError_t e;
     if (c.NS > 0) {
-        e = dispatch_skinny<F>(c.SMB, c.NS, c.TWO, p, s);
+        e = dispatch_skinny<F>(c.SMB, c.NS, c.TWO, c.DEEP, p, s);
         return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
     }
     switch (c.MB * 10 + c.NBW) {

@@ -544,6 +544,27 @@ def test_whole_k_wide_slab_groups_against_oracle(K, N, M, fmt):
     assert int(ws[:4096].count_nonzero()) == 0
 
 
+# At M <= 8 with up to three slabs per workgroup and at least six K tiles a wave the whole-K
+# kernel keeps one more tile of registers in flight (three buffers): 8192 x 8192 (2 slabs),
+# 4096 x 12288 (3), 8192 x 1280 (slabs and K splits from the split search), 6144 x 256
+# (1 slab, K split).
+@pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
+@pytest.mark.parametrize("K,N", [(8192, 8192), (4096, 12288), (8192, 1280), (6144, 256)])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_whole_k_three_buffers_against_oracle(M, K, N, fmt):
+    if fmt == "group128":
+        A, q, s = draw(K, N, M, seed=M + K + N + 3)
+        W, g, z = FmtWeights(q, s, 128), 128, None
+    else:
+        A, q, s, g, z = fmt_case(fmt, K, N, M, seed=M + K + N + 3)
+        W = FmtWeights(q, s, g, z)
+    ws = w4.workspace(M, K, N, torch.device("cuda"))
+    C = W.run(A, ws=ws)
+    check(C, oracle.gemm(A, q, s, group=g, zeros=z), f"three buffers {fmt} M={M} K={K} N={N}")
+    assert np.array_equal(bits(W.run(A, ws=ws)), bits(C))
+    assert int(ws[:4096].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("fmt", ["group128", "column_zeros"])
 def test_whole_k_split_k_one_hot_rows_are_bit_exact(fmt):
     # the other splits' pieces of a one-hot row are zeros: the sum is the one product
