@@ -1319,6 +1319,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // where it would have to wait for everything.
 
 constexpr int kSkinnyMaxKS = 8;            // split-K pieces summed in one load round
+constexpr int kTrRowBlock = 16 * 17;       // 16-byte LDS chunks of one transposed row block
 
 template <int NS>
 struct SkinnyGroups {
@@ -1336,7 +1337,7 @@ struct SkinnyBuf {
 // TWO: 32 rows at two workgroups per CU (weights of more than seven slabs per CU, symmetric
 // formats): the raw-decode chains are then formed one slab at a time, so that only one slab's
 // sums are live beside the running ones and the registers fit 256 per lane.
-template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth>
+template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth, bool FL = false>
 __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm_skinny_kernel(
     Params p)
 {
@@ -1344,6 +1345,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
     constexpr int NG = SG::n, NH = SG::nh;
     constexpr uint32_t PB = F::ZP ? 16 : 8;              // bytes per column, group and K step
     __shared__ f4 red[kWaves * NS * 64];
+    __shared__ u4 atr[FL ? kWaves * MB * kTrRowBlock : 1];   // per-wave A transposes (FL)
     priority_by_dispatch_round(p.gens);
 
     const int tid = threadIdx.x;
@@ -1382,11 +1384,17 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         return (static_cast<uint32_t>(u) * p.Gs + gs) * (16u * PB);
     };
     const uint32_t v_par = static_cast<uint32_t>(c) * PB;
-    // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step
+    // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step.  FL:
+    // the load of step t brings rows 4t .. 4t + 3 of the block instead, 16 lanes a row, 16
+    // bytes each: whole 128-byte lines (the fragment layout touches 16 rows of 64 bytes, half
+    // of 16 lines, per load, and the vector L1 is the bottleneck of those loads once A has
+    // real rows); the wave puts them in fragment order through its own LDS region (compute).
     uint32_t v_a[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        v_a[mb] = (static_cast<uint32_t>(row0 + 16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
+        v_a[mb] = FL ? (static_cast<uint32_t>(row0 + 16 * mb + (lane >> 4)) * p.K + 8 * c) * 2
+                     : (static_cast<uint32_t>(row0 + 16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
+    const uint32_t rows4 = static_cast<uint32_t>(p.K) * 8;      // 4 rows of A, in bytes
     auto slab = [&](int i) __attribute__((always_inline)) {
         const int j = j0 + i;
         return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
@@ -1398,13 +1406,27 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         const uint32_t vp = live ? v_par : kOutside;
         const int gg = live ? g : g1 - 1;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (FL) {
+                // the row in the vector offset (rows past M fall outside the buffer: zeros);
+                // one base per row block, the four steps' offsets added at each load
+                uint32_t va = v_a[mb];
+                asm volatile("" : "+v"(va));
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                b.a[mb][t] = __builtin_bit_cast(
-                    h8, __builtin_amdgcn_raw_buffer_load_b128(
-                            rA, live ? v_a[mb] : kOutside,
-                            static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+                for (int t = 0; t < 4; ++t)
+                    b.a[mb][t] = __builtin_bit_cast(
+                        h8, __builtin_amdgcn_raw_buffer_load_b128(
+                                rA, live ? va + static_cast<uint32_t>(t) * rows4 : kOutside,
+                                static_cast<uint32_t>(gg * kGroup) * 2, 0));
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    b.a[mb][t] = __builtin_bit_cast(
+                        h8, __builtin_amdgcn_raw_buffer_load_b128(
+                                rA, live ? v_a[mb] : kOutside,
+                                static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < NS; ++i)
             b.w[i] = __builtin_bit_cast(
@@ -1471,7 +1493,25 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         for (int i = 0; i < NS; ++i)
             acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const SkinnyBuf<MB, NS, F> &b) __attribute__((always_inline)) {
+    auto compute = [&](SkinnyBuf<MB, NS, F> &b) __attribute__((always_inline)) {
+        if constexpr (FL) {
+            // rows 4t .. 4t + 3 of step t -> the wave's LDS region (rows of 17 chunks, so
+            // that the 16 rows read at one chunk lie in 16 different bank groups) -> back in
+            // fragment order, in place.  One wave writes and reads its own region: LDS
+            // operations of a wave complete in order, no barrier.
+            u4 *reg = atr + wave * (MB * kTrRowBlock);
+            const int rq = lane >> 4;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    reg[(16 * mb + 4 * t + rq) * 17 + c] = __builtin_bit_cast(u4, b.a[mb][t]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    b.a[mb][t] = __builtin_bit_cast(h8, reg[(16 * mb + c) * 17 + 4 * t + rq]);
+        }
         float sf[NS];
         h2 zsub[NS], zadd[NS];
         uint32_t sh[NH], zh[NH];
@@ -1961,6 +2001,7 @@ struct Config {
     int SP;          // the skinny kernel's row sub-problems (2 for M = 65..128)
     bool TWO;        // the skinny kernel's 32-row form at two workgroups per CU
     bool DEEP;       // the skinny kernel with one more tile of registers in flight
+    bool FL;         // the skinny kernel's whole-line A loads (M > 8)
 };
 
 constexpr int kSkinnyMaxNS = 10;
@@ -2195,6 +2236,11 @@ Config choose_config(int M, int K, int N, int cus, bool zp)
     // wave walks only a few K tiles (1024 x 8192, two: 3.45 -> 3.7 us).
     c.DEEP = c.NS > 0 && !c.TWO && c.SMB == 1 && M <= 8 && c.NS <= kSkinnyDeepNS &&
              c.G >= 6 * kWaves * c.KS;
+    // Whole-line A loads once A has real rows past the first few (M > 8; measured 2-18% faster
+    // at M = 16, e.g. 8192 x 8192 12.3 -> 10.1 us, 4096 x 12288 8.5 -> 7.9 us; 10% on 8192 x
+    // 57344 at M = 32), not at M <= 8 where the loads of dead rows cost nothing (3-6% slower
+    // with the LDS round trip), nor on the nine-slab 32-row form, whose registers are full.
+    c.FL = c.NS > 0 && M > 8 && !(c.TWO && c.NS == kSkinnyTwoMaxNS);
     return c;
 }
 
@@ -2255,23 +2301,25 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth>
+template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth, bool FL = false>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO, DEPTH>),
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO, DEPTH, FL>),
                        dim3(p.W / (p.KS * p.SP), p.KS, p.SP), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <class F>
-hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, const Params &p, hipStream_t s)
+hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, bool fl, const Params &p,
+                           hipStream_t s)
 {
+    constexpr int D = kLoadDepth;
     if (deep) {
         if (mb == 1) {
             switch (ns) {
-            case 1: return launch_skinny<1, 1, F, false, kLoadDepth + 1>(p, s);
-            case 2: return launch_skinny<1, 2, F, false, kLoadDepth + 1>(p, s);
-            case 3: return launch_skinny<1, 3, F, false, kLoadDepth + 1>(p, s);
+            case 1: return launch_skinny<1, 1, F, false, D + 1>(p, s);
+            case 2: return launch_skinny<1, 2, F, false, D + 1>(p, s);
+            case 3: return launch_skinny<1, 3, F, false, D + 1>(p, s);
             default: break;
             }
         }
@@ -2281,8 +2329,8 @@ hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, const Params &p,
         if constexpr (!F::ZP) {
             if (mb == 2) {
                 switch (ns) {
-                case 7: return launch_skinny<2, 7, F, true>(p, s);
-                case 8: return launch_skinny<2, 8, F, true>(p, s);
+                case 7: return launch_skinny<2, 7, F, true, D, true>(p, s);
+                case 8: return launch_skinny<2, 8, F, true, D, true>(p, s);
                 case 9: return launch_skinny<2, 9, F, true>(p, s);
                 default: break;
                 }
@@ -2290,24 +2338,40 @@ hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, const Params &p,
         }
         return hipErrorInvalidValue;
     }
+    // 17 rows and more: always the whole-line A loads
     if (mb == 4) {
         switch (ns) {
-        case 1: return launch_skinny<4, 1, F>(p, s);
-        case 2: return launch_skinny<4, 2, F>(p, s);
-        case 3: return launch_skinny<4, 3, F>(p, s);
-        case 4: return launch_skinny<4, 4, F>(p, s);
+        case 1: return launch_skinny<4, 1, F, false, D, true>(p, s);
+        case 2: return launch_skinny<4, 2, F, false, D, true>(p, s);
+        case 3: return launch_skinny<4, 3, F, false, D, true>(p, s);
+        case 4: return launch_skinny<4, 4, F, false, D, true>(p, s);
         default: return hipErrorInvalidValue;
         }
     }
     if (mb == 2) {
         switch (ns) {
-        case 1: return launch_skinny<2, 1, F>(p, s);
-        case 2: return launch_skinny<2, 2, F>(p, s);
-        case 3: return launch_skinny<2, 3, F>(p, s);
-        case 4: return launch_skinny<2, 4, F>(p, s);
-        case 5: return launch_skinny<2, 5, F>(p, s);
-        case 6: return launch_skinny<2, 6, F>(p, s);
-        case 7: return launch_skinny<2, 7, F>(p, s);
+        case 1: return launch_skinny<2, 1, F, false, D, true>(p, s);
+        case 2: return launch_skinny<2, 2, F, false, D, true>(p, s);
+        case 3: return launch_skinny<2, 3, F, false, D, true>(p, s);
+        case 4: return launch_skinny<2, 4, F, false, D, true>(p, s);
+        case 5: return launch_skinny<2, 5, F, false, D, true>(p, s);
+        case 6: return launch_skinny<2, 6, F, false, D, true>(p, s);
+        case 7: return launch_skinny<2, 7, F, false, D, true>(p, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (fl) {
+        switch (ns) {
+        case 1: return launch_skinny<1, 1, F, false, D, true>(p, s);
+        case 2: return launch_skinny<1, 2, F, false, D, true>(p, s);
+        case 3: return launch_skinny<1, 3, F, false, D, true>(p, s);
+        case 4: return launch_skinny<1, 4, F, false, D, true>(p, s);
+        case 5: return launch_skinny<1, 5, F, false, D, true>(p, s);
+        case 6: return launch_skinny<1, 6, F, false, D, true>(p, s);
+        case 7: return launch_skinny<1, 7, F, false, D, true>(p, s);
+        case 8: return launch_skinny<1, 8, F, false, D, true>(p, s);
+        case 9: return launch_skinny<1, 9, F, false, D, true>(p, s);
+        case 10: return launch_skinny<1, 10, F, false, D, true>(p, s);
         default: return hipErrorInvalidValue;
         }
     }
@@ -2332,7 +2396,7 @@ int dispatch(const Config &c, const Params &p, hipStream_t s)
 {
     hipError_t e;
     if (c.NS > 0) {
-        e = dispatch_skinny<F>(c.SMB, c.NS, c.TWO, c.DEEP, p, s);
+        e = dispatch_skinny<F>(c.SMB, c.NS, c.TWO, c.DEEP, c.FL, p, s);
         return e == hipSuccess ? W4A16_OK : W4A16_EHIP;
     }
     switch (c.MB * 10 + c.NBW) {
