@@ -2236,11 +2236,15 @@ Config choose_config(int M, int K, int N, int cus, bool zp)
     // wave walks only a few K tiles (1024 x 8192, two: 3.45 -> 3.7 us).
     c.DEEP = c.NS > 0 && !c.TWO && c.SMB == 1 && M <= 8 && c.NS <= kSkinnyDeepNS &&
              c.G >= 6 * kWaves * c.KS;
-    // Whole-line A loads once A has real rows past the first few (M > 8; measured 2-18% faster
-    // at M = 16, e.g. 8192 x 8192 12.3 -> 10.1 us, 4096 x 12288 8.5 -> 7.9 us; 10% on 8192 x
-    // 57344 at M = 32), not at M <= 8 where the loads of dead rows cost nothing (3-6% slower
-    // with the LDS round trip), nor on the nine-slab 32-row form, whose registers are full.
-    c.FL = c.NS > 0 && M > 8 && !(c.TWO && c.NS == kSkinnyTwoMaxNS);
+    // Whole-line A loads once A has real rows past the first few: measured 2-19% faster at
+    // M = 17..64 (3584 x 8192 at M = 32 10.1 -> 8.2 us, 8192 x 57344 57.1 -> 50.4 us) and at
+    // M = 9..16 where a wave walks at least 8 K tiles (8192 x 8192 12.1 -> 10.1 us, 8192 x
+    // 7168 11.9 -> 10.1 us); not at M <= 8, where the loads of dead rows cost nothing (3-6%
+    // slower with the LDS round trip), nor at M = 9..16 over fewer tiles (1024 x 8192 and
+    // 3584 x 8192 at M = 16: 4% slower), nor on the nine-slab 32-row form, whose registers
+    // are full.
+    c.FL = c.NS > 0 && (M > 16 || (M > 8 && c.G >= 8 * kWaves * c.KS)) &&
+           !(c.TWO && c.NS == kSkinnyTwoMaxNS);
     return c;
 }
 

@@ -205,6 +205,7 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float x)
 // writes its matches at its offset.  The list comes out in increasing order, as
 // w4a16_moe_align's, so both entries put the same rows in the same blocks.
 constexpr int kRouteMax = 2048;                          // assignments the routing entry takes
+constexpr int kTrRows = 16 * 17;                         // LDS chunks of one transposed block
 
 __device__ __forceinline__ int route_rows(const int32_t *__restrict__ ids, int R, int e, int wave,
                                           int lane, int *rlist, int *wcnt)
@@ -287,7 +288,9 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
     using MG = MoeGroups<NS>;
     constexpr int NG = MG::n, NH = MG::nh;
     constexpr uint32_t PB = ZP ? 16 : 8;                 // parameter bytes per column and group
-    __shared__ f4 red[kWaves * MBX * NS * 64];
+    // partial sums after the K loop; during it, the waves' A transposes (FL passes)
+    __shared__ u4 red_q[std::max(kWaves * MBX * NS * 64, kWaves * std::min(MBX, 2) * kTrRows)];
+    f4 *red = reinterpret_cast<f4 *>(red_q);
     __shared__ int rlist[RT ? kRouteMax : 1];            // expert e's assignments (RT)
     __shared__ int wcnt[kWaves];
     __shared__ int ecnt[kMaxExperts];                    // rows per expert
@@ -384,19 +387,31 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
 
     // One pass over the K tiles for the row blocks [rb, rb + 16 MB): each weight tile loaded
     // feeds every row block of the pass.
-    auto pass = [&](auto mb_count, int rb) __attribute__((always_inline)) {
+    auto pass = [&](auto mb_count, auto fl_flag, int rb) __attribute__((always_inline)) {
         constexpr int MB = decltype(mb_count)::value;
-        // the lane's A row in each 16-row block: token a / topk of assignment a
-        uint32_t v_a[MB];
+        // FL (passes of one block with more than 8 rows, or of two, over at least 8 K tiles a
+        // wave): the load of step t brings rows 4t .. 4t + 3 of a block, 16 lanes a row, as
+        // whole 128-byte lines, and the wave puts them in fragment order through its LDS
+        // region (compute), as the dense whole-K kernel does.  With up to 8 rows the fragment
+        // layout's loads of rows past the expert's touch no memory, and over few K tiles the
+        // LDS round trip's latency shows: there it would only cost (64 experts, K = 1408 and
+        // 2048: 1-4% slower); with four blocks the registers are full.
+        constexpr bool FL = decltype(fl_flag)::value;
+        static_assert(!FL || MB <= 2, "registers");
+        constexpr int NA = FL ? 4 : 1;
+        // the lane's A row (token a / topk of assignment a) per block (and step, FL)
+        uint32_t v_a[MB][NA];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int i = rb + 16 * mb + c;
-            v_a[mb] = kOutside;
-            if (i < rows) {
-                const int a = row_of(i);
-                v_a[mb] = (static_cast<uint32_t>(a / p.topk) * p.K + 8 * quad) * 2;
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int t = 0; t < NA; ++t) {
+                const int i = rb + 16 * mb + (FL ? 4 * t + quad : c);
+                v_a[mb][t] = kOutside;
+                if (i < rows) {
+                    const int a = row_of(i);
+                    v_a[mb][t] = (static_cast<uint32_t>(a / p.topk) * p.K + 8 * (FL ? c : quad)) * 2;
+                }
             }
-        }
 
         auto load = [&](MoeBuf<MB, NS, ZP, BF> &b, int g) __attribute__((always_inline)) {
             const bool live = g < g1;
@@ -409,8 +424,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
                 for (int t = 0; t < 4; ++t)
                     b.a[mb][t] = __builtin_bit_cast(
                         u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                rA, live ? v_a[mb] : kOutside,
-                                static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+                                rA, live ? v_a[mb][FL ? t : 0] : kOutside,
+                                static_cast<uint32_t>(gg * kGroup + (FL ? 0 : 32 * t)) * 2, 0));
 #pragma unroll
             for (int i = 0; i < NS; ++i)
                 b.w[i] = __builtin_bit_cast(
@@ -442,7 +457,23 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
             for (int i = 0; i < NS; ++i)
                 acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
 
-        auto compute = [&](const MoeBuf<MB, NS, ZP, BF> &b) __attribute__((always_inline)) {
+        auto compute = [&](MoeBuf<MB, NS, ZP, BF> &b) __attribute__((always_inline)) {
+            if constexpr (FL) {
+                // rows 4t .. 4t + 3 of step t -> the wave's region (rows of 17 chunks: the 16
+                // rows read at one chunk fall in 16 bank groups) -> fragment order, in place;
+                // a wave's LDS operations complete in order
+                u4 *reg = red_q + wave * (MB * kTrRows);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        reg[(16 * mb + 4 * t + quad) * 17 + c] = b.a[mb][t];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        b.a[mb][t] = reg[(16 * mb + c) * 17 + 4 * t + quad];
+            }
             uint32_t sh[NH], zh[NH];
             pick(b.p, 0, sh);
             if constexpr (ZP)
@@ -587,6 +618,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
                 compute(b[0]);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
+        if constexpr (FL)
+            __syncthreads();                // every wave is done with its transposes (red_q)
 
         // Partial sums meet in LDS; wave w finishes slabs w, w + 4, ...  Result lane l holds
         // rows 16 mb + 4(l/16) + 0..3 of the block, column 16j + l % 16.
@@ -635,23 +668,32 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_moe_kernel(MoeParams p)
     // Passes of MBX, MBX / 2 or one row block: while more rows are left than half the largest
     // pass holds, the largest (so 17..32 rows take one pass of two blocks, 33..64 one of four,
     // its blocks past the rows reading no memory), then the smallest that covers the rest.
+    using yes = std::true_type;
+    using no = std::false_type;
+    const bool fl_ok = p.G >= 8 * kWaves;             // at least 8 K tiles a wave
     for (int rb = 0; rb < rows;) {
         const int left = rows - rb;
         if constexpr (MBX >= 4) {
             if (left > 32) {
-                pass(std::integral_constant<int, 4>{}, rb);
+                pass(std::integral_constant<int, 4>{}, no{}, rb);
                 rb += 64;
                 continue;
             }
         }
         if constexpr (MBX >= 2) {
             if (left > 16) {
-                pass(std::integral_constant<int, 2>{}, rb);
+                if (fl_ok)
+                    pass(std::integral_constant<int, 2>{}, yes{}, rb);
+                else
+                    pass(std::integral_constant<int, 2>{}, no{}, rb);
                 rb += 32;
                 continue;
             }
         }
-        pass(std::integral_constant<int, 1>{}, rb);
+        if (left > 8 && fl_ok)
+            pass(std::integral_constant<int, 1>{}, yes{}, rb);
+        else
+            pass(std::integral_constant<int, 1>{}, no{}, rb);
         rb += 16;
     }
 }

@@ -144,16 +144,21 @@ def test_moe_against_oracle(E, topk, K, N, T, zp, act):
 
 # Experts with row counts on every side of the pass sizes: 8 experts at 16 mean rows take
 # passes of up to two 16-row blocks (0, 3, 16, 17, 32, 33 rows ...), 4 experts at 32 mean rows
-# passes of up to four (31, 33, 64 rows; 110 rows: a pass of four, then one more of four).
+# passes of up to four (31, 33, 64 rows; 110 rows: a pass of four, then one more of four), 16
+# experts at 3.6 mean rows passes of one (9, 12, 16 rows).  K = 4096 (8 K tiles a wave and
+# more) takes the whole-line A loads in passes of more than 8 rows, K = 512 the fragment-order
+# loads throughout.
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("K", [512, 4096])
 @pytest.mark.parametrize("E,counts", [(8, [0, 3, 16, 17, 32, 33, 20, 7]),
-                                      (4, [0, 33, 64, 31]), (4, [1, 17, 110, 0])])
-def test_expert_row_counts_around_the_pass_sizes(E, counts, zp, act):
-    topk, K, N = 2, 512, 512
+                                      (4, [0, 33, 64, 31]), (4, [1, 17, 110, 0]),
+                                      (16, [12, 16, 9, 8, 1, 0, 2, 0, 0, 3, 0, 5, 0, 0, 0, 2])])
+def test_expert_row_counts_around_the_pass_sizes(E, counts, K, zp, act):
+    topk, N = 2, 512
     R = sum(counts)
     T = R // topk
-    d = draw_moe(E, topk, K, N, T, seed=R + E + len(counts), act=act, zero_points=zp)
+    d = draw_moe(E, topk, K, N, T, seed=R + E + K + len(counts), act=act, zero_points=zp)
     experts = np.repeat(np.arange(E, dtype=np.int32), counts)
     np.random.default_rng(E).shuffle(experts)
     d["topk_ids"] = experts.reshape(T, topk)
@@ -161,7 +166,7 @@ def test_expert_row_counts_around_the_pass_sizes(E, counts, zp, act):
     C = W.run(d)
     want, done = ref(d)
     assert done.all()
-    check(values(C), want, act, f"{act} zp={zp} E={E} rows per expert {counts}")
+    check(values(C), want, act, f"{act} zp={zp} E={E} K={K} rows per expert {counts}")
     assert torch.equal(W.run(d, routed=True), C)
 
 
