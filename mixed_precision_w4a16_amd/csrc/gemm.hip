@@ -1327,25 +1327,32 @@ struct SkinnyGroups {
     static constexpr int nh = (NS + 1) / 2;  // dwords holding NS halves
 };
 
-template <int MB, int NS, class F>
+template <int MB, int NS, class F, bool DM = false>
 struct SkinnyBuf {
     u4 w[NS];                                // weight quads, one per slab
-    h8 a[MB][4];                             // A fragments of the 4 32-k steps per row block
+    h8 a[DM ? 1 : MB][DM ? 1 : 4];           // A of the 4 32-k steps per row block (not DM)
     uint32_t p[F::COL ? 1 : SkinnyGroups<NS>::n][F::ZP ? 4 : 2];   // per-group parameters
 };
 
 // TWO: 32 rows at two workgroups per CU (weights of more than seven slabs per CU, symmetric
 // formats): the raw-decode chains are then formed one slab at a time, so that only one slab's
 // sums are live beside the running ones and the registers fit 256 per lane.
-template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth, bool FL = false>
+template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth, bool FL = false,
+          bool DM = false>
 __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm_skinny_kernel(
     Params p)
 {
     using SG = SkinnyGroups<NS>;
+    using Buf = SkinnyBuf<MB, NS, F, DM>;
     constexpr int NG = SG::n, NH = SG::nh;
     constexpr uint32_t PB = F::ZP ? 16 : 8;              // bytes per column, group and K step
-    __shared__ f4 red[kWaves * NS * 64];
-    __shared__ u4 atr[FL ? kWaves * MB * kTrRowBlock : 1];   // per-wave A transposes (FL)
+    static_assert(!DM || FL, "the DMA form loads whole lines");
+    // DM: each wave's A tiles arrive by DMA into its own LDS buffers (DEPTH of them, one per
+    // register buffer), which the partial sums (red) reuse after the K loop
+    constexpr int kRed = kWaves * NS * 64, kDma = DM ? kWaves * DEPTH * MB * 256 : 0;
+    __shared__ u4 smem[kRed > kDma ? kRed : kDma];
+    f4 *red = reinterpret_cast<f4 *>(smem);
+    __shared__ u4 atr[(FL && !DM) ? kWaves * MB * kTrRowBlock : 1];   // per-wave A transposes
     priority_by_dispatch_round(p.gens);
 
     const int tid = threadIdx.x;
@@ -1388,7 +1395,11 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
     // the load of step t brings rows 4t .. 4t + 3 of the block instead, 16 lanes a row, 16
     // bytes each: whole 128-byte lines (the fragment layout touches 16 rows of 64 bytes, half
     // of 16 lines, per load, and the vector L1 is the bottleneck of those loads once A has
-    // real rows); the wave puts them in fragment order through its own LDS region (compute).
+    // real rows: its address path stalls for more than half of its busy cycles at M = 16 and
+    // 32); the wave puts them in fragment order through its own LDS region (compute).  DM:
+    // the same lines by DMA straight into the wave's LDS buffer of the tile, no registers in
+    // flight and no LDS stores (the nine-slab 32-row form and four row blocks, whose registers
+    // are full).
     uint32_t v_a[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -1400,14 +1411,32 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
     };
 
-    auto load = [&](SkinnyBuf<MB, NS, F> &b, int g) __attribute__((always_inline)) {
+    // DM: lane (rq, p) of the load of step t fetches chunk p ^ r of row r = 4t + rq of the
+    // block (the XOR swizzle applied on the global side: a DMA writes 64 consecutive chunks),
+    // so the 16 rows read at one chunk lie in 16 bank groups
+    const uint32_t cx16 = static_cast<uint32_t>(c ^ (lane >> 4)) * 16;
+    u4 *const dma_base = smem + wave * (DEPTH * MB * 256);
+    auto load = [&](Buf &b, int g, int d) __attribute__((always_inline)) {
         const bool live = g < g1;
         const uint32_t vw = live ? static_cast<uint32_t>(lane) * 16 : kOutside;
         const uint32_t vp = live ? v_par : kOutside;
         const int gg = live ? g : g1 - 1;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            if constexpr (FL) {
+            if constexpr (DM) {
+                uint32_t va = v_a[mb];
+                asm volatile("" : "+v"(va));
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rA,
+                        (__attribute__((address_space(3))) void *)(dma_base +
+                                                                   (d * MB + mb) * 256 + t * 64),
+                        16,
+                        live ? va + static_cast<uint32_t>(t) * rows4 + (cx16 ^ (64u * t)) - 16u * c
+                             : kOutside,
+                        static_cast<uint32_t>(gg * kGroup) * 2, 0, 0);
+            } else if constexpr (FL) {
                 // the row in the vector offset (rows past M fall outside the buffer: zeros);
                 // one base per row block, the four steps' offsets added at each load
                 uint32_t va = v_a[mb];
@@ -1493,8 +1522,23 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         for (int i = 0; i < NS; ++i)
             acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](SkinnyBuf<MB, NS, F> &b) __attribute__((always_inline)) {
-        if constexpr (FL) {
+    auto compute = [&](Buf &b, int d) __attribute__((always_inline)) {
+        h8 af[DM ? MB : 1][DM ? 4 : 1];
+        if constexpr (DM) {
+            // every load issued before the previous tile's is complete, so this tile's DMA
+            // has landed: at most one load call's instructions are outstanding
+            constexpr int kPerLoad = 4 * MB + NS + (F::COL ? 0 : NG);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerLoad));
+            asm volatile("" ::: "memory");
+            const u4 *src = dma_base + d * (MB * 256);
+            const int q = lane >> 4;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    af[mb][t] = __builtin_bit_cast(
+                        h8, src[(mb * 4 + (c >> 2)) * 64 + (c & 3) * 16 + ((4 * t + q) ^ c)]);
+        } else if constexpr (FL) {
             // rows 4t .. 4t + 3 of step t -> the wave's LDS region (rows of 17 chunks, so
             // that the 16 rows read at one chunk lie in 16 different bank groups) -> back in
             // fragment order, in place.  One wave writes and reads its own region: LDS
@@ -1512,6 +1556,12 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
                 for (int t = 0; t < 4; ++t)
                     b.a[mb][t] = __builtin_bit_cast(h8, reg[(16 * mb + c) * 17 + 4 * t + rq]);
         }
+        auto av = [&](int mb, int t) __attribute__((always_inline)) -> const h8 & {
+            if constexpr (DM)
+                return af[mb][t];
+            else
+                return b.a[mb][t];
+        };
         float sf[NS];
         h2 zsub[NS], zadd[NS];
         uint32_t sh[NH], zh[NH];
@@ -1556,7 +1606,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     P[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        b.a[mb][t], off, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : P[mb], 0, 0, 0);
+                        av(mb, t), off, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : P[mb], 0, 0, 0);
             if constexpr (TWO) {
 #pragma unroll
                 for (int i = 0; i < NS; ++i) {
@@ -1567,7 +1617,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb)
                             D[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                b.a[mb][t], x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb], 0, 0, 0);
+                                av(mb, t), x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb], 0, 0, 0);
                     }
                     // (the scale converted here, where it is used: no nine live at once)
                     float sfi = 1.0f;
@@ -1597,7 +1647,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
                         D[mb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            b.a[mb][t], x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb][i], 0, 0, 0);
+                            av(mb, t), x, t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : D[mb][i], 0, 0, 0);
                 }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -1621,7 +1671,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
                     const h8 x = dequant8(b.w[i][t], mlo, mhi, magic, zsub[i], zadd[i]);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
-                        acc[mb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.a[mb][t], x,
+                        acc[mb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av(mb, t), x,
                                                                             acc[mb][i], 0, 0, 0);
                 }
         } else {
@@ -1636,7 +1686,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
                     for (int mb = 0; mb < MB; ++mb) {
                         const f4 cin = t == 0 ? f4{0.f, 0.f, 0.f, 0.f} : part[mb][i];
                         part[mb][i] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(b.a[mb][t], x, cin, 0, 0, 0);
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(av(mb, t), x, cin, 0, 0, 0);
                     }
                 }
 #pragma unroll
@@ -1660,10 +1710,10 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         // so each buffer's loads are issued right after the compute that frees it and are not
         // sunk toward their use.
         constexpr int D = DEPTH;
-        SkinnyBuf<MB, NS, F> b[D];
+        Buf b[D];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            load(b[d], g0 + d);
+            load(b[d], g0 + d, d);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1672,10 +1722,10 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         for (int it = 0; it < rounds; ++it) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute(b[d]);
+                compute(b[d], d);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-                load(b[d], g + d + D);
+                load(b[d], g + d + D, d);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1684,10 +1734,13 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
 #pragma unroll
         for (int d = 0; d < D - 1; ++d)
             if (g + d < g1)
-                compute(b[d]);
-        // the loads past the run touch no memory, but their registers are still written
+                compute(b[d], d);
+        // the loads past the run touch no memory, but their registers (and, DM, the waves'
+        // LDS buffers) are still written
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    if constexpr (DM)
+        __syncthreads();                       // every wave is done with its A buffers (red)
 
     // The four waves' partial sums meet in LDS, one row block at a time; wave w then
     // finishes slabs w, w + 4, ...
@@ -2243,8 +2296,7 @@ Config choose_config(int M, int K, int N, int cus, bool zp)
     // slower with the LDS round trip), nor at M = 9..16 over fewer tiles (1024 x 8192 and
     // 3584 x 8192 at M = 16: 4% slower), nor on the nine-slab 32-row form, whose registers
     // are full.
-    c.FL = c.NS > 0 && (M > 16 || (M > 8 && c.G >= 8 * kWaves * c.KS)) &&
-           !(c.TWO && c.NS == kSkinnyTwoMaxNS);
+    c.FL = c.NS > 0 && (M > 16 || (M > 8 && c.G >= 8 * kWaves * c.KS));
     return c;
 }
 
@@ -2305,10 +2357,11 @@ hipError_t launch_wide(const Params &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth, bool FL = false>
+template <int MB, int NS, class F, bool TWO = false, int DEPTH = kLoadDepth, bool FL = false,
+          bool DM = false>
 hipError_t launch_skinny(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO, DEPTH, FL>),
+    hipLaunchKernelGGL((w4a16_gemm_skinny_kernel<MB, NS, F, TWO, DEPTH, FL, DM>),
                        dim3(p.W / (p.KS * p.SP), p.KS, p.SP), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
@@ -2335,20 +2388,22 @@ hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, bool fl, const P
                 switch (ns) {
                 case 7: return launch_skinny<2, 7, F, true, D, true>(p, s);
                 case 8: return launch_skinny<2, 8, F, true, D, true>(p, s);
-                case 9: return launch_skinny<2, 9, F, true>(p, s);
+                case 9: return launch_skinny<2, 9, F, true, D, true, true>(p, s);
                 default: break;
                 }
             }
         }
         return hipErrorInvalidValue;
     }
-    // 17 rows and more: always the whole-line A loads
+    // 17 rows and more: always the whole-line A loads; with four row blocks by DMA (their
+    // registers are full; 10-15% faster than through registers at M = 64 and 128, while with
+    // one row block the DMA form measured up to 14% slower at M = 16)
     if (mb == 4) {
         switch (ns) {
-        case 1: return launch_skinny<4, 1, F, false, D, true>(p, s);
-        case 2: return launch_skinny<4, 2, F, false, D, true>(p, s);
-        case 3: return launch_skinny<4, 3, F, false, D, true>(p, s);
-        case 4: return launch_skinny<4, 4, F, false, D, true>(p, s);
+        case 1: return launch_skinny<4, 1, F, false, D, true, true>(p, s);
+        case 2: return launch_skinny<4, 2, F, false, D, true, true>(p, s);
+        case 3: return launch_skinny<4, 3, F, false, D, true, true>(p, s);
+        case 4: return launch_skinny<4, 4, F, false, D, true, true>(p, s);
         default: return hipErrorInvalidValue;
         }
     }
