@@ -1857,12 +1857,13 @@ struct SparseBuf {
     uint32_t p[SkinnyGroups<NS>::n][2];      // four scales of the lane's column per group
 };
 
-template <int MB, int NS>
+template <int MB, int NS, bool FL = false>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p)
 {
     using SG = SkinnyGroups<NS>;
     constexpr int NG = SG::n, NH = SG::nh;
     __shared__ f4 red[kWaves * MB * NS * 64];
+    __shared__ u4 atr[FL ? kWaves * MB * kTrRowBlock : 1];   // per-wave A transposes (FL)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1887,11 +1888,15 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p
     const uint32_t mlo = in_vgpr(0x000f000fu), mhi = in_vgpr(0x00f000f0u);
     const uint32_t magic = in_vgpr(0x64006400u);
     const uint32_t v_par = static_cast<uint32_t>(c) * 8;
-    // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step
+    // A operand of row block mb: row 16 mb + c, k = 8 * (lane / 16) of each 32-k step; FL:
+    // whole-line loads of rows 4t .. 4t + 3 per step and a transpose in the wave's LDS
+    // region, as the dense whole-K kernel
     uint32_t v_a[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        v_a[mb] = (static_cast<uint32_t>(16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
+        v_a[mb] = FL ? (static_cast<uint32_t>(16 * mb + (lane >> 4)) * p.K + 8 * c) * 2
+                     : (static_cast<uint32_t>(16 * mb + c) * p.K + 8 * (lane >> 4)) * 2;
+    const uint32_t rows4 = static_cast<uint32_t>(p.K) * 8;      // 4 rows of A, in bytes
     auto slab = [&](int i) __attribute__((always_inline)) {
         const int j = j0 + i;
         return j < S ? j : S - 1;          // slabs past N re-read the last one; never stored
@@ -1903,13 +1908,18 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p
         const uint32_t vp = live ? v_par : kOutside;
         const int gg = live ? g : g1 - 1;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            uint32_t va = v_a[mb];
+            if constexpr (FL)
+                asm volatile("" : "+v"(va));
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 b.a[mb][t] = __builtin_bit_cast(
                     h8, __builtin_amdgcn_raw_buffer_load_b128(
-                            rA, live ? v_a[mb] : kOutside,
-                            static_cast<uint32_t>(gg * kGroup + 32 * t) * 2, 0));
+                            rA,
+                            live ? (FL ? va + static_cast<uint32_t>(t) * rows4 : va) : kOutside,
+                            static_cast<uint32_t>(gg * kGroup + (FL ? 0 : 32 * t)) * 2, 0));
+        }
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b96(
@@ -1956,7 +1966,21 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_gemm_sparse_kernel(Params p
     // from zero in the accumulator and read right behind the instruction gave wrong results on
     // gfx950: unlike the dense instruction, whose zero accumulator is an inline constant, the
     // sparse one's accumulator is its destination register, written by a move just before.)
-    auto compute = [&](const SparseBuf<MB, NS> &b) __attribute__((always_inline)) {
+    auto compute = [&](SparseBuf<MB, NS> &b) __attribute__((always_inline)) {
+        if constexpr (FL) {
+            u4 *reg = atr + wave * (MB * kTrRowBlock);
+            const int rq = lane >> 4;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    reg[(16 * mb + 4 * t + rq) * 17 + c] = __builtin_bit_cast(u4, b.a[mb][t]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    b.a[mb][t] = __builtin_bit_cast(h8, reg[(16 * mb + c) * 17 + 4 * t + rq]);
+        }
         uint32_t sh[NH];
         pick(b.p, sh);
 #pragma unroll
@@ -2602,11 +2626,11 @@ extern "C" int w4a16_gemm_ex(const void *A, const uint32_t *packed, const uint16
 
 namespace {
 
-template <int MB, int NS>
+template <int MB, int NS, bool FL = false>
 hipError_t launch_sparse(const Params &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((w4a16_gemm_sparse_kernel<MB, NS>), dim3(p.W), dim3(kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((w4a16_gemm_sparse_kernel<MB, NS, FL>), dim3(p.W), dim3(kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -2615,8 +2639,23 @@ hipError_t launch_sparse(const Params &p, hipStream_t stream)
 constexpr int kSparseMaxNS[3] = {10, 6, 3};
 constexpr int kSparseWholeKRows = 16;   // more rows: the stripe kernel
 
-hipError_t dispatch_sparse(int mb, int ns, const Params &p, hipStream_t s)
+hipError_t dispatch_sparse(int mb, int ns, bool fl, const Params &p, hipStream_t s)
 {
+    if (fl) {
+        switch (mb * 16 + ns) {
+        case 17: return launch_sparse<1, 1, true>(p, s);
+        case 18: return launch_sparse<1, 2, true>(p, s);
+        case 19: return launch_sparse<1, 3, true>(p, s);
+        case 20: return launch_sparse<1, 4, true>(p, s);
+        case 21: return launch_sparse<1, 5, true>(p, s);
+        case 22: return launch_sparse<1, 6, true>(p, s);
+        case 23: return launch_sparse<1, 7, true>(p, s);
+        case 24: return launch_sparse<1, 8, true>(p, s);
+        case 25: return launch_sparse<1, 9, true>(p, s);
+        case 26: return launch_sparse<1, 10, true>(p, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (mb * 16 + ns) {
     case 17: return launch_sparse<1, 1>(p, s);
     case 18: return launch_sparse<1, 2>(p, s);
@@ -2684,7 +2723,9 @@ extern "C" int w4a16_gemm_24(const void *A, const uint32_t *packed, const uint16
         p.P = 1;
         p.W = (S + ns - 1) / ns;
         p.gens = std::min(3, (p.W + d.cus - 1) / d.cus);
-        return dispatch_sparse(mb, ns, p, s) == hipSuccess ? W4A16_OK : W4A16_EHIP;
+        // whole-line A loads above 8 rows over at least 8 K tiles a wave (as the dense kernel)
+        const bool fl = mb == 1 && M > 8 && p.G >= 8 * kWaves;
+        return dispatch_sparse(mb, ns, fl, p, s) == hipSuccess ? W4A16_OK : W4A16_EHIP;
     }
     const Config c = choose_config_24(M, K, N, d.cus);
     p.P = c.P;
