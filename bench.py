@@ -52,9 +52,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_72kx18k.json")
 # 128-row tiles on this shape), and the roof that bounds it.
 KERNELS = [
     ("w4a16_gemm_skinny_kernel<1,6> (whole-K workgroups, 6 slabs, 3 per CU)", (1, 2, 4, 8), "hbm"),
-    ("w4a16_gemm_skinny_kernel<1,9> (whole-K workgroups, 9 slabs, 2 per CU)", (16,), "hbm"),
-    ("w4a16_gemm_skinny_kernel<2,9,two> (whole-K workgroups, 9 slabs, 32 rows, 2 per CU)", (32,),
-     "hbm"),
+    ("w4a16_gemm_skinny_kernel<1,9,fl> (whole-K workgroups, 9 slabs, 2 per CU, whole-line A)",
+     (16,), "hbm"),
+    ("w4a16_gemm_skinny_kernel<2,9,two,dma> (whole-K workgroups, 9 slabs, 32 rows, 2 per CU, "
+     "A lines by DMA)", (32,), "hbm"),
     ("w4a16_gemm_kernel<4,4> (64-row tiles)", (64,), "hbm"),
     ("w4a16_gemm_wide_kernel<4,2> (128-row tiles)", (128,), "mfma"),
 ]

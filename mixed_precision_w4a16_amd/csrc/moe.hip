@@ -716,6 +716,7 @@ hipError_t dispatch_moe(int mb, int ns, const MoeParams &p, int blocks, hipStrea
     case 33: return launch_moe<2, 1, ZP, BF, RT>(p, blocks, s);
     case 34: return launch_moe<2, 2, ZP, BF, RT>(p, blocks, s);
     case 36: return launch_moe<2, 4, ZP, BF, RT>(p, blocks, s);
+    case 38: return launch_moe<2, 6, ZP, BF, RT>(p, blocks, s);
     case 65: return launch_moe<4, 1, ZP, BF, RT>(p, blocks, s);
     case 66: return launch_moe<4, 2, ZP, BF, RT>(p, blocks, s);
     default: return hipErrorInvalidValue;
@@ -775,6 +776,12 @@ int moe_run(MoeParams &p, int zero_points, int act_dtype, bool routed, void *str
     const long long S = N / 16;
     const long long active = std::min<long long>(E, static_cast<long long>(R));
     int ns = mb == 4 ? 2 : 4;
+    // Passes of two blocks over many workgroups (at least two rounds of two per CU): six
+    // slabs, more weight bytes per A fragment, measured 9% faster (8 experts x 28672 wide at
+    // T = 64: 111 -> 101 us; 64 experts x 2816: 46.6 -> 42.3 us); with fewer workgroups six
+    // slabs leave CUs idle (8 experts x 4096 wide: 73 -> 81 us).
+    if (mb == 2 && active * ((S + 5) / 6) >= 4LL * d.cus)
+        ns = 6;
     while (ns > 1 && active * ((S + ns - 1) / ns) < d.cus)
         ns /= 2;
     p.G = K / kGroup;

@@ -170,6 +170,21 @@ def test_expert_row_counts_around_the_pass_sizes(E, counts, K, zp, act):
     assert torch.equal(W.run(d, routed=True), C)
 
 
+# Passes of two row blocks over at least two rounds of workgroups take six slabs per
+# workgroup: 8 experts x 28672 columns (299 slab groups each), 64 tokens, top 2.
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("zp", [False, True])
+def test_six_slab_passes_against_oracle(zp, act):
+    E, topk, K, N, T = 8, 2, 512, 28672, 64
+    d = draw_moe(E, topk, K, N, T, seed=77, act=act, zero_points=zp)
+    W = Moe(d)
+    C = W.run(d)
+    want, done = ref(d)
+    assert done.all()
+    check(values(C), want, act, f"six slabs {act} zp={zp}")
+    assert torch.equal(W.run(d, routed=True), C)
+
+
 @pytest.mark.parametrize("routed", [False, True])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_rows_of_no_expert_are_not_written(act, routed):
