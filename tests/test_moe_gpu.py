@@ -170,6 +170,22 @@ def test_expert_row_counts_around_the_pass_sizes(E, counts, K, zp, act):
     assert torch.equal(W.run(d, routed=True), C)
 
 
+# Few rows over a long K with at most a workgroup per CU: three register buffers (K = 8192, 64
+# K tiles: 16 a wave).
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("T", [1, 3])
+def test_three_buffer_passes_against_oracle(T, zp, act):
+    E, topk, K, N = 8, 2, 8192, 1024
+    d = draw_moe(E, topk, K, N, T, seed=78 + T, act=act, zero_points=zp)
+    W = Moe(d)
+    C = W.run(d)
+    want, done = ref(d)
+    assert done.all()
+    check(values(C), want, act, f"three buffers {act} zp={zp} T={T}")
+    assert torch.equal(W.run(d, routed=True), C)
+
+
 # Passes of two row blocks over at least two rounds of workgroups take six slabs per
 # workgroup: 8 experts x 28672 columns (299 slab groups each), 64 tokens, top 2.
 @pytest.mark.parametrize("act", ["f16", "bf16"])
