@@ -1522,13 +1522,18 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         for (int i = 0; i < NS; ++i)
             acc[mb][i] = f4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](Buf &b, int d) __attribute__((always_inline)) {
+    auto compute = [&](Buf &b, int d, bool tail) __attribute__((always_inline)) {
         h8 af[DM ? MB : 1][DM ? 4 : 1];
         if constexpr (DM) {
-            // every load issued before the previous tile's is complete, so this tile's DMA
-            // has landed: at most one load call's instructions are outstanding
+            // This tile's DMA has landed once at most the DEPTH - 1 load calls issued after
+            // its own are outstanding (in the loop; the tail waits for all): the vector
+            // memory counter completes in order
             constexpr int kPerLoad = 4 * MB + NS + (F::COL ? 0 : NG);
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerLoad));
+            static_assert((DEPTH - 1) * kPerLoad <= 63, "vmcnt range");
+            if (tail)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm((DEPTH - 1) * kPerLoad));
             asm volatile("" ::: "memory");
             const u4 *src = dma_base + d * (MB * 256);
             const int q = lane >> 4;
@@ -1722,7 +1727,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
         for (int it = 0; it < rounds; ++it) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                compute(b[d], d);
+                compute(b[d], d, false);
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
                 load(b[d], g + d + D, d);
@@ -1734,7 +1739,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
 #pragma unroll
         for (int d = 0; d < D - 1; ++d)
             if (g + d < g1)
-                compute(b[d], d);
+                compute(b[d], d, true);
         // the loads past the run touch no memory, but their registers (and, DM, the waves'
         // LDS buffers) are still written
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
