@@ -2303,10 +2303,14 @@ Config choose_config(int M, int K, int N, int cus, bool zp)
         const int wn = (N / 16 + c.NS - 1) / c.NS;
         if (c.NS == 1 && c.KS == 1 && c.G > 128)
             c.NS = 0;                  // one slab a workgroup over a long K: the stripe kernel
-        else if (M > 16 && c.G > (M > 32 ? 8 : 16) * kWaves * c.KS)
-            c.NS = 0;                  // 32 rows over more than 16 tiles a wave, 64 over more
-                                       // than 8: the stripe kernel (28672 x 8192 at M = 32:
-                                       // 37.2 vs 39.1 us; 8192 x 10240 at M = 64: 31.7 vs 36.1)
+        else if (M > 16 && c.G > (M > 32 ? 16 : 32) * kWaves * c.KS)
+            c.NS = 0;                  // 32 rows over more than 32 tiles a wave, 64 over more
+                                       // than 16: the stripe kernel (28672 x 8192 at M = 64,
+                                       // 28 tiles: 48.6 vs 51.1 us).  With A as whole lines
+                                       // (by DMA for four row blocks) shorter walks favour
+                                       // the whole-K kernel: 8192 x 10240 at M = 64, 16
+                                       // tiles, 24.6 vs 31.7 us; 28672 x 8192 at M = 32, 28
+                                       // tiles, 34.0 vs 36.1
         else
             c.W = wn * c.KS * c.SP;
     }
