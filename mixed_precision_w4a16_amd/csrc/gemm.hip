@@ -2093,7 +2093,8 @@ constexpr int kSkinnyTwoMinNS = 7;
 constexpr int kSkinnyDeepNS = 3;          // one more buffer at M <= 8 up to this many slabs
 
 // Skinny kernel (M <= 128, N a multiple of 256; 17..128 rows only in the one-per-CU regime
-// below, at most 4 slabs per workgroup above 32 rows, two 64-row sub-problems above 64).  Weights of up to 7 slabs per CU (N up to
+// below, at most 7 slabs per workgroup at 33..64 rows and 4 above, two 64-row sub-problems
+// above 64).  Weights of up to 7 slabs per CU (N up to
 // 28672 on 256 CUs) take the fewest slabs that leave at most one workgroup per CU: measured
 // on K 4096..8192, N 7168..28672 this beats two or three per CU by 1.1-1.5x (8192 x 10240 at
 // M = 16: 13.6 us with 3 slabs, 20.7 with 2; 8192 x 28672: 23.8 us with 7, 29.5 with 4); a
@@ -2117,8 +2118,11 @@ int skinny_slabs(int M, int K, int N, int cus, bool zp, bool *two)
     const long long P = M > 64 ? 2 : 1;   // 64-row sub-problems side by side
     long long ns = (S + 2LL * cus - 1) / (2LL * cus);
     const long long ns1 = (P * S + cus - 1) / cus;
-    if (M > 32 && ns1 > 4)
-        return 0;                      // 64 rows: only up to 4 slabs (registers)
+    // four row blocks: up to 7 slabs for one 64-row sub-problem (one workgroup per CU, so the
+    // accumulators may spill into the AGPRs: 4096 x 22016 at M = 64, 6 slabs, 29.3 -> 25.7 us
+    // against the stripe kernel, 8192 x 28672, 7 slabs, 53.6 -> 49.4), up to 4 for two
+    if (M > 32 && ns1 > (M > 64 ? 4 : kSkinnyOneMaxNS))
+        return 0;
     if (ns1 <= kSkinnyOneMaxNS) {
         ns = ns1;
     } else if (M > 16) {
@@ -2437,6 +2441,9 @@ hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, bool fl, const P
         case 2: return launch_skinny<4, 2, F, false, D, true, true>(p, s);
         case 3: return launch_skinny<4, 3, F, false, D, true, true>(p, s);
         case 4: return launch_skinny<4, 4, F, false, D, true, true>(p, s);
+        case 5: return launch_skinny<4, 5, F, false, D, true, true>(p, s);
+        case 6: return launch_skinny<4, 6, F, false, D, true, true>(p, s);
+        case 7: return launch_skinny<4, 7, F, false, D, true, true>(p, s);
         default: return hipErrorInvalidValue;
         }
     }
