@@ -2093,8 +2093,7 @@ constexpr int kSkinnyTwoMinNS = 7;
 constexpr int kSkinnyDeepNS = 3;          // one more buffer at M <= 8 up to this many slabs
 
 // Skinny kernel (M <= 128, N a multiple of 256; 17..128 rows only in the one-per-CU regime
-// below, at most 7 slabs per workgroup at 33..64 rows and 4 above, two 64-row sub-problems
-// above 64).  Weights of up to 7 slabs per CU (N up to
+// below, two 64-row sub-problems above 64 rows).  Weights of up to 7 slabs per CU (N up to
 // 28672 on 256 CUs) take the fewest slabs that leave at most one workgroup per CU: measured
 // on K 4096..8192, N 7168..28672 this beats two or three per CU by 1.1-1.5x (8192 x 10240 at
 // M = 16: 13.6 us with 3 slabs, 20.7 with 2; 8192 x 28672: 23.8 us with 7, 29.5 with 4); a
@@ -2118,10 +2117,12 @@ int skinny_slabs(int M, int K, int N, int cus, bool zp, bool *two)
     const long long P = M > 64 ? 2 : 1;   // 64-row sub-problems side by side
     long long ns = (S + 2LL * cus - 1) / (2LL * cus);
     const long long ns1 = (P * S + cus - 1) / cus;
-    // four row blocks: up to 7 slabs for one 64-row sub-problem (one workgroup per CU, so the
-    // accumulators may spill into the AGPRs: 4096 x 22016 at M = 64, 6 slabs, 29.3 -> 25.7 us
-    // against the stripe kernel, 8192 x 28672, 7 slabs, 53.6 -> 49.4), up to 4 for two
-    if (M > 32 && ns1 > (M > 64 ? 4 : kSkinnyOneMaxNS))
+    // four row blocks: up to 7 slabs per 64-row sub-problem (one workgroup per CU, so the
+    // accumulators may spill into the AGPRs), measured against the stripe and 128-row kernels:
+    // 4096 x 22016 at M = 64, 6 slabs, 29.3 -> 25.7 us; 8192 x 28672, 7 slabs, 53.6 -> 49.4;
+    // two sub-problems, 4096 x 12288 at M = 128, 6 slabs, 27.7 -> 24.8; 8192 x 10240, 5,
+    // 41.7 -> 38.6
+    if (M > 32 && ns1 > kSkinnyOneMaxNS)
         return 0;
     if (ns1 <= kSkinnyOneMaxNS) {
         ns = ns1;

@@ -529,12 +529,13 @@ def test_whole_k_split_k_against_oracle(M, K, N, fmt):
 # 5 slabs and 2 splits, 28672 x 8192 at M = 9..16 8 slabs and 4 splits; longer walks of the
 # whole-K kernel: 28672 x 8192 at M = 32 (two row blocks, 28 tiles a wave), 8192 x 10240 at
 # M = 40 and 64 (four row blocks by DMA, 16 tiles a wave); four row blocks over 5, 6 and 7
-# slabs: 4096 x 20480, 4096 x 22016, 8192 x 28672.
+# slabs: 4096 x 20480, 4096 x 22016, 8192 x 28672; two 64-row sub-problems of 6 and 5 slabs:
+# 4096 x 12288 at M = 96, 8192 x 10240 at M = 128.
 @pytest.mark.parametrize("fmt", ["group128"] + list(FORMATS))
 @pytest.mark.parametrize("K,N,M", [(8192, 10240, 12), (8192, 10240, 24), (8192, 10240, 32),
                                    (28672, 8192, 16), (28672, 8192, 32), (8192, 10240, 40),
                                    (8192, 10240, 64), (4096, 20480, 64), (4096, 22016, 40),
-                                   (8192, 28672, 64)])
+                                   (8192, 28672, 64), (4096, 12288, 96), (8192, 10240, 128)])
 def test_whole_k_wide_slab_groups_against_oracle(K, N, M, fmt):
     if fmt == "group128":
         A, q, s = draw(K, N, M, seed=M + K + N + 2)
