@@ -2423,14 +2423,15 @@ hipError_t dispatch_skinny(int mb, int ns, bool two, bool deep, bool fl, const P
     if (two) {
         if constexpr (!F::ZP) {
             if (mb == 2) {
-                // Seven and eight slabs (A through registers): one register buffer, the loads
-                // hidden by the CU's other seven waves, measured 4-5% faster than two on
-                // 8192 x 57344 at M = 24 and 32 (47.7 -> 45.6, 49.3 -> 47.2 us); nine slabs (A
-                // by DMA) time the same either way and keep two.
+                // One register buffer: the CU's other seven waves hide each wave's loads.
+                // Against two buffers, alternated in one process (8192 x 57344, seven slabs, at
+                // M = 24 / 32: 0.93-0.96x the time in two runs, even in a third; 72k x 18k,
+                // nine slabs: 0.98-1.0x).  The form with one row block keeps two buffers: there
+                // a single one measured anywhere from 3% faster to 6% slower.
                 switch (ns) {
                 case 7: return launch_skinny<2, 7, F, true, 1, true>(p, s);
                 case 8: return launch_skinny<2, 8, F, true, 1, true>(p, s);
-                case 9: return launch_skinny<2, 9, F, true, D, true, true>(p, s);
+                case 9: return launch_skinny<2, 9, F, true, 1, true, true>(p, s);
                 default: break;
                 }
             }
