@@ -1398,8 +1398,8 @@ __global__ __launch_bounds__(kThreads, (MB == 1 || TWO) ? 2 : 1) void w4a16_gemm
     // real rows: its address path stalls for more than half of its busy cycles at M = 16 and
     // 32); the wave puts them in fragment order through its own LDS region (compute).  DM:
     // the same lines by DMA straight into the wave's LDS buffer of the tile, no registers in
-    // flight and no LDS stores (the nine-slab 32-row form and four row blocks, whose registers
-    // are full).
+    // flight and no LDS stores (the nine-slab 32-row form and four row blocks, where the
+    // registers are the limit).
     uint32_t v_a[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -2332,8 +2332,8 @@ Config choose_config(int M, int K, int N, int cus, bool zp)
     // M = 9..16 where a wave walks at least 8 K tiles (8192 x 8192 12.1 -> 10.1 us, 8192 x
     // 7168 11.9 -> 10.1 us); not at M <= 8, where the loads of dead rows cost nothing (3-6%
     // slower with the LDS round trip), nor at M = 9..16 over fewer tiles (1024 x 8192 and
-    // 3584 x 8192 at M = 16: 4% slower), nor on the nine-slab 32-row form, whose registers
-    // are full.
+    // 3584 x 8192 at M = 16: 4% slower).  (The nine-slab 32-row form takes its whole lines by
+    // DMA, see dispatch_skinny.)
     c.FL = c.NS > 0 && (M > 16 || (M > 8 && c.G >= 8 * kWaves * c.KS));
     return c;
 }
