@@ -1291,7 +1291,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a16_gemm_wide_kernel(
 // very end, when every stripe finishes at once (on small weights that chain is most of the
 // time).  Here a workgroup owns NS consecutive 16-column slabs over the whole K range, so no
 // output is shared between workgroups.  Its four waves split the K tiles into four contiguous
-// runs; each streams all NS slabs over its run (NS KiB of weights per tile, double-buffered),
+// runs; each streams all NS slabs over its run (NS KiB of weights per tile in two register
+// buffers; three at M <= 8 on small weights, one in the 32-row form at two workgroups per CU),
 // and the four fp32 partial sums meet in LDS at the end in a fixed order (the in-block
 // reduction of warp partial sums the deep-dive page describes in "让多个 warp 计算同一个输出
 // tile 的部分和").  A needs no LDS: each wave loads its A fragments (16 bytes per lane per 32-k
